@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for sparse-MLA attention (test infrastructure only).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg import this
+package.  It shares no code with the HIP library.
+"""
+from .smla_oracle import (EMPTY_ROW_LSE, SUMEXP_FLOOR, OracleInputError,
+                          sparse_mla_bwd, sparse_mla_fwd, token_backward,
+                          token_forward, touched_rows, valid_slots)
+
+__all__ = ["EMPTY_ROW_LSE", "SUMEXP_FLOOR", "OracleInputError", "sparse_mla_bwd",
+           "sparse_mla_fwd", "token_backward", "token_forward", "touched_rows",
+           "valid_slots"]

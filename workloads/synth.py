@@ -1,0 +1,285 @@
+"""Seeded synthetic inputs for sparse-MLA attention (DSA, absorbed-latent layout).
+
+This module only draws inputs. It holds none of the attention arithmetic, so
+both the fp64 oracle's tests and the HIP path's tests and benchmark may use it.
+
+Layout of everything returned (packed "thd" layout, one KV group):
+  q      [S, H, 576]  bf16 bits (uint16)   absorbed-latent query, 512 latent + 64 rope
+  kv     [S_kv, 576]  bf16 bits (uint16)   shared latent KV; value = columns 0:512
+  dout   [S, H, 512]  bf16 bits (uint16)   upstream gradient of out
+  idx    [S, K]       int32                absolute rows of kv; -1 marks padding
+
+The index structure follows the production workload the pages describe: the
+forward/backward fix of miles PR #2079 ("fix GLM-5 sparse-MLA kernel -1 index
+OOB and NaN gradients", section 实现拆解 item 4) was checked at H=8, topk=2048
+on ragged packed sequences including all -1 rows, and the -1 sentinel comes
+from padding a capped top-k back to the fixed width (Megatron-Bridge PR #17,
+"GLM-5 DSA option: tilelang (2/2)", section Bug fixes).
+
+Draw order for every workload: q, kv, dout as fp32 standard normals (times the
+workload's sigma) rounded to bf16 with round-to-nearest-even; then sequence
+lengths (where drawn); then indices; then the rows that are emptied or scaled.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+D_LATENT = 512
+D_ROPE = 64
+D_QK = D_LATENT + D_ROPE
+SM_SCALE = 1.0 / math.sqrt(192.0)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); return the bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32).astype(np.uint64)
+    rounding = np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))
+    out = ((b + rounding) >> np.uint64(16)).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bits to float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bits to float64."""
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+@dataclass
+class Workload:
+    name: str
+    q: np.ndarray          # uint16 [S, H, 576]
+    kv: np.ndarray         # uint16 [S_kv, 576]
+    dout: np.ndarray       # uint16 [S, H, 512]
+    idx: np.ndarray        # int32 [S, K]
+    sm_scale: float
+    seqlens: list = field(default_factory=list)
+    seed: int = 0
+
+    @property
+    def S(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def H(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def S_kv(self) -> int:
+        return self.kv.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.idx.shape[1]
+
+    @property
+    def n_valid(self) -> int:
+        """Number of valid (token, slot) pairs: slots holding a row in [0, S_kv)."""
+        return int(np.count_nonzero((self.idx >= 0) & (self.idx < self.S_kv)))
+
+
+def _normal_bf16(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return f32_to_bf16_bits(x)
+
+
+def _tensors(rng, S, H, S_kv, sigma=1.0):
+    q = _normal_bf16(rng, (S, H, D_QK), sigma)
+    kv = _normal_bf16(rng, (S_kv, D_QK), sigma)
+    dout = _normal_bf16(rng, (S, H, D_LATENT), 1.0)
+    return q, kv, dout
+
+
+def _starts(seqlens):
+    return np.concatenate([[0], np.cumsum(seqlens)[:-1]]).astype(np.int64)
+
+
+def causal_full_rows(rng, seqlens, K) -> np.ndarray:
+    """Row p of each sequence lists all p+1 in-sequence causal positions, in a
+    random order, followed by -1; positions beyond K are not possible here, so
+    every sequence length must be <= K."""
+    S = int(sum(seqlens))
+    idx = np.full((S, K), -1, dtype=np.int32)
+    for start, n in zip(_starts(seqlens), seqlens):
+        assert n <= K, "full causal rows need seqlen <= topk"
+        for p in range(n):
+            row = rng.permutation(p + 1).astype(np.int32) + np.int32(start)
+            idx[start + p, : p + 1] = row
+    return idx
+
+
+def causal_uniform_rows(rng, seqlens, K) -> np.ndarray:
+    """Row p picks min(K, p+1) distinct causal in-sequence positions uniformly
+    (in random order); the rest of the row is -1."""
+    S = int(sum(seqlens))
+    idx = np.full((S, K), -1, dtype=np.int32)
+    for start, n in zip(_starts(seqlens), seqlens):
+        for p in range(n):
+            cand = p + 1
+            if cand <= K:
+                row = rng.permutation(cand)
+            else:
+                row = rng.choice(cand, size=K, replace=False, shuffle=True)
+            idx[start + p, : len(row)] = row.astype(np.int32) + np.int32(start)
+    return idx
+
+
+def causal_recency_rows(rng, seqlens, K, recent=512) -> np.ndarray:
+    """Rows with at least K candidates take every one of the last `recent`
+    positions plus K-`recent` distinct uniform picks from the older positions;
+    shorter rows list every causal position.  (One reading of "half the picks
+    from the last 512 positions": half of K=2048 cannot be met with distinct
+    picks out of 512 positions, so all 512 are taken and the rest are uniform.)"""
+    S = int(sum(seqlens))
+    idx = np.full((S, K), -1, dtype=np.int32)
+    for start, n in zip(_starts(seqlens), seqlens):
+        for p in range(n):
+            cand = p + 1
+            if cand <= K:
+                row = rng.permutation(cand)
+            else:
+                old = rng.choice(cand - recent, size=K - recent, replace=False, shuffle=False)
+                row = np.concatenate([np.arange(cand - recent, cand), old])
+                row = row[rng.permutation(K)]
+            idx[start + p, : len(row)] = row.astype(np.int32) + np.int32(start)
+    return idx
+
+
+def ragged_lengths(rng, n_seq, lo, hi, total) -> list:
+    """n_seq lengths drawn uniformly in [lo, hi], then nudged by +-1 steps on
+    randomly chosen sequences (staying inside [lo, hi]) until they sum to total."""
+    lens = rng.integers(lo, hi + 1, size=n_seq).astype(np.int64)
+    assert n_seq * lo <= total <= n_seq * hi
+    while lens.sum() != total:
+        i = int(rng.integers(0, n_seq))
+        if lens.sum() < total and lens[i] < hi:
+            lens[i] += 1
+        elif lens.sum() > total and lens[i] > lo:
+            lens[i] -= 1
+    return [int(x) for x in lens]
+
+
+# ---------------------------------------------------------------------------
+# The five workloads.  Each is named by what it is; the seeds are 0..4.
+# ---------------------------------------------------------------------------
+
+def tiny(seed: int = 0) -> Workload:
+    """S=128 single sequence, H=8, topk=64; row s holds min(64, s+1) distinct
+    causal positions drawn uniformly, padded with -1."""
+    rng = np.random.default_rng(seed)
+    S, H, K = 128, 8, 64
+    q, kv, dout = _tensors(rng, S, H, S)
+    idx = causal_uniform_rows(rng, [S], K)
+    return Workload("tiny_s128_h8_k64", q, kv, dout, idx, SM_SCALE, [S], seed)
+
+
+def packed_ragged(seed: int = 1) -> Workload:
+    """S=4096 packed as sequences {512, 1024, 1536, 1024}, H=8, topk=2048.
+    Every length is below topk, so row p lists all p+1 in-sequence causal
+    positions (shuffled) followed by 2047-p trailing -1."""
+    rng = np.random.default_rng(seed)
+    seqlens = [512, 1024, 1536, 1024]
+    S, H, K = sum(seqlens), 8, 2048
+    q, kv, dout = _tensors(rng, S, H, S)
+    idx = causal_full_rows(rng, seqlens, K)
+    return Workload("packed_ragged_s4096_h8_k2048", q, kv, dout, idx, SM_SCALE, seqlens, seed)
+
+
+def padding_stress(seed: int = 2, sigma: float = 2.0) -> Workload:
+    """S=4096 packed as 16 sequences with lengths uniform in [16, 512] (nudged to
+    sum to 4096), H=8, topk=2048, q/kv ~ N(0, sigma^2) with sigma=2 (variance 4)
+    for large logits; full causal rows, then 5% of the rows set entirely to -1."""
+    rng = np.random.default_rng(seed)
+    S, H, K = 4096, 8, 2048
+    q, kv, dout = _tensors(rng, S, H, S, sigma=sigma)
+    seqlens = ragged_lengths(rng, 16, 16, 512, S)
+    idx = causal_full_rows(rng, seqlens, K)
+    n_empty = int(round(0.05 * S))
+    empty = rng.choice(S, size=n_empty, replace=False)
+    idx[empty, :] = -1
+    return Workload(f"padding_stress_s4096_h8_k2048_sigma{sigma:g}", q, kv, dout, idx,
+                    SM_SCALE, seqlens, seed)
+
+
+def recency_hot_rows(seed: int = 3) -> Workload:
+    """Single sequence S=8192, H=16, topk=2048 with a recency bias: every row
+    with more than 2048 candidates takes all of its last 512 positions plus
+    1536 uniform picks from the older ones (hot KV rows, dKV contention)."""
+    rng = np.random.default_rng(seed)
+    S, H, K = 8192, 16, 2048
+    q, kv, dout = _tensors(rng, S, H, S)
+    idx = causal_recency_rows(rng, [S], K)
+    return Workload("recency_s8192_h16_k2048", q, kv, dout, idx, SM_SCALE, [S], seed)
+
+
+def long_context(seed: int = 4) -> Workload:
+    """S=32768 packed as 2 x 16384, H=16, topk=2048 uniform distinct causal
+    picks; 1% of the kv rows (seeded) are drawn with 30x the scale."""
+    rng = np.random.default_rng(seed)
+    seqlens = [16384, 16384]
+    S, H, K = sum(seqlens), 16, 2048
+    q = _normal_bf16(rng, (S, H, D_QK), 1.0)
+    kv32 = rng.standard_normal(size=(S, D_QK), dtype=np.float32)
+    dout = _normal_bf16(rng, (S, H, D_LATENT), 1.0)
+    idx = causal_uniform_rows(rng, seqlens, K)
+    hot = rng.choice(S, size=int(round(0.01 * S)), replace=False)
+    kv32[hot] *= np.float32(30.0)
+    kv = f32_to_bf16_bits(kv32)
+    return Workload("long_context_s32768_h16_k2048", q, kv, dout, idx, SM_SCALE, seqlens, seed)
+
+
+WORKLOADS = {
+    "tiny": tiny,
+    "packed_ragged": packed_ragged,
+    "padding_stress": padding_stress,
+    "recency": recency_hot_rows,
+    "long_context": long_context,
+}
+
+
+def custom(S, H, K, S_kv=None, seed=0, sigma=1.0, pad_frac=0.3, empty_frac=0.1,
+           dup_frac=0.0, scatter_pad=True, oob_frac=0.0) -> Workload:
+    """Small free-form workload for edge-case tests: random rows of kv (not
+    causal), a fraction of slots set to -1 at random positions (or trailing),
+    some rows entirely -1, optional duplicate entries, optional out-of-range
+    entries (values >= S_kv or < -1) for the safety tests."""
+    rng = np.random.default_rng(seed)
+    S_kv = S if S_kv is None else S_kv
+    q, kv, dout = _tensors(rng, S, H, S_kv, sigma=sigma)
+    idx = np.empty((S, K), dtype=np.int32)
+    for s in range(S):
+        if K <= S_kv:
+            idx[s] = rng.choice(S_kv, size=K, replace=False)
+        else:
+            idx[s] = rng.integers(0, S_kv, size=K)
+    if dup_frac > 0:
+        m = rng.random((S, K)) < dup_frac
+        src = rng.integers(0, K, size=(S, K))
+        idx[m] = idx[np.nonzero(m)[0], src[m]]
+    if pad_frac > 0:
+        if scatter_pad:
+            idx[rng.random((S, K)) < pad_frac] = -1
+        else:
+            n_pad = int(round(pad_frac * K))
+            if n_pad:
+                idx[:, K - n_pad:] = -1
+    if empty_frac > 0:
+        n_e = max(1, int(round(empty_frac * S)))
+        idx[rng.choice(S, size=min(S, n_e), replace=False)] = -1
+    if oob_frac > 0:
+        m = rng.random((S, K)) < oob_frac
+        bad = np.where(rng.random((S, K)) < 0.5, S_kv + rng.integers(0, 1000, size=(S, K)),
+                       -2 - rng.integers(0, 1000, size=(S, K)))
+        idx[m] = bad[m].astype(np.int32)
+    return Workload(f"custom_s{S}_h{H}_k{K}_skv{S_kv}_seed{seed}", q, kv, dout, idx,
+                    SM_SCALE, [S], seed)
