@@ -1,0 +1,197 @@
+"""Benchmark: sparse-MLA forward + backward on one MI355X.
+
+One step = forward (plan + fwd kernel) and backward (plan + dq pass + dkv
+pass) over the whole workload, inputs resident in HBM.  The default workload
+is the packed ragged batch: S=4096 tokens as sequences {512, 1024, 1536,
+1024}, H=8 heads, topk=2048 full causal rows (2,361,344 valid pairs).
+
+Prints ONE JSON line with the metric (useful TFLOP/s, i.e. 7680*H flops per
+valid (token, slot) pair over the fwd+bwd step time), the roofline of the
+dominant kernel (timed with HIP events on the library's stream) and the CPU
+baseline (the fp64 oracle on a bounded token sample, on the host cores).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "sparse-MLA fwd+bwd useful TFLOP/s at H=8 topk=2048; % of bf16 MFMA peak"
+
+# Algorithmic flops per valid (token, slot) pair and head, per kernel.
+FLOPS_PER_PAIR_HEAD = {
+    "fwd": 2 * (576 + 512),                  # scores + PV
+    "bwd_dq": 2 * (576 + 512 + 576),         # recomputed scores, dP, dQ
+    "bwd_dkv": 2 * (576 + 512 + 576 + 512),  # recomputed scores, dP, dK, dV
+}
+USEFUL_PER_PAIR_HEAD = 7680                  # fwd 2176 + bwd 5504 (one recompute)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="packed_ragged",
+                    choices=["tiny", "packed_ragged", "padding_stress", "recency", "long_context"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, target_s: float):
+    """The fp64 oracle as it stands, on a seeded sample of tokens of the same
+    workload (their forward + backward, dkv scattered into the full kv)."""
+    import threadpoolctl
+
+    from oracle import sparse_mla_bwd, sparse_mla_fwd
+    from workloads import synth
+
+    info = threadpoolctl.threadpool_info()
+    threads = max([d.get("num_threads", 1) for d in info] or [1])
+    kv = synth.bf16_bits_to_f64(w.kv)
+    rng = np.random.default_rng(1234)
+    order = rng.permutation(w.S)
+
+    def run(toks):
+        toks = np.sort(toks)
+        q = synth.bf16_bits_to_f64(w.q[toks])
+        do = synth.bf16_bits_to_f64(w.dout[toks])
+        ix = w.idx[toks]
+        t = time.perf_counter()
+        sparse_mla_fwd(q, kv, ix, w.sm_scale)
+        sparse_mla_bwd(q, kv, do, ix, w.sm_scale)
+        dt = time.perf_counter() - t
+        nv = int(np.count_nonzero((ix >= 0) & (ix < w.S_kv)))
+        return dt, nv, len(toks)
+
+    dt0, nv0, n0 = run(order[:64])
+    per_pair = dt0 / max(nv0, 1)
+    nv_mean = w.n_valid / w.S
+    n = int(min(w.S, max(64, target_s / max(per_pair * nv_mean, 1e-9))))
+    dt, nv, n = run(order[:n])
+    flops = USEFUL_PER_PAIR_HEAD * w.H * nv
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} of {w.S} tokens (seeded), {nv} valid pairs, fwd+bwd fp64, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not a measured configuration.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bwd_sparse_mla_amd as smla
+    from workloads import synth
+
+    w = synth.WORKLOADS[args.workload]()
+    print(f"[bench] workload {w.name}: S={w.S} H={w.H} K={w.K} S_kv={w.S_kv} "
+          f"valid pairs={w.n_valid}", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    to_bf16 = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    q, kv, dout = to_bf16(w.q), to_bf16(w.kv), to_bf16(w.dout)
+    idx = torch.from_numpy(np.ascontiguousarray(w.idx)).to(dev)
+    run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, dev)
+    run._check(q, kv, idx, dout)
+
+    def step():
+        run.fwd(q, kv, idx, w.sm_scale)
+        run.bwd(q, kv, dout, idx, w.sm_scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)",
+          file=sys.stderr, flush=True)
+    for name, t in (("out", run.out), ("lse", run.lse), ("dq", run.dq), ("dkv", run.dkv)):
+        bad = int((~torch.isfinite(t.float())).sum())
+        if bad:
+            raise RuntimeError(f"{bad} nonfinite values in {name}")
+
+    nv = w.n_valid
+    useful = USEFUL_PER_PAIR_HEAD * w.H * nv
+    value = useful / (ms * 1e-3) / 1e12
+
+    kernels = {}
+    roofline = None
+    if not args.no_kernel_timing:
+        smla.timing_start(16 * args.steps)
+        for _ in range(args.steps):
+            step()
+        smla.timing_stop()
+        torch.cuda.synchronize()
+        for name in ("fill", "plan", "fwd", "bwd_dq", "bwd_dkv"):
+            n, tot = smla.timing_read(name)
+            if n:
+                kernels[name] = {"launches": n, "avg_ms": tot / n}
+        # plan runs in fwd and in bwd: per-step totals
+        dom = max((k for k in kernels if k in FLOPS_PER_PAIR_HEAD),
+                  key=lambda k: kernels[k]["avg_ms"])
+        flops = FLOPS_PER_PAIR_HEAD[dom] * w.H * nv
+        ach = flops / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "flops_per_launch": flops, "avg_ms": round(kernels[dom]["avg_ms"], 5)}
+        print(f"[bench] kernels {kernels}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "S": w.S, "S_kv": w.S_kv, "H": w.H, "topk": w.K,
+                   "seqlens": w.seqlens, "valid_pairs": nv, "useful_gflop": useful / 1e9,
+                   "parallelism": "none (one GPU)", "dkv_mode": "deterministic"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+        "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,13 @@
+"""DSA sparse-MLA attention (forward and backward) on AMD Instinct MI355X.
+
+The computation runs in hand-written HIP kernels for gfx950 behind the C ABI
+of libsmla.so (include/smla.h); this package only marshals arguments.
+"""
+from ._lib import SmlaError, load as load_library
+from .ops import (SparseMLA, SparseMLARunner, bwd_workspace_bytes, fwd_workspace_bytes,
+                  sparse_mla_bwd, sparse_mla_fwd, timing_read, timing_start, timing_stop,
+                  validate_indices)
+
+__all__ = ["SmlaError", "SparseMLA", "SparseMLARunner", "bwd_workspace_bytes",
+           "fwd_workspace_bytes", "load_library", "sparse_mla_bwd", "sparse_mla_fwd",
+           "timing_read", "timing_start", "timing_stop", "validate_indices"]

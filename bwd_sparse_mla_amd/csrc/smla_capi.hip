@@ -1,0 +1,344 @@
+// C ABI of libsmla (see include/smla.h): argument checks, workspace layout
+// and the launch sequence of each call.  No allocation, no synchronization.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "smla.h"
+#include "smla_internal.h"
+
+namespace smla {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int64_t s_q, int64_t s_kv, int heads, int topk) {
+  if (s_q < 0 || s_kv < 1 || s_kv > MAX_SKV)
+    return fail(SMLA_ERR_SHAPE, "s_q must be >= 0 and s_kv in [1, 2^24)");
+  if (heads != 8 && heads != 16 && heads != 32 && heads != 64)
+    return fail(SMLA_ERR_SHAPE, "heads must be 8, 16, 32 or 64");
+  if (topk < 1 || topk > MAX_TOPK) return fail(SMLA_ERR_SHAPE, "topk must be in [1, 16384]");
+  if (s_q > (int64_t(1) << 31) / heads)
+    return fail(SMLA_ERR_SHAPE, "s_q * heads must stay below 2^31");
+  return SMLA_OK;
+}
+
+// gfx950 check, cached per device ordinal.
+int check_device() {
+  static std::mutex mu;
+  static int cache[64];  // 0 unknown, 1 ok, 2 unsupported
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SMLA_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(SMLA_ERR_DEVICE, "device ordinal out of range");
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev] == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(SMLA_ERR_HIP, "hipGetDeviceProperties failed");
+      cache[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    if (cache[dev] != 1) return fail(SMLA_ERR_DEVICE, "current device is not gfx950");
+  }
+  return SMLA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SMLA_OK;
+  return fail(SMLA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Kernel timing for benchmarks: event pairs around each launch.
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct Timing {
+  bool active = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<TimedLaunch> recs;
+  size_t next = 0;
+};
+Timing g_timing;
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  if (!g_timing.active || g_timing.next + 2 > g_timing.pool.size()) return launch();
+  hipEvent_t a = g_timing.pool[g_timing.next], b = g_timing.pool[g_timing.next + 1];
+  g_timing.next += 2;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e == hipSuccess) g_timing.recs.push_back({name, a, b});
+  return e;
+}
+
+}  // namespace
+
+Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward) {
+  Plan p;
+  p.s_q = s_q;
+  p.s_kv = s_kv;
+  p.heads = heads;
+  p.topk = topk;
+  p.T = tokens_per_group(heads);
+  p.G = (s_q + p.T - 1) / p.T;
+  p.NB = (s_kv + TILE_KV - 1) / TILE_KV;
+  p.qcap = (int64_t)p.T * topk;
+  p.rcap = (int64_t)p.T * (topk < p.NB ? topk : p.NB);
+  size_t o = 0;
+  p.off_qcount = o;  o = align256(o + (size_t)p.G * 4);
+  p.off_xcount = o;  o = align256(o + (size_t)p.G * 4);
+  p.off_qrow = o;    o = align256(o + (size_t)p.G * p.qcap * 4);
+  p.off_qmask = o;   o = align256(o + (size_t)p.G * p.qcap);
+  // xtotal sits directly before ktab so one fill clears both.
+  p.off_xtotal = o;  o += 256;
+  if (backward) {
+    p.off_ktab = o;    o = align256(o + (size_t)p.NB * p.G * 8);
+    p.off_krtok = o;   o = align256(o + (size_t)p.G * p.rcap * 4);
+    p.off_krmask = o;  o = align256(o + (size_t)p.G * p.rcap * 8);
+    p.off_delta = o;   o = align256(o + (size_t)s_q * heads * 4);
+  }
+  p.bytes = o;
+  return p;
+}
+
+}  // namespace smla
+
+using namespace smla;
+
+extern "C" {
+
+const char* smla_last_error(void) { return g_last_error.c_str(); }
+
+int smla_version(void) { return SMLA_ABI_VERSION; }
+
+int smla_device_supported(int device) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return 0;
+  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+size_t smla_fwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk) {
+  if (check_shape(s_q, s_kv, heads, topk) != SMLA_OK) return 0;
+  return make_plan(s_q, s_kv, heads, topk, false).bytes;
+}
+
+size_t smla_bwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
+                               uint32_t flags) {
+  (void)flags;
+  if (check_shape(s_q, s_kv, heads, topk) != SMLA_OK) return 0;
+  return make_plan(s_q, s_kv, heads, topk, true).bytes;
+}
+
+int smla_fwd(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,
+             int32_t heads, int32_t topk, float sm_scale, void* out, float* lse,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = check_shape(s_q, s_kv, heads, topk);
+  if (st) return st;
+  if (!kv || (s_q > 0 && (!q || !indices || !out || !lse)))
+    return fail(SMLA_ERR_NULL, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(indices) || !aligned16(out) || !aligned16(lse))
+    return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const Plan p = make_plan(s_q, s_kv, heads, topk, false);
+  if (!workspace || workspace_bytes < p.bytes)
+    return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_fwd_workspace_size()");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SMLA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if ((st = check_device())) return st;
+  if (s_q == 0) return SMLA_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+
+  PlanArgs pa{};
+  pa.idx = indices;
+  pa.s_q = s_q;
+  pa.s_kv = s_kv;
+  pa.topk = topk;
+  pa.G = p.G;
+  pa.NB = p.NB;
+  pa.qcap = p.qcap;
+  pa.rcap = p.rcap;
+  pa.qcount = reinterpret_cast<int*>(ws + p.off_qcount);
+  pa.xcount = reinterpret_cast<int*>(ws + p.off_xcount);
+  pa.xtotal = reinterpret_cast<int*>(ws + p.off_xtotal);
+  pa.qrow = reinterpret_cast<int32_t*>(ws + p.off_qrow);
+  pa.qmask = reinterpret_cast<uint8_t*>(ws + p.off_qmask);
+  pa.ktab = nullptr;
+  if ((st = hip_status(timed("fill", s, [&] { return launch_fill_u32(pa.xtotal, 1, 0u, s); }), "fill"))) return st;
+  if ((st = hip_status(timed("plan", s, [&] { return launch_plan(pa, heads, s); }), "plan"))) return st;
+
+  FwdArgs fa{};
+  fa.q = static_cast<const uint16_t*>(q);
+  fa.kv = static_cast<const uint16_t*>(kv);
+  fa.s_q = s_q;
+  fa.s_kv = s_kv;
+  fa.scale_log2 = sm_scale * 1.4426950408889634f;
+  fa.G = p.G;
+  fa.qcap = p.qcap;
+  fa.qcount = pa.qcount;
+  fa.qrow = pa.qrow;
+  fa.qmask = pa.qmask;
+  fa.out = static_cast<uint16_t*>(out);
+  fa.lse = lse;
+  return hip_status(timed("fwd", s, [&] { return launch_fwd(fa, heads, s); }), "fwd");
+}
+
+int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
+             const int32_t* indices, const float* lse, int64_t s_q, int64_t s_kv, int32_t heads,
+             int32_t topk, float sm_scale, void* dq, void* dkv, float* dkv_f32, uint32_t flags,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = check_shape(s_q, s_kv, heads, topk);
+  if (st) return st;
+  if (!kv || (s_q > 0 && (!q || !out || !dout || !indices || !lse || !dq)))
+    return fail(SMLA_ERR_NULL, "null tensor pointer");
+  if (!dkv && !dkv_f32) return fail(SMLA_ERR_NULL, "dkv and dkv_f32 are both null");
+  if (flags & ~(SMLA_DKV_ACCUMULATE | SMLA_DKV_ATOMIC))
+    return fail(SMLA_ERR_FLAGS, "unknown flag bits");
+  if ((flags & SMLA_DKV_ACCUMULATE) && !dkv_f32)
+    return fail(SMLA_ERR_FLAGS, "SMLA_DKV_ACCUMULATE needs dkv_f32");
+  if (flags & SMLA_DKV_ATOMIC)
+    return fail(SMLA_ERR_FLAGS, "SMLA_DKV_ATOMIC is not available in this build");
+  const void* ptrs[] = {q, kv, out, dout, indices, lse, dq};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if ((dkv && !aligned16(dkv)) || (dkv_f32 && !aligned16(dkv_f32)))
+    return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const Plan p = make_plan(s_q, s_kv, heads, topk, true);
+  if (!workspace || workspace_bytes < p.bytes)
+    return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_bwd_workspace_size()");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SMLA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if ((st = check_device())) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+
+  PlanArgs pa{};
+  pa.idx = indices;
+  pa.s_q = s_q;
+  pa.s_kv = s_kv;
+  pa.topk = topk;
+  pa.G = p.G;
+  pa.NB = p.NB;
+  pa.qcap = p.qcap;
+  pa.rcap = p.rcap;
+  pa.qcount = reinterpret_cast<int*>(ws + p.off_qcount);
+  pa.xcount = reinterpret_cast<int*>(ws + p.off_xcount);
+  pa.xtotal = reinterpret_cast<int*>(ws + p.off_xtotal);
+  pa.qrow = reinterpret_cast<int32_t*>(ws + p.off_qrow);
+  pa.qmask = reinterpret_cast<uint8_t*>(ws + p.off_qmask);
+  pa.ktab = reinterpret_cast<int2*>(ws + p.off_ktab);
+  pa.krtok = reinterpret_cast<int32_t*>(ws + p.off_krtok);
+  pa.krmask = reinterpret_cast<unsigned long long*>(ws + p.off_krmask);
+  // xtotal (one 256-byte slot) and ktab are contiguous: clear both at once.
+  const size_t clear_words = (256 + (size_t)p.NB * p.G * 8) / 4;
+  if ((st = hip_status(timed("fill", s, [&] { return launch_fill_u32(pa.xtotal, clear_words, 0u, s); }), "fill"))) return st;
+  if (s_q > 0 && (st = hip_status(timed("plan", s, [&] { return launch_plan(pa, heads, s); }), "plan"))) return st;
+
+  BwdArgs ba{};
+  ba.q = static_cast<const uint16_t*>(q);
+  ba.kv = static_cast<const uint16_t*>(kv);
+  ba.out = static_cast<const uint16_t*>(out);
+  ba.dout = static_cast<const uint16_t*>(dout);
+  ba.lse = lse;
+  ba.s_q = s_q;
+  ba.s_kv = s_kv;
+  ba.scale = sm_scale;
+  ba.scale_log2 = sm_scale * 1.4426950408889634f;
+  ba.G = p.G;
+  ba.NB = p.NB;
+  ba.qcap = p.qcap;
+  ba.rcap = p.rcap;
+  ba.qcount = pa.qcount;
+  ba.xcount = pa.xcount;
+  ba.xtotal = pa.xtotal;
+  ba.qrow = pa.qrow;
+  ba.qmask = pa.qmask;
+  ba.ktab = pa.ktab;
+  ba.krtok = pa.krtok;
+  ba.krmask = pa.krmask;
+  ba.delta = reinterpret_cast<float*>(ws + p.off_delta);
+  ba.dq = static_cast<uint16_t*>(dq);
+  ba.dkv = static_cast<uint16_t*>(dkv);
+  ba.dkv_f32 = dkv_f32;
+  ba.accumulate = (flags & SMLA_DKV_ACCUMULATE) ? 1 : 0;
+  if (s_q > 0 && (st = hip_status(timed("bwd_dq", s, [&] { return launch_bwd_dq(ba, heads, s); }), "bwd_dq"))) return st;
+  return hip_status(timed("bwd_dkv", s, [&] { return launch_bwd_dkv(ba, heads, s); }), "bwd_dkv");
+}
+
+int smla_validate_indices(const int32_t* indices, int64_t s_q, int32_t topk, int64_t s_kv,
+                          unsigned long long* n_bad, void* stream) {
+  g_last_error.clear();
+  if (!n_bad) return fail(SMLA_ERR_NULL, "n_bad is null");
+  if (s_q < 0 || topk < 1 || s_kv < 1) return fail(SMLA_ERR_SHAPE, "bad sizes");
+  if (s_q > 0 && !indices) return fail(SMLA_ERR_NULL, "indices is null");
+  if ((reinterpret_cast<uintptr_t>(n_bad) & 7u) != 0)
+    return fail(SMLA_ERR_ALIGN, "n_bad must be 8-byte aligned");
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(
+      timed("validate", s, [&] { return launch_validate(indices, s_q * topk, s_kv, n_bad, s); }),
+      "validate");
+}
+
+int smla_timing_start(int max_launches) {
+  g_last_error.clear();
+  if (max_launches < 1 || max_launches > (1 << 20))
+    return fail(SMLA_ERR_SHAPE, "max_launches must be in [1, 2^20]");
+  for (hipEvent_t e : g_timing.pool) (void)hipEventDestroy(e);
+  g_timing.pool.clear();
+  g_timing.recs.clear();
+  g_timing.next = 0;
+  for (int i = 0; i < 2 * max_launches; ++i) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return fail(SMLA_ERR_HIP, "hipEventCreate failed");
+    g_timing.pool.push_back(e);
+  }
+  g_timing.active = true;
+  return SMLA_OK;
+}
+
+int smla_timing_stop(void) {
+  g_timing.active = false;
+  return SMLA_OK;
+}
+
+int smla_timing_read(const char* kernel, int* launches, double* total_ms) {
+  g_last_error.clear();
+  if (!kernel || !launches || !total_ms) return fail(SMLA_ERR_NULL, "null argument");
+  int n = 0;
+  double tot = 0.0;
+  for (const TimedLaunch& r : g_timing.recs) {
+    if (std::strcmp(r.name, kernel) != 0) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return fail(SMLA_ERR_HIP, "event sync failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      return fail(SMLA_ERR_HIP, "hipEventElapsedTime failed");
+    ++n;
+    tot += ms;
+  }
+  *launches = n;
+  *total_ms = tot;
+  return SMLA_OK;
+}
+
+}  // extern "C"

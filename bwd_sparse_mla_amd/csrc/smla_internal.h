@@ -1,0 +1,96 @@
+// Host-visible launch interface between the C ABI (smla_capi.hip) and the
+// kernels.  Nothing here is exported from the shared library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace smla {
+
+// Rows of queries one workgroup of the query-major kernels owns: T = 64 / H
+// consecutive tokens ("query group").  64 rows fill four 16-row MFMA tiles.
+constexpr int GROUP_ROWS = 64;
+constexpr int TILE_KV = 64;      // kv rows per LDS tile / per kv block
+constexpr int MAX_TOPK = 16384;
+constexpr int64_t MAX_SKV = (int64_t(1) << 24) - 1;
+
+inline int tokens_per_group(int heads) { return GROUP_ROWS / heads; }
+
+// Sizes derived from the problem shape; also the workspace layout.
+struct Plan {
+  int64_t s_q = 0, s_kv = 0;
+  int heads = 0, topk = 0;
+  int T = 0;          // tokens per query group
+  int64_t G = 0;      // number of query groups
+  int64_t NB = 0;     // number of 64-row kv blocks
+  int64_t qcap = 0;   // union entries reserved per group: T * topk
+  int64_t rcap = 0;   // kv-block records reserved per group: T * min(topk, NB)
+  // byte offsets into the workspace
+  size_t off_qcount = 0, off_xcount = 0, off_xtotal = 0, off_qrow = 0, off_qmask = 0;
+  size_t off_ktab = 0, off_krtok = 0, off_krmask = 0, off_delta = 0;
+  size_t bytes = 0;
+};
+
+Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward);
+
+struct PlanArgs {
+  const int32_t* idx;
+  int64_t s_q, s_kv;
+  int topk;
+  int64_t G, NB, qcap, rcap;
+  int* qcount;        // [G]   union entries (main + extra) per group
+  int* xcount;        // [G]   extra entries (repeated slots) per group
+  int* xtotal;        // [1]   sum of xcount
+  int32_t* qrow;      // [G, qcap] kv row of each union entry
+  uint8_t* qmask;     // [G, qcap] mask of the group's tokens that select it
+  int2* ktab;         // [NB, G] (record start within the group, record count); may be null
+  int32_t* krtok;     // [G, rcap] token of each kv-block record
+  unsigned long long* krmask;  // [G, rcap] 64-bit row mask of each record
+};
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* kv;
+  int64_t s_q, s_kv;
+  float scale_log2;   // sm_scale * log2(e)
+  int64_t G, qcap;
+  const int* qcount;
+  const int32_t* qrow;
+  const uint8_t* qmask;
+  uint16_t* out;
+  float* lse;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* kv;
+  const uint16_t* out;
+  const uint16_t* dout;
+  const float* lse;
+  int64_t s_q, s_kv;
+  float scale, scale_log2;
+  int64_t G, NB, qcap, rcap;
+  const int* qcount;
+  const int* xcount;
+  const int* xtotal;
+  const int32_t* qrow;
+  const uint8_t* qmask;
+  const int2* ktab;
+  const int32_t* krtok;
+  const unsigned long long* krmask;
+  float* delta;       // [s_q * H] rowsum(dout * out), written by the dq pass
+  uint16_t* dq;
+  uint16_t* dkv;      // may be null
+  float* dkv_f32;     // may be null
+  int accumulate;
+};
+
+hipError_t launch_fill_u32(void* ptr, size_t n_words, uint32_t value, hipStream_t stream);
+hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream);
+hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream);
+hipError_t launch_validate(const int32_t* idx, int64_t n, int64_t s_kv,
+                           unsigned long long* n_bad, hipStream_t stream);
+
+}  // namespace smla

@@ -1,0 +1,246 @@
+// Index planning for sparse-MLA attention (gfx950).
+//
+// The top-k index rows are turned into two structures that let the compute
+// kernels share gathered KV tiles between query tokens:
+//
+//  * query-major: for every query group of T = 64/H consecutive tokens, the
+//    union of the KV rows its tokens select (ascending), each with a T-bit
+//    mask of the tokens that select it.  A token that lists a row more than
+//    once gets one extra entry per repeat (mask = that token only), appended
+//    after the union, so every slot stays its own softmax term.
+//  * kv-major: for every 64-row KV block, the (token, 64-bit row mask)
+//    records of the tokens that select rows of that block, stored per group
+//    and indexed by a [block, group] table.  Walking the table in group order
+//    visits the records sorted by (block, token): a deterministic order for
+//    the per-row dKV reduction.
+//
+// A slot is valid iff 0 <= index < s_kv; -1 (padding) and any other value are
+// skipped, so padding never reaches memory (miles PR #2079 digest, "fix GLM-5
+// sparse-MLA kernel -1 index OOB and NaN gradients", 实现拆解 item 1: -1 used
+// to address the element before the KV buffer).
+#include "smla_device.h"
+#include "smla_internal.h"
+
+namespace smla {
+
+namespace {
+
+constexpr int WIN_BITS = 16384;            // kv rows per bitmap window
+constexpr int WIN_WORDS = WIN_BITS / 32;   // 512: two per thread
+constexpr int WIN_BLOCKS = WIN_BITS / 64;  // 256: one per thread
+constexpr int XFLAG_WORDS = 4096;          // T * topk <= 8 * 16384 slots
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <int T>
+__global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
+  __shared__ unsigned bm[T][WIN_WORDS];      // per-token row bitmaps of one window
+  __shared__ unsigned xflag[XFLAG_WORDS];    // slots that repeat an earlier slot's row
+  __shared__ int scratch[8];
+  __shared__ int s_lo, s_hi;
+
+  const int tid = threadIdx.x;
+  const int64_t g = blockIdx.x;
+  const int64_t t0 = g * T;
+  const int nt = (int)min<int64_t>(T, a.s_q - t0);
+  const int K = a.topk;
+  const int nslots = nt * K;
+  const int32_t* ix = a.idx + t0 * K;
+  const int nxw = (nslots + 31) >> 5;
+  const int skv = (int)a.s_kv;
+
+  if (tid == 0) {
+    s_lo = 0x7fffffff;
+    s_hi = -1;
+  }
+  for (int w = tid; w < nxw; w += 256) xflag[w] = 0u;
+  __syncthreads();
+
+  // Span of the valid rows this group selects.
+  int lo = 0x7fffffff, hi = -1;
+  for (int s = tid; s < nslots; s += 256) {
+    const int v = ix[s];
+    if (v >= 0 && v < skv) {
+      lo = min(lo, v);
+      hi = max(hi, v);
+    }
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if ((tid & 63) == 0) {
+    atomicMin(&s_lo, lo);
+    atomicMax(&s_hi, hi);
+  }
+  __syncthreads();
+  lo = s_lo;
+  hi = s_hi;
+
+  int32_t* qrow = a.qrow + g * a.qcap;
+  uint8_t* qmask = a.qmask + g * a.qcap;
+  int qbase = 0, rbase = 0;
+  // Windows start on a 64-row block boundary so kv blocks never straddle two.
+  for (int w0 = (hi >= 0 ? (lo & ~63) : 1); w0 <= hi; w0 += WIN_BITS) {
+    for (int i = tid; i < T * WIN_WORDS; i += 256) (&bm[0][0])[i] = 0u;
+    __syncthreads();
+    for (int s = tid; s < nslots; s += 256) {
+      const int v = ix[s];
+      if (v >= w0 && v < w0 + WIN_BITS && v < skv) {
+        const int t = s / K;
+        const int bit = v - w0;
+        const unsigned m = 1u << (bit & 31);
+        const unsigned old = atomicOr(&bm[t][bit >> 5], m);
+        if (old & m) atomicOr(&xflag[s >> 5], 1u << (s & 31));
+      }
+    }
+    __syncthreads();
+
+    // Union entries, ascending row order: thread tid owns words 2tid, 2tid+1.
+    unsigned U[2];
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int w = 2 * tid + k;
+      unsigned u = 0;
+#pragma unroll
+      for (int t = 0; t < T; ++t) u |= bm[t][w];
+      U[k] = u;
+      c += __popc(u);
+    }
+    int total;
+    int pos = qbase + block_exclusive_scan256(c, scratch, &total);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int w = 2 * tid + k;
+      unsigned u = U[k];
+      while (u) {
+        const int b = __ffs(u) - 1;
+        u &= u - 1;
+        unsigned mask = 0;
+#pragma unroll
+        for (int t = 0; t < T; ++t) mask |= ((bm[t][w] >> b) & 1u) << t;
+        qrow[pos] = w0 + 32 * w + b;
+        qmask[pos] = (uint8_t)mask;
+        ++pos;
+      }
+    }
+    qbase += total;
+
+    if (a.ktab) {
+      // kv-block records: thread tid owns block (w0 >> 6) + tid.
+      unsigned long long mk[T];
+      int cnt = 0;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        mk[t] = (unsigned long long)bm[t][2 * tid] |
+                ((unsigned long long)bm[t][2 * tid + 1] << 32);
+        cnt += (mk[t] != 0ull);
+      }
+      int rtotal;
+      const int rpos = rbase + block_exclusive_scan256(cnt, scratch, &rtotal);
+      if (cnt) {
+        const int64_t b = (int64_t)(w0 >> 6) + tid;  // < NB: a set bit is a row < s_kv
+        a.ktab[b * a.G + g] = make_int2(rpos, cnt);
+        int64_t r = g * a.rcap + rpos;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          if (mk[t]) {
+            a.krtok[r] = (int32_t)(t0 + t);
+            a.krmask[r] = mk[t];
+            ++r;
+          }
+        }
+      }
+      rbase += rtotal;
+    }
+    __syncthreads();  // bm is cleared by the next window
+  }
+
+  // Repeated slots, in slot order: one extra union entry each.
+  const int wpt = (nxw + 255) / 256;
+  const int wb = min(nxw, tid * wpt), we = min(nxw, wb + wpt);
+  int c = 0;
+  for (int w = wb; w < we; ++w) c += __popc(xflag[w]);
+  int xtot;
+  int pos = qbase + block_exclusive_scan256(c, scratch, &xtot);
+  for (int w = wb; w < we; ++w) {
+    unsigned f = xflag[w];
+    while (f) {
+      const int b = __ffs(f) - 1;
+      f &= f - 1;
+      const int s = 32 * w + b;
+      const int t = s / K;
+      qrow[pos] = ix[s];
+      qmask[pos] = (uint8_t)(1u << t);
+      ++pos;
+    }
+  }
+  if (tid == 0) {
+    a.qcount[g] = qbase + xtot;
+    a.xcount[g] = xtot;
+    if (xtot) atomicAdd(a.xtotal, xtot);
+  }
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = v;
+}
+
+__global__ void validate_kernel(const int32_t* idx, int64_t n, int64_t s_kv,
+                                unsigned long long* n_bad) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  unsigned long long c = 0;
+  for (; i < n; i += stride) {
+    const int v = idx[i];
+    c += (v != -1 && (v < 0 || v >= s_kv)) ? 1ull : 0ull;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if ((threadIdx.x & 63) == 0 && c) atomicAdd(n_bad, c);
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream) {
+  if (a.G == 0) return hipSuccess;
+  dim3 grid((unsigned)a.G), block(256);
+  switch (heads) {
+    case 8: plan_kernel<8><<<grid, block, 0, stream>>>(a); break;
+    case 16: plan_kernel<4><<<grid, block, 0, stream>>>(a); break;
+    case 32: plan_kernel<2><<<grid, block, 0, stream>>>(a); break;
+    case 64: plan_kernel<1><<<grid, block, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(void* ptr, size_t n_words, uint32_t value, hipStream_t stream) {
+  if (n_words == 0) return hipSuccess;
+  size_t blocks = (n_words + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  fill_u32_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>((uint32_t*)ptr, n_words, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate(const int32_t* idx, int64_t n, int64_t s_kv,
+                           unsigned long long* n_bad, hipStream_t stream) {
+  hipError_t e = launch_fill_u32(n_bad, 2, 0u, stream);
+  if (e != hipSuccess || n == 0) return e;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  validate_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(idx, n, s_kv, n_bad);
+  return hipGetLastError();
+}
+
+}  // namespace smla

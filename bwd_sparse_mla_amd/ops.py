@@ -1,0 +1,267 @@
+"""Python binding of libsmla: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(include/smla.h).  PyTorch provides device memory and the current stream.
+
+Accepted layouts (packed "thd" tokens, one KV group):
+  q        [S, H, 576]  or [1, S, H, 576]                bf16
+  kv       [S_kv, 576], [S_kv, 1, 576] or [1, S_kv, 1, 576]  bf16
+  indices  [S, K], [S, 1, K] or [1, S, 1, K]            int32 or int64 (-1 = padding)
+  dout     like out: q's leading dims + (512,)           bf16
+Outputs keep the caller's leading dims: out [..., 512], lse [..., H] fp32,
+dq like q, dkv like kv.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+D_V = 512
+D_K = 576
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _flat_q(q: torch.Tensor) -> torch.Tensor:
+    if q.dim() == 4:
+        if q.shape[0] != 1:
+            raise ValueError("q with a batch dimension must have batch 1 (packed layout)")
+        q = q[0]
+    if q.dim() != 3 or q.shape[-1] != D_K:
+        raise ValueError(f"q must be [S, H, {D_K}], got {tuple(q.shape)}")
+    return q
+
+
+def _flat_kv(kv: torch.Tensor) -> torch.Tensor:
+    if kv.dim() == 4:
+        if kv.shape[0] != 1:
+            raise ValueError("kv with a batch dimension must have batch 1")
+        kv = kv[0]
+    if kv.dim() == 3:
+        if kv.shape[1] != 1:
+            raise ValueError("only one KV group is supported")
+        kv = kv[:, 0]
+    if kv.dim() != 2 or kv.shape[-1] != D_K:
+        raise ValueError(f"kv must be [S_kv, {D_K}], got {tuple(kv.shape)}")
+    return kv
+
+
+def _flat_idx(idx: torch.Tensor) -> torch.Tensor:
+    if idx.dim() == 4:
+        if idx.shape[0] != 1:
+            raise ValueError("indices with a batch dimension must have batch 1")
+        idx = idx[0]
+    if idx.dim() == 3:
+        if idx.shape[1] != 1:
+            raise ValueError("only one KV group is supported")
+        idx = idx[:, 0]
+    if idx.dim() != 2:
+        raise ValueError(f"indices must be [S, K], got {tuple(idx.shape)}")
+    return idx
+
+
+def _prep(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.contiguous()
+
+
+def _workspace(nbytes: int, device) -> tuple[torch.Tensor, int]:
+    """A device buffer of nbytes with a 256-byte aligned start; returns
+    (owner tensor, aligned address)."""
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    addr = buf.data_ptr()
+    return buf, (addr + 255) & ~255
+
+
+def fwd_workspace_bytes(s_q: int, s_kv: int, heads: int, topk: int) -> int:
+    n = _lib.load().smla_fwd_workspace_size(s_q, s_kv, heads, topk)
+    if n == 0:
+        raise ValueError("unsupported shape for smla_fwd")
+    return n
+
+
+def bwd_workspace_bytes(s_q: int, s_kv: int, heads: int, topk: int, flags: int = 0) -> int:
+    n = _lib.load().smla_bwd_workspace_size(s_q, s_kv, heads, topk, flags)
+    if n == 0:
+        raise ValueError("unsupported shape for smla_bwd")
+    return n
+
+
+def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_scale: float,
+                   out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Forward: returns (out [..., H, 512] bf16, lse [..., H] fp32, natural log)."""
+    lib = _lib.load()
+    lead = q.shape[:-1]
+    q3 = _prep(_flat_q(q), torch.bfloat16, "q")
+    kv2 = _prep(_flat_kv(kv), torch.bfloat16, "kv")
+    ix = _flat_idx(indices)
+    if ix.dtype != torch.int32:
+        ix = ix.to(torch.int32)
+    ix = _prep(ix, torch.int32, "indices")
+    S, H, _ = q3.shape
+    if ix.shape[0] != S:
+        raise ValueError("indices must have one row per query token")
+    K = ix.shape[1]
+    S_kv = kv2.shape[0]
+    dev = q3.device
+    if out is None:
+        out = torch.empty(*lead[:-1], H, D_V, dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty(*lead[:-1], H, dtype=torch.float32, device=dev)
+    ws, ws_addr = _workspace(fwd_workspace_bytes(S, S_kv, H, K), dev)
+    _lib.check(lib.smla_fwd(_ptr(q3), _ptr(kv2), _ptr(ix), S, S_kv, H, K, float(sm_scale),
+                            _ptr(out), _ptr(lse), ctypes.c_void_p(ws_addr),
+                            ws.numel() - (ws_addr - ws.data_ptr()), _stream(dev)))
+    return out, lse
+
+
+def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                   indices: torch.Tensor, lse: torch.Tensor, sm_scale: float, *,
+                   dkv_f32: torch.Tensor | None = None, accumulate: bool = False,
+                   want_bf16_dkv: bool = True):
+    """Backward: returns (dq like q, dkv like kv in bf16 or None).
+
+    dkv_f32, if given, is an fp32 [S_kv, 576] tensor that receives the fp32
+    dkv (overwritten, or added to with accumulate=True).  The default mode is
+    the deterministic per-row reduction."""
+    lib = _lib.load()
+    q3 = _prep(_flat_q(q), torch.bfloat16, "q")
+    kv2 = _prep(_flat_kv(kv), torch.bfloat16, "kv")
+    S, H, _ = q3.shape
+    o3 = _prep(out.reshape(S, H, D_V), torch.bfloat16, "out")
+    do3 = _prep(dout.reshape(S, H, D_V), torch.bfloat16, "dout")
+    ls = _prep(lse.reshape(S, H), torch.float32, "lse")
+    ix = _flat_idx(indices)
+    if ix.dtype != torch.int32:
+        ix = ix.to(torch.int32)
+    ix = _prep(ix, torch.int32, "indices")
+    if ix.shape[0] != S:
+        raise ValueError("indices must have one row per query token")
+    K = ix.shape[1]
+    S_kv = kv2.shape[0]
+    dev = q3.device
+    flags = 0
+    if accumulate:
+        if dkv_f32 is None:
+            raise ValueError("accumulate=True needs dkv_f32")
+        flags |= _lib.SMLA_DKV_ACCUMULATE
+    if dkv_f32 is not None:
+        if dkv_f32.dtype != torch.float32 or not dkv_f32.is_contiguous() \
+                or dkv_f32.numel() != S_kv * D_K:
+            raise ValueError("dkv_f32 must be a contiguous fp32 tensor of S_kv*576 elements")
+    dq = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    dkv = torch.empty(kv.shape, dtype=torch.bfloat16, device=dev) if want_bf16_dkv else None
+    ws, ws_addr = _workspace(bwd_workspace_bytes(S, S_kv, H, K, flags), dev)
+    _lib.check(lib.smla_bwd(_ptr(q3), _ptr(kv2), _ptr(o3), _ptr(do3), _ptr(ix), _ptr(ls),
+                            S, S_kv, H, K, float(sm_scale), _ptr(dq), _ptr(dkv), _ptr(dkv_f32),
+                            flags, ctypes.c_void_p(ws_addr),
+                            ws.numel() - (ws_addr - ws.data_ptr()), _stream(dev)))
+    return dq, dkv
+
+
+def validate_indices(indices: torch.Tensor, s_kv: int) -> int:
+    """Number of index entries that are neither -1 nor in [0, s_kv).
+    (Synchronizes the current stream to read the count.)"""
+    lib = _lib.load()
+    ix = _flat_idx(indices)
+    if ix.dtype != torch.int32:
+        ix = ix.to(torch.int32)
+    ix = _prep(ix, torch.int32, "indices")
+    cnt = torch.empty(1, dtype=torch.int64, device=ix.device)
+    _lib.check(lib.smla_validate_indices(_ptr(ix), ix.shape[0], ix.shape[1], s_kv, _ptr(cnt),
+                                         _stream(ix.device)))
+    return int(cnt.item())
+
+
+class SparseMLA(torch.autograd.Function):
+    """out = SparseMLA.apply(q, kv, indices, sm_scale): differentiable in q and kv."""
+
+    @staticmethod
+    def forward(ctx, q, kv, indices, sm_scale):
+        out, lse = sparse_mla_fwd(q, kv, indices, sm_scale)
+        ctx.save_for_backward(q, kv, indices, out, lse)
+        ctx.sm_scale = sm_scale
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        q, kv, indices, out, lse = ctx.saved_tensors
+        dq, dkv = sparse_mla_bwd(q, kv, out, grad_out.contiguous(), indices, lse, ctx.sm_scale)
+        return dq, dkv, None, None
+
+
+class SparseMLARunner:
+    """Repeated forward + backward on fixed shapes with every buffer
+    preallocated: each call enqueues the library's kernels and allocates
+    nothing.  Inputs must already be contiguous bf16/int32 GPU tensors of the
+    shapes given here."""
+
+    def __init__(self, s_q: int, s_kv: int, heads: int, topk: int, device="cuda"):
+        self.lib = _lib.load()
+        self.shape = (s_q, s_kv, heads, topk)
+        dev = torch.device(device)
+        self.out = torch.empty(s_q, heads, D_V, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(s_q, heads, dtype=torch.float32, device=dev)
+        self.dq = torch.empty(s_q, heads, D_K, dtype=torch.bfloat16, device=dev)
+        self.dkv = torch.empty(s_kv, D_K, dtype=torch.bfloat16, device=dev)
+        fb = fwd_workspace_bytes(s_q, s_kv, heads, topk)
+        bb = bwd_workspace_bytes(s_q, s_kv, heads, topk)
+        self._fws, self._fws_addr = _workspace(fb, dev)
+        self._bws, self._bws_addr = _workspace(bb, dev)
+        self._fb, self._bb = fb, bb
+        self.device = dev
+
+    def _check(self, q, kv, idx, dout=None):
+        s_q, s_kv, h, k = self.shape
+        assert q.shape == (s_q, h, D_K) and q.dtype == torch.bfloat16 and q.is_contiguous()
+        assert kv.shape == (s_kv, D_K) and kv.dtype == torch.bfloat16 and kv.is_contiguous()
+        assert idx.shape == (s_q, k) and idx.dtype == torch.int32 and idx.is_contiguous()
+        if dout is not None:
+            assert dout.shape == (s_q, h, D_V) and dout.dtype == torch.bfloat16
+            assert dout.is_contiguous()
+
+    def fwd(self, q, kv, idx, sm_scale):
+        s_q, s_kv, h, k = self.shape
+        _lib.check(self.lib.smla_fwd(_ptr(q), _ptr(kv), _ptr(idx), s_q, s_kv, h, k,
+                                     float(sm_scale), _ptr(self.out), _ptr(self.lse),
+                                     ctypes.c_void_p(self._fws_addr), self._fb,
+                                     _stream(self.device)))
+        return self.out, self.lse
+
+    def bwd(self, q, kv, dout, idx, sm_scale):
+        s_q, s_kv, h, k = self.shape
+        _lib.check(self.lib.smla_bwd(_ptr(q), _ptr(kv), _ptr(self.out), _ptr(dout), _ptr(idx),
+                                     _ptr(self.lse), s_q, s_kv, h, k, float(sm_scale),
+                                     _ptr(self.dq), _ptr(self.dkv), ctypes.c_void_p(0), 0,
+                                     ctypes.c_void_p(self._bws_addr), self._bb,
+                                     _stream(self.device)))
+        return self.dq, self.dkv
+
+
+def timing_start(max_launches: int) -> None:
+    """Bracket every kernel the library launches with HIP events (benchmarks)."""
+    _lib.check(_lib.load().smla_timing_start(max_launches))
+
+
+def timing_stop() -> None:
+    _lib.check(_lib.load().smla_timing_stop())
+
+
+def timing_read(kernel: str) -> tuple[int, float]:
+    """(launches recorded, total milliseconds) for one kernel name."""
+    n = ctypes.c_int(0)
+    ms = ctypes.c_double(0.0)
+    _lib.check(_lib.load().smla_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value

@@ -1,0 +1,145 @@
+/*
+ * smla.h -- C ABI of libsmla: DSA sparse-MLA attention, forward and backward,
+ * native on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (absorbed-latent layout, one KV group shared by all heads):
+ * each query token s has H heads of 576-wide queries and a row of `topk`
+ * indices into a shared latent KV of 576-wide rows.  Index -1 marks a padding
+ * slot.  Keys are the whole 576-wide rows, values their first 512 columns.
+ *
+ *   forward:   out[s,h,:] = sum_k p_k kv[J_k, :512],  p = softmax_k(scale * q[s,h] . kv[J_k])
+ *              lse[s,h]   = natural-log normaliser of that softmax
+ *   backward:  dq, dkv of the loss sum(dout * out), given out and lse
+ *
+ * Sources: the backward call takes (q, kv, out, dout, indices, lse, sm_scale)
+ * and returns (dq, dkv), with the value width fixed at 512 (slime issue
+ * #2201, "GLM-5.2 SparseMLA TileLang backward returns NaN gradients from
+ * finite inputs", sections Strongest repro evidence and Suspected area).
+ * Padding slots contribute exactly zero, the per-head softmax denominator is
+ * floored at 1e-30 so an all-padding row outputs exact zeros with a finite
+ * LSE, and dkv is accumulated through the indices (miles PR #2079 digest,
+ * "fix GLM-5 sparse-MLA kernel -1 index OOB and NaN gradients", section
+ * 实现拆解 items 1-3 and the key code snippets).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are device pointers owned by the caller, row-major
+ *    and contiguous, 16-byte aligned.  bf16 tensors are passed as void*.
+ *  - q [s_q, heads, 576] bf16; kv [s_kv, 576] bf16 (one KV group);
+ *    indices [s_q, topk] int32; out and dout [s_q, heads, 512] bf16;
+ *    lse [s_q, heads] fp32 (natural log); dq [s_q, heads, 576] bf16;
+ *    dkv [s_kv, 576] bf16; dkv_f32 [s_kv, 576] fp32.
+ *  - A slot is valid iff 0 <= index < s_kv.  -1 is padding.  Any other value
+ *    is a contract violation; the kernels treat it as padding (they never
+ *    read or write outside the buffers) and smla_validate_indices counts it.
+ *  - Supported: heads in {8, 16, 32, 64}; 1 <= topk <= 16384;
+ *    1 <= s_kv < 2^24; s_q >= 0.  With s_q == 0 the pointers of the q-sized
+ *    tensors (q, indices, out, dout, lse, dq) may be NULL; the forward then
+ *    launches nothing and the backward only writes dkv (zeros).
+ *  - Every call returns SMLA_OK (0) or a positive error code.  Argument errors
+ *    are returned before anything is launched; smla_last_error() then gives a
+ *    message (thread-local).  No exception crosses the ABI.
+ *  - The library never allocates device memory and never synchronizes: work
+ *    is enqueued on `stream` (a hipStream_t; NULL is the default stream) and
+ *    the call returns.  Scratch space comes from the caller's `workspace`,
+ *    whose size the *_workspace_size queries give.  A workspace must not be
+ *    shared by calls that may run concurrently.
+ *  - Inputs must be finite.  A nonfinite value in a kv row selected by one
+ *    token can reach the other tokens of its query group through zero
+ *    probabilities; rows never selected are never read.
+ */
+#ifndef SMLA_H_
+#define SMLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMLA_ABI_VERSION 1
+
+enum smla_status {
+  SMLA_OK = 0,
+  SMLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SMLA_ERR_SHAPE = 2,       /* unsupported heads/topk/s_kv, or negative sizes */
+  SMLA_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  SMLA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
+  SMLA_ERR_FLAGS = 5,       /* unknown flag bits, or a flag without its buffer */
+  SMLA_ERR_HIP = 6,         /* a HIP launch failed */
+  SMLA_ERR_DEVICE = 7       /* the current device is not gfx950 */
+};
+
+/* smla_bwd flags.  flags == 0 is the default, deterministic mode: dkv is a
+ * per-row reduction over the (token, slot) pairs sorted by kv row, bitwise
+ * reproducible run to run. */
+#define SMLA_DKV_ACCUMULATE 1u  /* add into the caller's fp32 dkv_f32 instead of
+                                   overwriting it; rows no valid slot selects
+                                   are left untouched (bit for bit) */
+#define SMLA_DKV_ATOMIC 2u      /* accumulate dkv with fp32 atomics from the
+                                   query-major pass (not bitwise reproducible) */
+
+/* Forward.
+ * in:  q, kv, indices, sm_scale (the softmax scale applied to q . k).
+ * out: out [s_q, heads, 512] bf16 -- exact zeros for rows without a valid slot;
+ *      lse [s_q, heads] fp32 natural log -- ln(1e-30) for rows without a valid
+ *      slot, otherwise max_k z_k + ln(sum_k exp(z_k - max)).
+ * workspace: at least smla_fwd_workspace_size(...) bytes, 256-byte aligned. */
+int smla_fwd(const void* q, const void* kv, const int32_t* indices,
+             int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk, float sm_scale,
+             void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t smla_fwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk);
+
+/* Backward.
+ * in:  q, kv, indices and sm_scale as given to the forward; out and lse as the
+ *      forward returned them (delta = rowsum(dout * out) uses this out, the
+ *      probabilities are recomputed as exp(scale q.k - lse) from this lse);
+ *      dout [s_q, heads, 512] bf16.
+ * out: dq [s_q, heads, 576] bf16 (required);
+ *      dkv [s_kv, 576] bf16 (may be NULL if only dkv_f32 is wanted);
+ *      dkv_f32 [s_kv, 576] fp32 (may be NULL; required with SMLA_DKV_ACCUMULATE).
+ *      Rows of dkv that no valid slot selects are exact zeros (without
+ *      SMLA_DKV_ACCUMULATE).  dkv and dkv_f32 must not both be NULL.
+ * flags: 0, SMLA_DKV_ACCUMULATE and/or SMLA_DKV_ATOMIC.
+ * workspace: at least smla_bwd_workspace_size(...) bytes, 256-byte aligned. */
+int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
+             const int32_t* indices, const float* lse,
+             int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk, float sm_scale,
+             void* dq, void* dkv, float* dkv_f32, uint32_t flags,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+size_t smla_bwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
+                               uint32_t flags);
+
+/* Counts index entries that are neither -1 nor in [0, s_kv) and stores the
+ * count in *n_bad (a device pointer to one uint64, overwritten). */
+int smla_validate_indices(const int32_t* indices, int64_t s_q, int32_t topk, int64_t s_kv,
+                          unsigned long long* n_bad, void* stream);
+
+/* Kernel timing, for benchmarks (not thread-safe).  Between
+ * smla_timing_start(max_launches) and smla_timing_stop(), every kernel this
+ * library launches is bracketed by two HIP events recorded on its stream (at
+ * most max_launches kernels are recorded; the events are created by
+ * smla_timing_start and destroyed by the next start).  smla_timing_read waits
+ * for the recorded events of the kernels named `kernel` ("fill", "plan",
+ * "fwd", "bwd_dq", "bwd_dkv", "validate") and returns how many were recorded
+ * and their summed duration in milliseconds. */
+int smla_timing_start(int max_launches);
+int smla_timing_stop(void);
+int smla_timing_read(const char* kernel, int* launches, double* total_ms);
+
+/* Message of the last error returned on this thread ("" if none). */
+const char* smla_last_error(void);
+
+/* SMLA_ABI_VERSION of the built library. */
+int smla_version(void);
+
+/* 1 if `device` is a gfx950 GPU this library was built for, else 0. */
+int smla_device_supported(int device);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H_ */

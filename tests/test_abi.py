@@ -1,0 +1,111 @@
+"""The C ABI library: it loads, exports every entry point include/smla.h
+declares, and rejects bad arguments before launching anything (no GPU needed:
+argument checks run before the device is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bwd_sparse_mla_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libsmla.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_pages_calls():
+    names = declared_functions()
+    assert "smla_fwd" in names and "smla_bwd" in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from bwd_sparse_mla_amd import _lib
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks {name}"
+
+
+def test_version_and_workspace_queries(lib):
+    assert lib.smla_version() == 1
+    fwd = lib.smla_fwd_workspace_size(4096, 4096, 8, 2048)
+    bwd = lib.smla_bwd_workspace_size(4096, 4096, 8, 2048, 0)
+    assert 0 < fwd < bwd
+    assert lib.smla_fwd_workspace_size(4096, 4096, 12, 2048) == 0     # unsupported heads
+    assert lib.smla_fwd_workspace_size(4096, 4096, 8, 0) == 0         # topk < 1
+    assert lib.smla_bwd_workspace_size(16, 1 << 24, 8, 8, 0) == 0     # s_kv too large
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: the checks return first
+
+
+def call_fwd(lib, q=FAKE, kv=FAKE, idx=FAKE, s_q=16, s_kv=16, heads=8, topk=4, out=FAKE,
+             lse=FAKE, ws=FAKE, ws_bytes=None):
+    P = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = lib.smla_fwd_workspace_size(s_q, s_kv, heads, topk) or 1
+    return lib.smla_fwd(P(q), P(kv), P(idx), s_q, s_kv, heads, topk, 0.1, P(out), P(lse), P(ws),
+                        ws_bytes, P(0))
+
+
+def test_fwd_argument_errors(lib):
+    from bwd_sparse_mla_amd import _lib
+    assert call_fwd(lib, heads=12) == 2
+    assert call_fwd(lib, topk=0) == 2
+    assert call_fwd(lib, s_kv=0) == 2
+    assert call_fwd(lib, s_q=-1) == 2
+    assert call_fwd(lib, q=0) == 1
+    assert call_fwd(lib, kv=0, s_q=0) == 1
+    assert call_fwd(lib, lse=0) == 1
+    assert call_fwd(lib, kv=FAKE + 2) == 3
+    assert call_fwd(lib, ws=FAKE + 16) == 3
+    assert call_fwd(lib, ws_bytes=10) == 4
+    assert call_fwd(lib, ws=0) == 4
+    assert b"workspace" in lib.smla_last_error()
+    with pytest.raises(_lib.SmlaError):
+        _lib.check(call_fwd(lib, heads=12))
+
+
+def call_bwd(lib, flags=0, dkv=FAKE, dkv32=FAKE, dq=FAKE, heads=8, ws_bytes=None):
+    P = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = lib.smla_bwd_workspace_size(16, 16, heads, 4, flags) or 1
+    return lib.smla_bwd(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 16, 16, heads, 4,
+                        0.1, P(dq), P(dkv), P(dkv32), flags, P(FAKE), ws_bytes, P(0))
+
+
+def test_bwd_argument_errors(lib):
+    assert call_bwd(lib, heads=7) == 2
+    assert call_bwd(lib, dq=0) == 1
+    assert call_bwd(lib, dkv=0, dkv32=0) == 1
+    assert call_bwd(lib, flags=8) == 5
+    assert call_bwd(lib, flags=1, dkv32=0) == 5
+    assert call_bwd(lib, dkv32=FAKE + 4) == 3
+    assert call_bwd(lib, ws_bytes=64) == 4
+
+
+def test_validate_argument_errors(lib):
+    P = ctypes.c_void_p
+    assert lib.smla_validate_indices(P(FAKE), 4, 4, 4, P(0), P(0)) == 1
+    assert lib.smla_validate_indices(P(FAKE), 4, 0, 4, P(FAKE), P(0)) == 2
+    assert lib.smla_validate_indices(P(FAKE), 4, 4, 4, P(FAKE + 4), P(0)) == 3
+
+
+def test_no_cpu_fallback_in_product_package():
+    """The product package never imports the oracle or computes on the CPU."""
+    pkg = os.path.join(ROOT, "bwd_sparse_mla_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            text = open(os.path.join(pkg, fn)).read()
+            assert "oracle" not in text.replace("never imports the oracle", ""), fn
