@@ -34,24 +34,48 @@ namespace {
 // ---------------------------------------------------------------------------
 // dq pass
 // ---------------------------------------------------------------------------
+// Query group of T = 64/H tokens (64 rows), union tiles of 32 kv rows,
+// double buffered.  dout of the group's rows lives in LDS (it is the A operand
+// of dP), Q in registers; per tile each wave computes scores and dP for its 16
+// rows, then dq += dS . K for all 64 rows and its 144 output columns.
+constexpr int DQ_TILE = 32;
+
 template <int H>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
-  __shared__ __attribute__((aligned(16))) char sK[2][TILE_KV * TILE_STRIDE];
-  __shared__ __attribute__((aligned(16))) unsigned short sdS[GROUP_ROWS * 72];
-  __shared__ int sMask[2][TILE_KV];
+  constexpr int SDS = DQ_TILE + 8;  // dS row stride (bf16): 80 bytes, conflict-free reads
+  __shared__ __attribute__((aligned(16))) char sK[2][kv_tile_bytes(DQ_TILE)];
+  __shared__ __attribute__((aligned(16))) char sDO[GROUP_ROWS * DO_STRIDE];
+  __shared__ __attribute__((aligned(16))) unsigned short sdS[GROUP_ROWS * SDS];
+  __shared__ __attribute__((aligned(16))) unsigned char sMask[2][256];   // token masks (copied as words)
+  __shared__ __attribute__((aligned(16))) int sRow[2][64];   // kv row indices of a tile's entries
   __shared__ float sDelta[GROUP_ROWS];
   __shared__ float sLse2[GROUP_ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, r16 = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int64_t grp = blockIdx.x;
   const int64_t t0 = grp * T;
   const int n_ent = a.qcount[grp];
   const int32_t* erow = a.qrow + grp * a.qcap;
   const uint8_t* emask = a.qmask + grp * a.qcap;
-  const int ntiles = (n_ent + TILE_KV - 1) / TILE_KV;
+  const int ntiles = (n_ent + DQ_TILE - 1) / DQ_TILE;
 
+  // dout rows of the group into LDS (64 rows x 65 chunks = 65 copies).
+  {
+    const uint64_t zero = reinterpret_cast<uint64_t>(g_zero16);
+#pragma unroll 1
+    for (int i = wv; i < DO_STRIDE_CHUNKS; i += 4) {
+      const int p = i * 64 + lane;
+      const int row = p / DO_STRIDE_CHUNKS, cc = p - row * DO_STRIDE_CHUNKS;
+      const int64_t tok = t0 + row / H;
+      const uint64_t src =
+          reinterpret_cast<uint64_t>(a.dout + (tok * H + row % H) * D_V + 8 * cc);
+      g2lds16(reinterpret_cast<const void*>((cc < DO_CHUNKS && tok < a.s_q) ? src : zero),
+              sDO + i * 1024);
+    }
+  }
   // delta = rowsum(dout * out) for the group's 64 rows (4 threads per row).
   {
     const int row = tid >> 2, part = tid & 3;
@@ -80,24 +104,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  short8_t qf[18], dof[16];
+  short8_t qf[18];
   {
     const int rr = 16 * wave + r16;
     const int64_t tok = t0 + rr / H;
     if (tok < a.s_q) {
       const uint16_t* qrow = a.q + (tok * H + rr % H) * D_K + 8 * g16;
-      const uint16_t* drow = a.dout + (tok * H + rr % H) * D_V + 8 * g16;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) qf[ks] = ld16_global(qrow + 32 * ks);
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) dof[ks] = ld16_global(drow + 32 * ks);
     } else {
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) qf[ks] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) dof[ks] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
+  wait_vmcnt0();
   __syncthreads();
   int tl[4];
   float del[4], ls2[4];
@@ -115,114 +135,144 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int tile, int buf) {
-    gather_kv_tile<TILE_KV>(sK[buf], a.kv, a.s_kv, erow, tile * TILE_KV,
-                            min(TILE_KV, n_ent - tile * TILE_KV), wv, lane);
-    if (tid < TILE_KV) {
-      const int e = tile * TILE_KV + tid;
-      sMask[buf][tid] = e < n_ent ? (int)emask[e] : 0;
-    }
+  // Tile t's kv rows are copied from rows_t (LDS); masks of tile t+1 and row
+  // indices of tile t+2 follow by direct copies.
+  auto issue = [&](int tile, char* kbuf, const int* rows_t, unsigned char* mbuf, int* rows_t2) __attribute__((always_inline)) {
+    gather_kv_tile<DQ_TILE>(kbuf, a.kv, a.s_kv, rows_t, min(DQ_TILE, n_ent - tile * DQ_TILE), wv,
+                            lane);
+    copy_union_entries(nullptr, mbuf, erow, emask, tile * DQ_TILE, n_ent, DQ_TILE, wv, 1, 1, lane);
+    if (tile + 1 < ntiles)
+      copy_union_entries(rows_t2, nullptr, erow, emask, (tile + 1) * DQ_TILE, n_ent, DQ_TILE, wv,
+                         2, 2, lane);
   };
 
-  if (ntiles > 0) issue(0, 0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
+  const char* drow = sDO + (16 * wave + r16) * DO_STRIDE + 16 * g16;  // A fragments of dout
+  auto step = [&](int tile, const char* kt, const unsigned char* mkb, char* knext,
+                  unsigned char* mnext, const int* rnext, int* rcur) __attribute__((always_inline)) {
     wait_vmcnt0();
     __syncthreads();
-    const char* kt = sK[buf];
-
-    float4_t s[4], dp[4];
+    // Prefetch the next tile into the other buffer (free: every wave has
+    // passed the barrier above, so the previous tile's reads are done).
+    if (tile + 1 < ntiles) issue(tile + 1, knext, rnext, mnext, rcur);
+    float4_t s[2], dp[2];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < 2; ++nt) {
       s[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
       dp[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
+      short8_t da;
+      if (ks < 16) da = ld16_lds(drow + 64 * ks);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < 2; ++nt) {
         const short8_t b = ld16_lds(kt + (nt * 16 + r16) * TILE_STRIDE + (4 * ks + g16) * 16);
         s[nt] = mfma_bf16(qf[ks], b, s[nt]);
-        if (ks < 16) dp[nt] = mfma_bf16(dof[ks], b, dp[nt]);
+        if (ks < 16) dp[nt] = mfma_bf16(da, b, dp[nt]);
       }
     }
-    if (tile + 1 < ntiles) issue(tile + 1, buf ^ 1);
-
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int mk = sMask[buf][nt * 16 + r16];
+    for (int nt = 0; nt < 2; ++nt) {
+      const int mk = mkb[nt * 16 + r16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool v = (mk >> tl[i]) & 1;
         const float p = v ? fast_exp2(s[nt][i] * a.scale_log2 - ls2[i]) : 0.f;
         const float ds = p * (dp[nt][i] - del[i]);
-        sdS[(16 * wave + 4 * g16 + i) * 72 + nt * 16 + r16] = f2bf(ds);
+        sdS[(16 * wave + 4 * g16 + i) * SDS + nt * 16 + r16] = f2bf(ds);
       }
     }
     __syncthreads();
-
-    short8_t da[4][2];
+    short8_t dsa[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-        da[rb][k2] = ld16_lds(&sdS[(16 * rb + r16) * 72 + 32 * k2 + 8 * g16]);
+    for (int rb = 0; rb < 4; ++rb) dsa[rb] = ld16_lds(&sdS[(16 * rb + r16) * SDS + 8 * g16]);
 #pragma unroll
     for (int n = 0; n < 9; ++n) {
-      const int col = 144 * wave + 16 * n;
-      const short8_t b0 = ld_b_tr(kt, TILE_STRIDE, 0, col, lane);
-      const short8_t b1 = ld_b_tr(kt, TILE_STRIDE, 32, col, lane);
+      const short8_t b = ld_b_tr(kt, TILE_STRIDE, 0, 144 * wave + 16 * n, lane);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        acc[rb][n] = mfma_bf16(da[rb][0], b0, acc[rb][n]);
-        acc[rb][n] = mfma_bf16(da[rb][1], b1, acc[rb][n]);
-      }
+      for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(dsa[rb], b, acc[rb][n]);
     }
+  };
+
+  if (ntiles > 0) {
+    copy_union_entries(sRow[0], sMask[0], erow, emask, 0, n_ent, DQ_TILE, wv, 0, 1, lane);
+    if (ntiles > 1) copy_union_entries(sRow[1], nullptr, erow, emask, DQ_TILE, n_ent, DQ_TILE, wv, 2, 2, lane);
+    wait_vmcnt0();
+    __syncthreads();
+    gather_kv_tile<DQ_TILE>(sK[0], a.kv, a.s_kv, sRow[0], min(DQ_TILE, n_ent), wv, lane);
+  }
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int b = tile & 1;
+    step(tile, sK[b], sMask[b], sK[b ^ 1], sMask[b ^ 1], sRow[b ^ 1], sRow[b]);
   }
 
-  // Epilogue: dq = scale * acc through LDS, 16-byte stores.
+  // Epilogue: dq = scale * acc, staged through LDS in two halves of 32 rows
+  // (sK[0] holds rows 0..31, sK[1] rows 32..63), then 16-byte stores.
   __syncthreads();
-  unsigned short* so = reinterpret_cast<unsigned short*>(sK[0]);  // [64][584]
-  constexpr int SO = TILE_STRIDE / 2;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < 4; ++rb) {
+    unsigned short* so = reinterpret_cast<unsigned short*>(sK[rb >> 1]);
 #pragma unroll
     for (int n = 0; n < 9; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        so[(16 * rb + 4 * g16 + i) * SO + 144 * wave + 16 * n + r16] = f2bf(acc[rb][n][i] * a.scale);
+        so[(16 * (rb & 1) + 4 * g16 + i) * D_K + 144 * wave + 16 * n + r16] =
+            f2bf(acc[rb][n][i] * a.scale);
+  }
   __syncthreads();
   for (int p = tid; p < GROUP_ROWS * ROW_CHUNKS; p += 256) {
     const int row = p / ROW_CHUNKS, c = p - row * ROW_CHUNKS;
     const int64_t tok = t0 + row / H;
+    const unsigned short* so = reinterpret_cast<const unsigned short*>(sK[row >> 5]);
     if (tok < a.s_q)
       *reinterpret_cast<uint4_t*>(a.dq + (tok * H + row % H) * D_K + 8 * c) =
-          *reinterpret_cast<const uint4_t*>(so + row * SO + 8 * c);
+          *reinterpret_cast<const uint4_t*>(so + (row & 31) * D_K + 8 * c);
   }
 }
 
 // ---------------------------------------------------------------------------
 // dkv pass
 // ---------------------------------------------------------------------------
+// Work item: kv block `blk` (64 rows) and split `split` of the block's chunk
+// list; a chunk is one query group with records for the block (T tokens, 64
+// query rows, contiguous in q / dout / lse / delta).  Chunks are processed as
+// two sub-chunks of 32 query rows, double buffered: every step first issues
+// the direct global->LDS copies of the next sub-chunk (Q, dout, its tokens'
+// row masks, lse, delta -- all addresses computed, no memory read on the way)
+// and then computes the current one.  The item accumulates dkv for the
+// block's 64 rows in registers and writes its fp32 partial sum;
+// dkv_finalize_kernel adds a block's partials in split order.  Launch order is
+// split-major, so every block's first split goes first.
+constexpr int DKV_SUB = 32;                                 // query rows per sub-chunk
+constexpr int DKV_Q_COPIES = kv_tile_copies(DKV_SUB);      // 37
+constexpr int DKV_DO_COPIES = (DKV_SUB * DO_STRIDE_CHUNKS + 63) / 64;  // 33
+constexpr int DKV_COPIES = DKV_Q_COPIES + DKV_DO_COPIES + 3;           // + masks, lse, delta
+
 template <int H>
 __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
-  constexpr int T = GROUP_ROWS / H;   // token slots per chunk = tokens per group
-  __shared__ __attribute__((aligned(16))) char sQ[GROUP_ROWS * TILE_STRIDE];
-  __shared__ __attribute__((aligned(16))) char sDO[GROUP_ROWS * DO_STRIDE];
-  __shared__ __attribute__((aligned(16))) unsigned short sPT[TILE_KV * 72];
-  __shared__ __attribute__((aligned(16))) unsigned short sDST[TILE_KV * 72];
-  __shared__ int2 sTab[256];
-  __shared__ unsigned long long sMask[T];
-  __shared__ int sTok[T];
-  __shared__ float sLse2[GROUP_ROWS];
-  __shared__ float sDel[GROUP_ROWS];
-  __shared__ int scratch[8];
+  constexpr int T = GROUP_ROWS / H;
+  constexpr int SP = DKV_SUB + 8;  // P^T / dS^T row stride (bf16): 80 bytes
+  __shared__ __attribute__((aligned(16))) char sQ[2][DKV_Q_COPIES * 1024];
+  __shared__ __attribute__((aligned(16))) char sD[2][DKV_DO_COPIES * 1024];
+  __shared__ __attribute__((aligned(16))) unsigned sM[2][64];   // T row masks (2 words each)
+  __shared__ __attribute__((aligned(16))) float sL[2][64];      // lse of the 32 rows
+  __shared__ __attribute__((aligned(16))) float sE[2][64];      // delta of the 32 rows
+  __shared__ __attribute__((aligned(16))) unsigned short sPT[TILE_KV * SP];
+  __shared__ __attribute__((aligned(16))) unsigned short sDST[TILE_KV * SP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, r16 = lane & 15;
-  const int64_t blk = blockIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int64_t blk = blockIdx.x % a.NB;
+  const int split = (int)(blockIdx.x / a.NB);
+  const int nch = a.nchunk[blk];
+  const int nsplit = dkv_nsplit(nch, a.maxsplit);
+  if (split >= nsplit) return;
+  const int c_lo = (int)((int64_t)split * nch / nsplit);
+  const int c_hi = (int)((int64_t)(split + 1) * nch / nsplit);
+  const int nsub = 2 * (c_hi - c_lo);
   const int64_t kb0 = blk * TILE_KV;
+  const int64_t qrows = a.s_q * H;   // rows of q / dout / lse / delta
 
   // This wave's 16 kv rows as A fragments (K for S^T; their first 512
   // columns, ks < 16, are V for dP^T).
@@ -245,228 +295,257 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
   unsigned long long touched = 0ull;
 
-  // One chunk: up to T token slots (sTok/sMask filled, cnt slots valid).
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  // Token of a chunk slot, clamped into [0, s_q) before it forms an address.
-  auto slot_token = [&](int slot) -> int64_t {
-    int64_t t = sTok[slot];
-    return t < 0 ? 0 : (t >= a.s_q ? a.s_q - 1 : t);
+  const uint64_t zero = reinterpret_cast<uint64_t>(g_zero16);
+  const int lane_id = lane;
+  // Copies of sub-chunk u into one buffer set; copy ci by wave ci % 4.
+  auto issue = [&](int u, char* q_dst, char* d_dst, unsigned* m_dst, float* l_dst, float* e_dst) __attribute__((always_inline)) {
+    const int2 ce = a.clist[blk * a.G + c_lo + (u >> 1)];  // (group, record start)
+    // The lane's copy offsets are loop invariant; an opaque copy of the lane
+    // id makes them recomputed per sub-chunk instead of held in ~60 registers
+    // across the whole loop (which spilled).
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int64_t row0 = (int64_t)ce.x * GROUP_ROWS + DKV_SUB * (u & 1);
+    const uint64_t mbase = reinterpret_cast<uint64_t>(a.krmask + (int64_t)ce.x * a.rcap + ce.y);
+#pragma unroll
+    for (int j = 0; j < (DKV_COPIES + 3) / 4; ++j) {
+      const int ci = wv + 4 * j;
+      if (ci < DKV_Q_COPIES) {
+        const int p = ci * 64 + lane;
+        const int r = p / TILE_STRIDE_CHUNKS, c = p - r * TILE_STRIDE_CHUNKS;
+        const int64_t qr = row0 + r;
+        const uint64_t src = reinterpret_cast<uint64_t>(a.q + qr * D_K + 8 * c);
+        g2lds16(reinterpret_cast<const void*>((r < DKV_SUB && c < ROW_CHUNKS && qr < qrows) ? src : zero),
+                q_dst + ci * 1024);
+      } else if (ci < DKV_Q_COPIES + DKV_DO_COPIES) {
+        const int cd = ci - DKV_Q_COPIES;
+        const int p = cd * 64 + lane;
+        const int r = p / DO_STRIDE_CHUNKS, c = p - r * DO_STRIDE_CHUNKS;
+        const int64_t qr = row0 + r;
+        const uint64_t src = reinterpret_cast<uint64_t>(a.dout + qr * D_V + 8 * c);
+        g2lds16(reinterpret_cast<const void*>((r < DKV_SUB && c < DO_CHUNKS && qr < qrows) ? src : zero),
+                d_dst + cd * 1024);
+      } else if (ci == DKV_Q_COPIES + DKV_DO_COPIES) {
+        g2lds4(reinterpret_cast<const void*>(lane < 2 * T ? mbase + 4u * lane : zero), m_dst);
+      } else if (ci == DKV_Q_COPIES + DKV_DO_COPIES + 1) {
+        const uint64_t src = reinterpret_cast<uint64_t>(a.lse + row0 + lane);
+        g2lds4(reinterpret_cast<const void*>((lane < DKV_SUB && row0 + lane < qrows) ? src : zero), l_dst);
+      } else if (ci == DKV_Q_COPIES + DKV_DO_COPIES + 2) {
+        const uint64_t src = reinterpret_cast<uint64_t>(a.delta + row0 + lane);
+        g2lds4(reinterpret_cast<const void*>((lane < DKV_SUB && row0 + lane < qrows) ? src : zero), e_dst);
+      }
+    }
   };
-  auto process_chunk = [&](int cnt) {
-    // Q rows of the chunk: 64 rows x 73 chunks = 73 copies; dO: 64 x 65 = 65.
-#pragma unroll
-    for (int j = 0; j < (TILE_STRIDE_CHUNKS + 3) / 4; ++j) {
-      const int i = wv + 4 * j;
-      if (i < TILE_STRIDE_CHUNKS) {
-        const int p = i * 64 + lane;
-        const int row = p / TILE_STRIDE_CHUNKS, c = p - row * TILE_STRIDE_CHUNKS;
-        const int slot = row / H;
-        const void* src = g_zero16;
-        if (c < ROW_CHUNKS && slot < cnt)
-          src = a.q + (slot_token(slot) * H + row % H) * D_K + 8 * c;
-        g2lds16(src, sQ + i * 1024);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < (DO_STRIDE_CHUNKS + 3) / 4; ++j) {
-      const int i = wv + 4 * j;
-      if (i < DO_STRIDE_CHUNKS) {
-        const int p = i * 64 + lane;
-        const int row = p / DO_STRIDE_CHUNKS, c = p - row * DO_STRIDE_CHUNKS;
-        const int slot = row / H;
-        const void* src = g_zero16;
-        if (c < DO_CHUNKS && slot < cnt)
-          src = a.dout + (slot_token(slot) * H + row % H) * D_V + 8 * c;
-        g2lds16(src, sDO + i * 1024);
-      }
-    }
-    if (tid < GROUP_ROWS) {
-      const int slot = tid / H;
-      float l2 = 0.f, dl = 0.f;
-      if (slot < cnt) {
-        const int64_t r = slot_token(slot) * H + tid % H;
-        l2 = a.lse[r] * LOG2E;
-        dl = a.delta[r];
-      }
-      sLse2[tid] = l2;
-      sDel[tid] = dl;
-    }
+
+  auto step = [&](int u, const char* sq, const char* sd, const unsigned* sm, const float* sl,
+                  const float* se, char* nq, char* nd, unsigned* nm, float* nl, float* ne) __attribute__((always_inline)) {
     wait_vmcnt0();
     __syncthreads();
-
-    float4_t st[4], dpt[4];
+    if (u + 1 < nsub) issue(u + 1, nq, nd, nm, nl, ne);
+    const int half = u & 1;
+    // rows each token of the chunk selects; this sub-chunk's query rows are
+    // 32*half .. 32*half+31 of the group, token slot = row / H
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int sl2 = 0; sl2 < T; ++sl2)
+      touched |= (unsigned long long)sm[2 * sl2] | ((unsigned long long)sm[2 * sl2 + 1] << 32);
+
+    float4_t st[2], dpt[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
       st[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
       dpt[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const short8_t b = ld16_lds(sQ + (nt * 16 + r16) * TILE_STRIDE + (4 * ks + g16) * 16);
+      for (int nt = 0; nt < 2; ++nt) {
+        const short8_t b = ld16_lds(sq + (nt * 16 + r16) * TILE_STRIDE + (4 * ks + g16) * 16);
         st[nt] = mfma_bf16(kf[ks], b, st[nt]);
         if (ks < 16) {
-          const short8_t b2 = ld16_lds(sDO + (nt * 16 + r16) * DO_STRIDE + (4 * ks + g16) * 16);
+          const short8_t b2 = ld16_lds(sd + (nt * 16 + r16) * DO_STRIDE + (4 * ks + g16) * 16);
           dpt[nt] = mfma_bf16(kf[ks], b2, dpt[nt]);
         }
       }
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < 2; ++nt) {
       const int q = nt * 16 + r16;
-      const int slot = q / H;
-      const unsigned long long m = slot < cnt ? sMask[slot] : 0ull;
-      const float l2 = sLse2[q], dl = sDel[q];
+      const int slot = (DKV_SUB * half + q) / H;
+      const unsigned long long m =
+          (unsigned long long)sm[2 * slot] | ((unsigned long long)sm[2 * slot + 1] << 32);
+      const float l2 = sl[q] * LOG2E, dl = se[q];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kvl = 16 * wave + 4 * g16 + i;
         const bool v = (m >> kvl) & 1ull;
         const float p = v ? fast_exp2(st[nt][i] * a.scale_log2 - l2) : 0.f;
         const float ds = p * (dpt[nt][i] - dl) * a.scale;
-        sPT[kvl * 72 + q] = f2bf(p);
-        sDST[kvl * 72 + q] = f2bf(ds);
+        sPT[kvl * SP + q] = f2bf(p);
+        sDST[kvl * SP + q] = f2bf(ds);
       }
     }
     __syncthreads();
 
-    short8_t ad[4][2], ap[4][2];
+    short8_t ad[4], ap[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        ad[rb][k2] = ld16_lds(&sDST[(16 * rb + r16) * 72 + 32 * k2 + 8 * g16]);
-        ap[rb][k2] = ld16_lds(&sPT[(16 * rb + r16) * 72 + 32 * k2 + 8 * g16]);
-      }
+    for (int rb = 0; rb < 4; ++rb) {
+      ad[rb] = ld16_lds(&sDST[(16 * rb + r16) * SP + 8 * g16]);
+      ap[rb] = ld16_lds(&sPT[(16 * rb + r16) * SP + 8 * g16]);
+    }
 #pragma unroll
     for (int n = 0; n < 9; ++n) {
       const int col = 144 * wave + 16 * n;
-      const short8_t bq0 = ld_b_tr(sQ, TILE_STRIDE, 0, col, lane);
-      const short8_t bq1 = ld_b_tr(sQ, TILE_STRIDE, 32, col, lane);
+      const short8_t bq = ld_b_tr(sq, TILE_STRIDE, 0, col, lane);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        acc[rb][n] = mfma_bf16(ad[rb][0], bq0, acc[rb][n]);
-        acc[rb][n] = mfma_bf16(ad[rb][1], bq1, acc[rb][n]);
-      }
+      for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(ad[rb], bq, acc[rb][n]);
       if (col < D_V) {
-        const short8_t bo0 = ld_b_tr(sDO, DO_STRIDE, 0, col, lane);
-        const short8_t bo1 = ld_b_tr(sDO, DO_STRIDE, 32, col, lane);
+        const short8_t bo = ld_b_tr(sd, DO_STRIDE, 0, col, lane);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          acc[rb][n] = mfma_bf16(ap[rb][0], bo0, acc[rb][n]);
-          acc[rb][n] = mfma_bf16(ap[rb][1], bo1, acc[rb][n]);
-        }
+        for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(ap[rb], bo, acc[rb][n]);
       }
     }
-    __syncthreads();  // sQ / sDO / sPT / sDST are refilled by the next chunk
   };
 
-  // Records of this block, group by group (ascending group, then token).
-  for (int64_t gb = 0; gb < a.G; gb += 256) {
-    if (gb + tid < a.G) sTab[tid] = a.ktab[blk * a.G + gb + tid];
-    else sTab[tid] = make_int2(0, 0);
-    __syncthreads();
-    const int ng = (int)min<int64_t>(256, a.G - gb);
-    for (int j = 0; j < ng; ++j) {
-      const int2 e = sTab[j];
-      if (e.y == 0) continue;
-      const int64_t base = (gb + j) * a.rcap + e.x;
-      if (tid < e.y) {
-        sTok[tid] = a.krtok[base + tid];
-        sMask[tid] = a.krmask[base + tid];
-      }
-      __syncthreads();
-      for (int c = 0; c < e.y; ++c) touched |= sMask[c];
-      process_chunk(e.y);
-    }
-    __syncthreads();  // sTab is reloaded
+  if (nsub > 0) issue(0, sQ[0], sD[0], sM[0], sL[0], sE[0]);
+  for (int u = 0; u < nsub; ++u) {
+    const int b = u & 1;
+    step(u, sQ[b], sD[b], sM[b], sL[b], sE[b], sQ[b ^ 1], sD[b ^ 1], sM[b ^ 1], sL[b ^ 1], sE[b ^ 1]);
   }
 
-  // Repeated slots (rare): one single-row record each, in group/slot order.
-  if (*a.xtotal > 0) {
-    int fill = 0;
+  // Partial sum of this item: rows 16rb+4g16+i, columns 144*wave + 16n + r16.
+  float* dst = a.part + ((blk * a.maxsplit + split) * TILE_KV + 4 * g16) * D_K + 144 * wave + r16;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int n = 0; n < 9; ++n) dst[(16 * rb + i) * D_K + 16 * n] = acc[rb][n][i];
+  if (tid == 0) a.ptouch[blk * a.maxsplit + split] = touched;
+}
+
+// Compacts each kv block's row of the [block, group] record table into the
+// block's chunk list (groups with records for the block, ascending).
+__global__ __launch_bounds__(256) void dkv_schedule_kernel(BwdArgs a) {
+  __shared__ int scratch[8];
+  const int64_t blk = blockIdx.x;
+  const int tid = threadIdx.x;
+  int base = 0;
+  for (int64_t gb = 0; gb < a.G; gb += 256) {
+    const int64_t g = gb + tid;
+    int2 e = make_int2(0, 0);
+    if (g < a.G) e = a.ktab[blk * a.G + g];
+    const int nz = e.y > 0 ? 1 : 0;
+    int total;
+    const int pos = base + block_exclusive_scan256(nz, scratch, &total);
+    if (nz) a.clist[blk * a.G + pos] = make_int2((int)g, e.x);
+    base += total;
+  }
+  if (tid == 0) a.nchunk[blk] = base;
+}
+
+// Sum of 256 per-thread values, identical on every thread (fixed order).
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return r;
+}
+
+// Writes dkv for 16 rows of a block (4 workgroups per block): the block's
+// split partials added in split order, plus -- only when some index row
+// repeats an entry -- the extra slots' contributions, each computed directly
+// in (group, slot) order.  Output semantics (bf16, fp32, accumulate, rows no
+// slot selects) are applied here.  Bitwise reproducible.
+template <int H>
+__global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
+  constexpr int T = GROUP_ROWS / H;
+  __shared__ float sX[16 * D_K];   // extra-slot contributions of the 16 rows
+  __shared__ float red[4];
+  __shared__ int sHave;
+  const int tid = threadIdx.x;
+  const int64_t blk = blockIdx.x >> 2;
+  const int quarter = blockIdx.x & 3;
+  const int64_t r0 = blk * TILE_KV + 16 * quarter;  // first row of this workgroup
+  const int nsplit = dkv_nsplit(a.nchunk[blk], a.maxsplit);
+  unsigned long long touched = 0ull;
+  for (int sp = 0; sp < nsplit; ++sp) touched |= a.ptouch[blk * a.maxsplit + sp];
+  touched = (touched >> (16 * quarter)) & 0xFFFFull;
+
+  const bool extras = *a.xtotal > 0;
+  if (extras) {
+    for (int e = tid; e < 16 * D_K; e += 256) sX[e] = 0.f;
+    __syncthreads();
     for (int64_t g = 0; g < a.G; ++g) {
       const int xc = a.xcount[g];
       if (xc == 0) continue;
       const int n_main = a.qcount[g] - xc;
-      const int32_t* xrow = a.qrow + g * a.qcap + n_main;
-      const uint8_t* xmask = a.qmask + g * a.qcap + n_main;
-      for (int x0 = 0; x0 < xc; x0 += 256) {
-        const int x = x0 + tid;
-        int match = 0, tok = 0;
-        unsigned long long bit = 0ull;
-        if (x < xc) {
-          const int64_t row = xrow[x];
-          if (row >= kb0 && row < kb0 + TILE_KV) {
-            match = 1;
-            tok = (int)(g * T + (__ffs((unsigned)xmask[x]) - 1));
-            bit = 1ull << (row - kb0);
+      for (int x = 0; x < xc; ++x) {
+        const int64_t row = a.qrow[g * a.qcap + n_main + x];
+        if (row < r0 || row >= r0 + 16 || row >= a.s_kv) continue;
+        int64_t t = g * T + (__ffs((unsigned)a.qmask[g * a.qcap + n_main + x]) - 1);
+        t = t < 0 ? 0 : (t >= a.s_q ? a.s_q - 1 : t);
+        const int rl = (int)(row - r0);
+        touched |= 1ull << rl;
+        const uint16_t* kr = a.kv + row * D_K;
+        for (int h = 0; h < H; ++h) {
+          const uint16_t* qr = a.q + (t * H + h) * D_K;
+          const uint16_t* dr = a.dout + (t * H + h) * D_V;
+          float z = 0.f, dp = 0.f;
+          for (int c = tid; c < D_K; c += 256) {
+            const float k = bf2f(kr[c]);
+            z += bf2f(qr[c]) * k;
+            if (c < D_V) dp += bf2f(dr[c]) * k;
           }
-        }
-        int total;
-        const int pos = block_exclusive_scan256(match, scratch, &total);
-        for (int done = 0; done < total;) {
-          const int take = min(T - fill, total - done);
-          if (match && pos >= done && pos < done + take) {
-            sTok[fill + pos - done] = tok;
-            sMask[fill + pos - done] = bit;
+          z = block_sum256(z, red);
+          dp = block_sum256(dp, red);
+          const float p = fast_exp2(z * a.scale_log2 - a.lse[t * H + h] * LOG2E);
+          const float ds = p * (dp - a.delta[t * H + h]) * a.scale;
+          for (int c = tid; c < D_K; c += 256) {
+            float v = ds * bf2f(qr[c]);
+            if (c < D_V) v += p * bf2f(dr[c]);
+            sX[rl * D_K + c] += v;
           }
-          fill += take;
-          done += take;
           __syncthreads();
-          if (fill == T) {
-            for (int c = 0; c < T; ++c) touched |= sMask[c];
-            process_chunk(T);
-            fill = 0;
-          }
         }
       }
     }
-    if (fill > 0) {
-      for (int c = 0; c < fill; ++c) touched |= sMask[c];
-      process_chunk(fill);
-    }
+    __syncthreads();
   }
 
-  // Epilogue: each dkv row of the block is written once.
-  unsigned short* so = reinterpret_cast<unsigned short*>(sQ);  // [64][584]
-  constexpr int SO = TILE_STRIDE / 2;
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kvl = 16 * rb + 4 * g16 + i;
-      const int64_t row = kb0 + kvl;
-      const bool hit = (touched >> kvl) & 1ull;
-#pragma unroll
-      for (int n = 0; n < 9; ++n) {
-        const int col = 144 * wave + 16 * n + r16;
-        float v = acc[rb][n][i];
-        if (row < a.s_kv && a.dkv_f32) {
-          float* dst = a.dkv_f32 + row * D_K + col;
-          if (a.accumulate) {
-            const float old = *dst;
-            if (hit) {
-              v = old + v;
-              *dst = v;
-            } else {
-              v = old;
-            }
-          } else {
-            *dst = v;
-          }
+  const float* src = a.part + (blk * a.maxsplit * TILE_KV + 16 * quarter) * D_K;
+  constexpr int N4 = 16 * D_K / 4;  // float4 elements of 16 rows
+  for (int e = tid; e < N4; e += 256) {
+    float4_t v = *reinterpret_cast<const float4_t*>(src + 4 * e);
+    for (int sp = 1; sp < nsplit; ++sp)
+      v += *reinterpret_cast<const float4_t*>(src + (int64_t)sp * TILE_KV * D_K + 4 * e);
+    if (extras) v += *reinterpret_cast<const float4_t*>(sX + 4 * e);
+    const int kvl = (4 * e) / D_K;
+    const int col = (4 * e) % D_K;
+    const int64_t row = r0 + kvl;
+    if (row >= a.s_kv) continue;
+    const bool hit = (touched >> kvl) & 1ull;
+    if (a.dkv_f32) {
+      float4_t* d = reinterpret_cast<float4_t*>(a.dkv_f32 + row * D_K + col);
+      if (a.accumulate) {
+        const float4_t old = *d;
+        if (hit) {
+          v = old + v;
+          *d = v;
+        } else {
+          v = old;
         }
-        so[kvl * SO + col] = f2bf(v);
+      } else {
+        *d = v;
       }
     }
-  if (a.dkv) {
-    __syncthreads();
-    for (int p = tid; p < TILE_KV * ROW_CHUNKS; p += 256) {
-      const int kvl = p / ROW_CHUNKS, c = p - kvl * ROW_CHUNKS;
-      const int64_t row = kb0 + kvl;
-      if (row < a.s_kv)
-        *reinterpret_cast<uint4_t*>(a.dkv + row * D_K + 8 * c) =
-            *reinterpret_cast<const uint4_t*>(so + kvl * SO + 8 * c);
+    if (a.dkv) {
+      uint2 b;
+      b.x = pack_bf2(v[0], v[1]);
+      b.y = pack_bf2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(a.dkv + row * D_K + col) = b;
     }
   }
 }
@@ -488,12 +567,28 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream) {
 
 hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream) {
   if (a.NB == 0) return hipSuccess;
-  dim3 grid((unsigned)a.NB), block(256);
+  dkv_schedule_kernel<<<dim3((unsigned)a.NB), dim3(256), 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(a.NB * a.maxsplit)), block(256);
+  const dim3 fgrid((unsigned)(a.NB * 4));
   switch (heads) {
-    case 8: bwd_dkv_kernel<8><<<grid, block, 0, stream>>>(a); break;
-    case 16: bwd_dkv_kernel<16><<<grid, block, 0, stream>>>(a); break;
-    case 32: bwd_dkv_kernel<32><<<grid, block, 0, stream>>>(a); break;
-    case 64: bwd_dkv_kernel<64><<<grid, block, 0, stream>>>(a); break;
+    case 8:
+      bwd_dkv_kernel<8><<<grid, block, 0, stream>>>(a);
+      dkv_finalize_kernel<8><<<fgrid, block, 0, stream>>>(a);
+      break;
+    case 16:
+      bwd_dkv_kernel<16><<<grid, block, 0, stream>>>(a);
+      dkv_finalize_kernel<16><<<fgrid, block, 0, stream>>>(a);
+      break;
+    case 32:
+      bwd_dkv_kernel<32><<<grid, block, 0, stream>>>(a);
+      dkv_finalize_kernel<32><<<fgrid, block, 0, stream>>>(a);
+      break;
+    case 64:
+      bwd_dkv_kernel<64><<<grid, block, 0, stream>>>(a);
+      dkv_finalize_kernel<64><<<fgrid, block, 0, stream>>>(a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

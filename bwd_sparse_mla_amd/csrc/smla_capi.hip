@@ -100,8 +100,9 @@ Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward) {
   p.T = tokens_per_group(heads);
   p.G = (s_q + p.T - 1) / p.T;
   p.NB = (s_kv + TILE_KV - 1) / TILE_KV;
-  p.qcap = (int64_t)p.T * topk;
-  p.rcap = (int64_t)p.T * (topk < p.NB ? topk : p.NB);
+  p.qcap = ((int64_t)p.T * topk + 63) / 64 * 64;  // a multiple of 64: aligned mask words
+  const int64_t tk = (int64_t)p.T * topk;
+  p.rcap = (int64_t)p.T * (tk < p.NB ? tk : p.NB);
   size_t o = 0;
   p.off_qcount = o;  o = align256(o + (size_t)p.G * 4);
   p.off_xcount = o;  o = align256(o + (size_t)p.G * 4);
@@ -111,9 +112,15 @@ Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward) {
   p.off_xtotal = o;  o += 256;
   if (backward) {
     p.off_ktab = o;    o = align256(o + (size_t)p.NB * p.G * 8);
-    p.off_krtok = o;   o = align256(o + (size_t)p.G * p.rcap * 4);
     p.off_krmask = o;  o = align256(o + (size_t)p.G * p.rcap * 8);
     p.off_delta = o;   o = align256(o + (size_t)s_q * heads * 4);
+    // Split the per-block dkv reduction so that about 1024 workgroups run.
+    int64_t ms = (1024 + p.NB - 1) / p.NB;
+    p.maxsplit = (int)(ms < 1 ? 1 : (ms > 16 ? 16 : ms));
+    p.off_clist = o;   o = align256(o + (size_t)p.NB * p.G * 8);
+    p.off_nchunk = o;  o = align256(o + (size_t)p.NB * 4);
+    p.off_ptouch = o;  o = align256(o + (size_t)p.NB * p.maxsplit * 8);
+    p.off_part = o;    o = align256(o + (size_t)p.NB * p.maxsplit * TILE_KV * 576 * 4);
   }
   p.bytes = o;
   return p;
@@ -246,7 +253,6 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   pa.qrow = reinterpret_cast<int32_t*>(ws + p.off_qrow);
   pa.qmask = reinterpret_cast<uint8_t*>(ws + p.off_qmask);
   pa.ktab = reinterpret_cast<int2*>(ws + p.off_ktab);
-  pa.krtok = reinterpret_cast<int32_t*>(ws + p.off_krtok);
   pa.krmask = reinterpret_cast<unsigned long long*>(ws + p.off_krmask);
   // xtotal (one 256-byte slot) and ktab are contiguous: clear both at once.
   const size_t clear_words = (256 + (size_t)p.NB * p.G * 8) / 4;
@@ -273,9 +279,13 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   ba.qrow = pa.qrow;
   ba.qmask = pa.qmask;
   ba.ktab = pa.ktab;
-  ba.krtok = pa.krtok;
   ba.krmask = pa.krmask;
   ba.delta = reinterpret_cast<float*>(ws + p.off_delta);
+  ba.clist = reinterpret_cast<int2*>(ws + p.off_clist);
+  ba.nchunk = reinterpret_cast<int*>(ws + p.off_nchunk);
+  ba.maxsplit = p.maxsplit;
+  ba.part = reinterpret_cast<float*>(ws + p.off_part);
+  ba.ptouch = reinterpret_cast<unsigned long long*>(ws + p.off_ptouch);
   ba.dq = static_cast<uint16_t*>(dq);
   ba.dkv = static_cast<uint16_t*>(dkv);
   ba.dkv_f32 = dkv_f32;

@@ -88,9 +88,26 @@ __device__ __forceinline__ short8_t ld_b_tr(const char* tile, int stride, int k0
   return r;
 }
 
-// Asynchronous 16-byte global -> LDS copy: lane i writes lds_base + 16*i.
+// Asynchronous global -> LDS copies (global_load_lds): lane i writes
+// lds_base + size*i; lds_base must be wave-uniform.  They are issued through
+// inline asm on purpose: the compiler then inserts no vmcnt wait for them
+// (its alias analysis cannot tell the next tile's buffer from the current
+// one), so a prefetch overlaps the current tile.  Every consumer waits
+// explicitly (wait_vmcnt0 + barrier) before it reads a copied buffer.  The
+// "memory" clobber keeps the compiler from moving other memory accesses
+// across a copy.  M0 carries the LDS address; nothing else in these kernels
+// uses M0.
+__device__ __forceinline__ uint32_t lds_offset(const void* lds_ptr) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)lds_ptr));
+}
 __device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_ptr)(lds_base), 16, 0, 0);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gsrc), "s"(lds_offset(lds_base)) : "memory", "m0");
+}
+__device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gsrc), "s"(lds_offset(lds_base)) : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(0) (other counters untouched).
@@ -141,47 +158,73 @@ __device__ __forceinline__ int block_exclusive_scan256(int v, int* scratch, int*
 // padding row of a tile holds true zeros and never reaches outside the inputs.
 __device__ __attribute__((aligned(16))) const unsigned g_zero16[4] = {0u, 0u, 0u, 0u};
 
-// Gathers tile `tile` of a query group's union rows into an LDS tile of
-// TILE_KV rows x TILE_STRIDE bytes (72 data chunks + 1 pad chunk per row) with
-// direct global->LDS copies: 73 copies of 64 lanes x 16 bytes, copy i issued
-// by wave i % 4.  Rows past the group's entry count and pad chunks copy the
-// zero chunk.  Every row index is clamped into [0, s_kv) before it forms an
-// address, so no value in `rows` can reach outside kv.  The row indices are
-// all loaded before the first copy is issued, so the copies are not
-// serialised behind the index loads.  `wv` must be wave-uniform.
+// Bytes of an LDS tile of `rows` kv rows gathered by gather_kv_tile: the
+// rows at TILE_STRIDE bytes (72 data chunks + 1 pad chunk each), rounded up to
+// whole 1 KB copies.
+__host__ __device__ constexpr int kv_tile_copies(int rows) {
+  return (rows * TILE_STRIDE_CHUNKS + 63) / 64;
+}
+__host__ __device__ constexpr int kv_tile_bytes(int rows) { return kv_tile_copies(rows) * 1024; }
+
+// Gathers `count` (>= 1) union rows, whose kv row indices sit in LDS at
+// `rows` (entries 0..count-1), into an LDS tile of TILE_ROWS rows
+// (kv_tile_bytes(TILE_ROWS) bytes) with direct global->LDS copies of 64 lanes
+// x 16 bytes, copy i issued by wave i % 4.  Rows past `count`, pad chunks and
+// the tail of the last copy read the zero chunk.  Every row index is clamped
+// into [0, s_kv) before it forms an address, so no value in `rows` can reach
+// outside kv.  All indices are read from LDS before the first copy and no
+// memory read sits between copies, so the copies issue back to back.
+// `wv` must be wave-uniform.
 template <int TILE_ROWS>
 __device__ __forceinline__ void gather_kv_tile(char* dst, const uint16_t* kv, int64_t s_kv,
-                                               const int32_t* rows, int first, int count,
-                                               int wv, int lane) {
-  constexpr int NCOPY = TILE_ROWS * TILE_STRIDE_CHUNKS / 64;  // 73 for 64 rows
+                                               const int* rows, int count, int wv, int lane) {
+  constexpr int NCOPY = kv_tile_copies(TILE_ROWS);
   constexpr int PER_WAVE = (NCOPY + 3) / 4;
-  // 1) unconditional, in-range index loads (count >= 1), issued back to back;
-  // 2) every source address formed (branch-free) before the first copy, so the
-  //    wait for the index loads happens once and never behind a copy;
-  // 3) the copies.
   int rowv[PER_WAVE];
 #pragma unroll
   for (int j = 0; j < PER_WAVE; ++j) {
     const int p = (wv + 4 * j) * 64 + lane;
     const int r = p / TILE_STRIDE_CHUNKS;
-    rowv[j] = rows[first + (r < count ? r : count - 1)];
+    rowv[j] = rows[r < count ? r : count - 1];
   }
   const uint64_t zero = reinterpret_cast<uint64_t>(g_zero16);
   const uint64_t base = reinterpret_cast<uint64_t>(kv);
-  uint64_t src[PER_WAVE];
-#pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
-    const int p = (wv + 4 * j) * 64 + lane;
-    const int r = p / TILE_STRIDE_CHUNKS, c = p - r * TILE_STRIDE_CHUNKS;
-    int64_t row = rowv[j];
-    row = row < 0 ? 0 : (row >= s_kv ? s_kv - 1 : row);
-    const uint64_t a = base + (uint64_t)(row * D_K + 8 * c) * 2u;
-    src[j] = (c < ROW_CHUNKS && r < count) ? a : zero;
-  }
 #pragma unroll
   for (int j = 0; j < PER_WAVE; ++j) {
     const int i = wv + 4 * j;
-    if (i < NCOPY) g2lds16(reinterpret_cast<const void*>(src[j]), dst + i * 1024);
+    if (i < NCOPY) {
+      const int p = i * 64 + lane;
+      const int r = p / TILE_STRIDE_CHUNKS, c = p - r * TILE_STRIDE_CHUNKS;
+      int64_t row = rowv[j];
+      row = row < 0 ? 0 : (row >= s_kv ? s_kv - 1 : row);
+      const uint64_t a = base + (uint64_t)(row * D_K + 8 * c) * 2u;
+      g2lds16(reinterpret_cast<const void*>((c < ROW_CHUNKS && r < count) ? a : zero),
+              dst + i * 1024);
+    }
+  }
+}
+
+// Copies `tile_rows` entries [first, first + tile_rows) of a query group's
+// union (kv row indices, and token masks as 4-byte words of 4 entries each)
+// into LDS with one direct copy each; rows at or past `count` read the zero
+// chunk.  The planner zero-fills the masks from `count` up to the next
+// multiple of 64 and `first` is a multiple of the tile size, so the mask
+// words never carry stale entries.  Issued by wave `wv_rows` (rows) and wave
+// `wv_mask` (masks) only.
+__device__ __forceinline__ void copy_union_entries(int* rows_dst, unsigned char* mask_dst,
+                                                   const int32_t* erow, const uint8_t* emask,
+                                                   int first, int count, int tile_rows,
+                                                   int wv, int wv_rows, int wv_mask, int lane) {
+  const uint64_t zero = reinterpret_cast<uint64_t>(g_zero16);
+  if (rows_dst && wv == wv_rows) {
+    const bool ok = lane < tile_rows && first + lane < count;
+    g2lds4(reinterpret_cast<const void*>(ok ? reinterpret_cast<uint64_t>(erow + first + lane) : zero),
+           rows_dst);
+  }
+  if (mask_dst && wv == wv_mask) {
+    const bool ok = 4 * lane < tile_rows && first + 4 * lane < count;
+    g2lds4(reinterpret_cast<const void*>(ok ? reinterpret_cast<uint64_t>(emask + first + 4 * lane) : zero),
+           mask_dst);
   }
 }
 

@@ -29,9 +29,11 @@ namespace {
 template <int H>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
-  __shared__ __attribute__((aligned(16))) char sK[2][TILE_KV * TILE_STRIDE];
+  // Double-buffered kv tiles: the next tile is copied while this one is used.
+  __shared__ __attribute__((aligned(16))) char sK[2][kv_tile_bytes(TILE_KV)];
   __shared__ __attribute__((aligned(16))) unsigned short sP[GROUP_ROWS * 72];
-  __shared__ int sMask[2][TILE_KV];
+  __shared__ __attribute__((aligned(16))) unsigned char sMask[2][256];   // token masks (copied as words)
+  __shared__ __attribute__((aligned(16))) int sRow[2][64];   // kv row indices of a tile's entries
   __shared__ float sAlpha[GROUP_ROWS];
   __shared__ float sL[GROUP_ROWS];
 
@@ -76,22 +78,26 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
 
   // 64 rows x 73 chunks (72 data + 1 pad) = 73 copies of 64 lanes x 16 bytes.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int tile, int buf) {
-    gather_kv_tile<TILE_KV>(sK[buf], a.kv, a.s_kv, erow, tile * TILE_KV,
-                            min(TILE_KV, n_ent - tile * TILE_KV), wv, lane);
-    if (tid < TILE_KV) {
-      const int e = tile * TILE_KV + tid;
-      sMask[buf][tid] = e < n_ent ? (int)emask[e] : 0;
-    }
+  // Tile t's kv rows are copied from rows_t (LDS); masks of tile t+1 and row
+  // indices of tile t+2 follow by direct copies, so nothing the copies need is
+  // read from global memory between them.
+  auto issue = [&](int tile, char* kbuf, const int* rows_t, unsigned char* mbuf, int* rows_t2) __attribute__((always_inline)) {
+    gather_kv_tile<TILE_KV>(kbuf, a.kv, a.s_kv, rows_t, min(TILE_KV, n_ent - tile * TILE_KV), wv,
+                            lane);
+    copy_union_entries(nullptr, mbuf, erow, emask, tile * TILE_KV, n_ent, TILE_KV, wv, 1, 1, lane);
+    if (tile + 1 < ntiles)
+      copy_union_entries(rows_t2, nullptr, erow, emask, (tile + 1) * TILE_KV, n_ent, TILE_KV, wv,
+                         2, 2, lane);
   };
 
-  if (ntiles > 0) issue(0, 0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
+  // One tile: kt/mk hold it, knext/mnext receive the prefetch of the next.
+  auto step = [&](int tile, const char* kt, const unsigned char* mkb, char* knext,
+                  unsigned char* mnext, const int* rnext, int* rcur) __attribute__((always_inline)) {
     wait_vmcnt0();
     __syncthreads();
-    const char* kt = sK[buf];
-
+    // Prefetch the next tile into the other buffer (free: every wave has
+    // passed the barrier above, so the previous tile's reads are done).
+    if (tile + 1 < ntiles) issue(tile + 1, knext, rnext, mnext, rcur);
     float4_t s[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) s[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
@@ -103,11 +109,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
         s[nt] = mfma_bf16(qf[ks], b, s[nt]);
       }
     }
-    if (tile + 1 < ntiles) issue(tile + 1, buf ^ 1);
 
     int mk[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) mk[nt] = sMask[buf][nt * 16 + r16];
+    for (int nt = 0; nt < 4; ++nt) mk[nt] = mkb[nt * 16 + r16];
     float alpha[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -171,6 +176,18 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
         acc[rb][n] = mfma_bf16(pa[rb][1], b1, acc[rb][n]);
       }
     }
+  };
+
+  if (ntiles > 0) {
+    copy_union_entries(sRow[0], sMask[0], erow, emask, 0, n_ent, TILE_KV, wv, 0, 1, lane);
+    if (ntiles > 1) copy_union_entries(sRow[1], nullptr, erow, emask, TILE_KV, n_ent, TILE_KV, wv, 2, 2, lane);
+    wait_vmcnt0();
+    __syncthreads();
+    gather_kv_tile<TILE_KV>(sK[0], a.kv, a.s_kv, sRow[0], min(TILE_KV, n_ent), wv, lane);
+  }
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int b = tile & 1;
+    step(tile, sK[b], sMask[b], sK[b ^ 1], sMask[b ^ 1], sRow[b ^ 1], sRow[b]);
   }
 
   // Epilogue: LSE from the row owners, then normalised output through LDS.

@@ -23,11 +23,13 @@ struct Plan {
   int T = 0;          // tokens per query group
   int64_t G = 0;      // number of query groups
   int64_t NB = 0;     // number of 64-row kv blocks
-  int64_t qcap = 0;   // union entries reserved per group: T * topk
-  int64_t rcap = 0;   // kv-block records reserved per group: T * min(topk, NB)
+  int64_t qcap = 0;   // union entries reserved per group: T * topk rounded up to 64
+  int64_t rcap = 0;   // kv-block records reserved per group: T * min(T * topk, NB)
   // byte offsets into the workspace
   size_t off_qcount = 0, off_xcount = 0, off_xtotal = 0, off_qrow = 0, off_qmask = 0;
-  size_t off_ktab = 0, off_krtok = 0, off_krmask = 0, off_delta = 0;
+  size_t off_ktab = 0, off_krmask = 0, off_delta = 0;
+  size_t off_clist = 0, off_nchunk = 0, off_part = 0, off_ptouch = 0;
+  int maxsplit = 1;   // dkv partial sums per kv block (split over its records)
   size_t bytes = 0;
 };
 
@@ -43,9 +45,8 @@ struct PlanArgs {
   int* xtotal;        // [1]   sum of xcount
   int32_t* qrow;      // [G, qcap] kv row of each union entry
   uint8_t* qmask;     // [G, qcap] mask of the group's tokens that select it
-  int2* ktab;         // [NB, G] (record start within the group, record count); may be null
-  int32_t* krtok;     // [G, rcap] token of each kv-block record
-  unsigned long long* krmask;  // [G, rcap] 64-bit row mask of each record
+  int2* ktab;         // [NB, G] (record start within the group, T) or (0, 0); may be null
+  unsigned long long* krmask;  // [G, rcap] 64-bit row masks, T per (block, group) pair
 };
 
 struct FwdArgs {
@@ -76,9 +77,13 @@ struct BwdArgs {
   const int32_t* qrow;
   const uint8_t* qmask;
   const int2* ktab;
-  const int32_t* krtok;
   const unsigned long long* krmask;
   float* delta;       // [s_q * H] rowsum(dout * out), written by the dq pass
+  int2* clist;        // [NB, G] per block: (group, record start), compacted
+  int* nchunk;        // [NB] entries of clist per block
+  int maxsplit;       // splits per kv block at most
+  float* part;        // [NB * maxsplit, 64, 576] fp32 partial dkv of each split
+  unsigned long long* ptouch;  // [NB * maxsplit] rows each split touched
   uint16_t* dq;
   uint16_t* dkv;      // may be null
   float* dkv_f32;     // may be null
@@ -90,6 +95,12 @@ hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream);
+// dkv split schedule: chunks a split covers at least, and the split count.
+constexpr int DKV_MIN_CHUNKS = 8;
+__host__ __device__ inline int dkv_nsplit(int nchunk, int maxsplit) {
+  int n = (nchunk + DKV_MIN_CHUNKS - 1) / DKV_MIN_CHUNKS;
+  return n < 1 ? 1 : (n > maxsplit ? maxsplit : n);
+}
 hipError_t launch_validate(const int32_t* idx, int64_t n, int64_t s_kv,
                            unsigned long long* n_bad, hipStream_t stream);
 

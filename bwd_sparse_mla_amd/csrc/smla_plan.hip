@@ -8,11 +8,12 @@
 //    mask of the tokens that select it.  A token that lists a row more than
 //    once gets one extra entry per repeat (mask = that token only), appended
 //    after the union, so every slot stays its own softmax term.
-//  * kv-major: for every 64-row KV block, the (token, 64-bit row mask)
-//    records of the tokens that select rows of that block, stored per group
-//    and indexed by a [block, group] table.  Walking the table in group order
-//    visits the records sorted by (block, token): a deterministic order for
-//    the per-row dKV reduction.
+//  * kv-major: for every (64-row KV block, query group) pair where some token
+//    of the group selects a row of the block, T records -- one 64-bit row
+//    mask per token of the group -- stored per group and indexed by a
+//    [block, group] table.  Walking the table in group order visits the
+//    records sorted by (block, token): a deterministic order for the per-row
+//    dKV reduction.
 //
 // A slot is valid iff 0 <= index < s_kv; -1 (padding) and any other value are
 // skipped, so padding never reaches memory (miles PR #2079 digest, "fix GLM-5
@@ -135,29 +136,25 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     qbase += total;
 
     if (a.ktab) {
-      // kv-block records: thread tid owns block (w0 >> 6) + tid.
+      // kv-block records: thread tid owns block (w0 >> 6) + tid.  A block any
+      // token of the group selects gets T records, one 64-bit row mask per
+      // token of the group (zero for tokens that select none of its rows).
       unsigned long long mk[T];
-      int cnt = 0;
+      int any = 0;
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         mk[t] = (unsigned long long)bm[t][2 * tid] |
                 ((unsigned long long)bm[t][2 * tid + 1] << 32);
-        cnt += (mk[t] != 0ull);
+        any |= (mk[t] != 0ull);
       }
       int rtotal;
-      const int rpos = rbase + block_exclusive_scan256(cnt, scratch, &rtotal);
-      if (cnt) {
+      const int rpos = rbase + block_exclusive_scan256(any ? T : 0, scratch, &rtotal);
+      if (any) {
         const int64_t b = (int64_t)(w0 >> 6) + tid;  // < NB: a set bit is a row < s_kv
-        a.ktab[b * a.G + g] = make_int2(rpos, cnt);
-        int64_t r = g * a.rcap + rpos;
+        a.ktab[b * a.G + g] = make_int2(rpos, T);
+        const int64_t r = g * a.rcap + rpos;
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          if (mk[t]) {
-            a.krtok[r] = (int32_t)(t0 + t);
-            a.krmask[r] = mk[t];
-            ++r;
-          }
-        }
+        for (int t = 0; t < T; ++t) a.krmask[r + t] = mk[t];
       }
       rbase += rtotal;
     }
@@ -188,6 +185,10 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     a.xcount[g] = xtot;
     if (xtot) atomicAdd(a.xtotal, xtot);
   }
+  // Zero the masks of the last tile's unused entries (up to the next multiple
+  // of 64; qcap is a multiple of 64): the compute kernels copy masks in words.
+  const int n_all = qbase + xtot;
+  if (tid < 64 && n_all + tid < ((n_all + 63) & ~63)) qmask[n_all + tid] = 0;
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
