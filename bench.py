@@ -13,6 +13,8 @@ baseline (the fp64 oracle on a bounded token sample, on the host cores).
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -47,8 +49,53 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="time the steps without per-kernel HIP events")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (three times) and "
+                         "exit: the calibration run for the HBM byte counters")
     return ap.parse_args()
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources (csrc/*.hip, *.h, include/*.h, sorted)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "bwd_sparse_mla_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain
+    copy's reading), or None when there is none for the current sources."""
+    digest = source_digest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as fh:
+            for ln in fh:
+                if not ln.startswith("traffic: "):
+                    continue
+                rec = json.loads(ln[len("traffic: "):])
+                if (rec.get("kernel") == kernel and rec.get("workload") == workload
+                        and rec.get("source_sha256") == digest):
+                    return rec
+    return None
+
+
+def copy_probe(mib: int) -> None:
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
 def cpu_baseline(w, target_s: float):
@@ -97,6 +144,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
+
     import torch
 
     import bwd_sparse_mla_amd as smla
@@ -120,6 +171,13 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The timed region: K steps between two events on the library's stream
+    # (torch's current stream).  Unless --no-kernel-timing, the library also
+    # brackets each of its own launches with HIP events on that stream, so
+    # the per-kernel averages below come from these same K steps.
+    timing = not args.no_kernel_timing
+    if timing:
+        smla.timing_start(16 * args.steps)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -129,6 +187,8 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if timing:
+        smla.timing_stop()
     ms = e0.elapsed_time(e1) / args.steps
     print(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)",
           file=sys.stderr, flush=True)
@@ -143,25 +203,24 @@ def main():
 
     kernels = {}
     roofline = None
-    if not args.no_kernel_timing:
-        smla.timing_start(16 * args.steps)
-        for _ in range(args.steps):
-            step()
-        smla.timing_stop()
-        torch.cuda.synchronize()
+    if timing:
         for name in ("fill", "plan", "fwd", "bwd_dq", "bwd_dkv"):
             n, tot = smla.timing_read(name)
             if n:
                 kernels[name] = {"launches": n, "avg_ms": tot / n}
-        # plan runs in fwd and in bwd: per-step totals
         dom = max((k for k in kernels if k in FLOPS_PER_PAIR_HEAD),
                   key=lambda k: kernels[k]["avg_ms"])
         flops = FLOPS_PER_PAIR_HEAD[dom] * w.H * nv
         ach = flops / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+        rec = recorded_traffic(dom, w.name)
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None if rec is None else rec["bytes_per_launch"],
                     "flops_per_launch": flops, "avg_ms": round(kernels[dom]["avg_ms"], 5)}
+        if rec is not None:
+            roofline["traffic_GBs"] = round(
+                rec["bytes_per_launch"] / (kernels[dom]["avg_ms"] * 1e-3) / 1e9, 1)
         print(f"[bench] kernels {kernels}", file=sys.stderr, flush=True)
 
     cpu = None
