@@ -44,7 +44,7 @@ template <int H>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
   constexpr int SDS = DQ_TILE + 8;  // dS row stride (bf16): 80 bytes, conflict-free reads
-  __shared__ __attribute__((aligned(16))) char sK[2][kv_tile_bytes(DQ_TILE)];
+  __shared__ __attribute__((aligned(16))) char sK[2][KV32_TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sDO[GROUP_ROWS * DO_STRIDE];
   __shared__ __attribute__((aligned(16))) unsigned short sdS[GROUP_ROWS * SDS];
   __shared__ __attribute__((aligned(16))) unsigned char sMask[2][256];   // token masks (copied as words)
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 
   // dout rows of the group into LDS (64 rows x 65 chunks = 65 copies).
   {
-    const uint64_t zero = reinterpret_cast<uint64_t>(g_zero16);
+    const uint64_t zero = reinterpret_cast<uint64_t>(zero_row());
 #pragma unroll 1
     for (int i = wv; i < DO_STRIDE_CHUNKS; i += 4) {
       const int p = i * 64 + lane;
@@ -119,15 +119,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   }
   wait_vmcnt0();
   __syncthreads();
-  int tl[4];
-  float del[4], ls2[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = 16 * wave + 4 * g16 + i;
-    tl[i] = rr / H;
-    del[i] = sDelta[rr];
-    ls2[i] = sLse2[rr];
-  }
+  // Scores and dP are computed transposed (K Q^T, K dO^T): lane (g, r) of
+  // wave w holds row 16w + r of the group and kv entries 16nt + 4g + i.
+  const int tl = (16 * wave + r16) / H;   // group-local token of the lane's row
+  const float del = sDelta[16 * wave + r16];
+  const float ls2 = sLse2[16 * wave + r16];
 
   float4_t acc[4][9];
 #pragma unroll
@@ -135,11 +131,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  // Tile t's kv rows are copied from rows_t (LDS); masks of tile t+1 and row
-  // indices of tile t+2 follow by direct copies.
+  // kv rows of a tile (count entries at rows_t in LDS) into a swizzled
+  // 32-row tile: 32 row copies and 4 tail copies, 9 per wave.
+  auto gather = [&](char* kbuf, const int* rows_t, int count) __attribute__((always_inline)) {
+    gather_kv_rows<DQ_TILE, ROW_CHUNKS>(kbuf, a.kv, a.s_kv, rows_t, count, wv, lane);
+  };
+  // Tile t's kv rows are copied from rows_t (LDS); masks of tile t and row
+  // indices of tile t+1 follow by direct copies.
   auto issue = [&](int tile, char* kbuf, const int* rows_t, unsigned char* mbuf, int* rows_t2) __attribute__((always_inline)) {
-    gather_kv_tile<DQ_TILE>(kbuf, a.kv, a.s_kv, rows_t, min(DQ_TILE, n_ent - tile * DQ_TILE), wv,
-                            lane);
+    gather(kbuf, rows_t, min(DQ_TILE, n_ent - tile * DQ_TILE));
     copy_union_entries(nullptr, mbuf, erow, emask, tile * DQ_TILE, n_ent, DQ_TILE, wv, 1, 1, lane);
     if (tile + 1 < ntiles)
       copy_union_entries(rows_t2, nullptr, erow, emask, (tile + 1) * DQ_TILE, n_ent, DQ_TILE, wv,
@@ -160,27 +160,45 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
       s[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
       dp[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
     }
+    // K fragments (and this wave's dout fragment) one k-step ahead of their
+    // MFMAs; the scheduling barriers keep the reads from sinking onto their
+    // uses.
+    short8_t kc[2], kn[2], dc, dn;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) kc[nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 0, lane);
+    dc = ld16_lds(drow);
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      short8_t da;
-      if (ks < 16) da = ld16_lds(drow + 64 * ks);
+      if (ks + 1 < 18) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) kn[nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * (ks + 1), lane);
+        if (ks + 1 < 16) dn = ld16_lds(drow + 64 * (ks + 1));
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const short8_t b = ld16_lds(kt + (nt * 16 + r16) * TILE_STRIDE + (4 * ks + g16) * 16);
-        s[nt] = mfma_bf16(qf[ks], b, s[nt]);
-        if (ks < 16) dp[nt] = mfma_bf16(da, b, dp[nt]);
+        s[nt] = mfma_bf16(kc[nt], qf[ks], s[nt]);
+        if (ks < 16) dp[nt] = mfma_bf16(kc[nt], dc, dp[nt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) kc[nt] = kn[nt];
+      dc = dn;
     }
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int mk = mkb[nt * 16 + r16];
+      const unsigned mk = *reinterpret_cast<const unsigned*>(mkb + nt * 16 + 4 * g16);
+      float d[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool v = (mk >> tl[i]) & 1;
-        const float p = v ? fast_exp2(s[nt][i] * a.scale_log2 - ls2[i]) : 0.f;
-        const float ds = p * (dp[nt][i] - del[i]);
-        sdS[(16 * wave + 4 * g16 + i) * SDS + nt * 16 + r16] = f2bf(ds);
+        const bool v = (mk >> (8 * i + tl)) & 1u;
+        const float p = v ? fast_exp2(s[nt][i] * a.scale_log2 - ls2) : 0.f;
+        d[i] = p * (dp[nt][i] - del);
       }
+      uint2 pk;
+      pk.x = pack_bf2(d[0], d[1]);
+      pk.y = pack_bf2(d[2], d[3]);
+      *reinterpret_cast<uint2*>(&sdS[(16 * wave + r16) * SDS + nt * 16 + 4 * g16]) = pk;
     }
     __syncthreads();
     short8_t dsa[4];
@@ -188,7 +206,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     for (int rb = 0; rb < 4; ++rb) dsa[rb] = ld16_lds(&sdS[(16 * rb + r16) * SDS + 8 * g16]);
 #pragma unroll
     for (int n = 0; n < 9; ++n) {
-      const short8_t b = ld_b_tr(kt, TILE_STRIDE, 0, 144 * wave + 16 * n, lane);
+      const short8_t b = ld_bt_rs<DQ_TILE>(kt, 0, 144 * wave + 16 * n, lane);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(dsa[rb], b, acc[rb][n]);
     }
@@ -199,7 +217,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     if (ntiles > 1) copy_union_entries(sRow[1], nullptr, erow, emask, DQ_TILE, n_ent, DQ_TILE, wv, 2, 2, lane);
     wait_vmcnt0();
     __syncthreads();
-    gather_kv_tile<DQ_TILE>(sK[0], a.kv, a.s_kv, sRow[0], min(DQ_TILE, n_ent), wv, lane);
+    gather(sK[0], sRow[0], min(DQ_TILE, n_ent));
   }
   for (int tile = 0; tile < ntiles; ++tile) {
     const int b = tile & 1;
@@ -244,16 +262,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 // dkv_finalize_kernel adds a block's partials in split order.  Launch order is
 // split-major, so every block's first split goes first.
 constexpr int DKV_SUB = 32;                                 // query rows per sub-chunk
-constexpr int DKV_Q_COPIES = kv_tile_copies(DKV_SUB);      // 37
-constexpr int DKV_DO_COPIES = (DKV_SUB * DO_STRIDE_CHUNKS + 63) / 64;  // 33
-constexpr int DKV_COPIES = DKV_Q_COPIES + DKV_DO_COPIES + 3;           // + masks, lse, delta
 
 template <int H>
 __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
   constexpr int SP = DKV_SUB + 8;  // P^T / dS^T row stride (bf16): 80 bytes
-  __shared__ __attribute__((aligned(16))) char sQ[2][DKV_Q_COPIES * 1024];
-  __shared__ __attribute__((aligned(16))) char sD[2][DKV_DO_COPIES * 1024];
+  __shared__ __attribute__((aligned(16))) char sQ[2][KV32_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sD[2][DO32_TILE_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned sM[2][64];   // T row masks (2 words each)
   __shared__ __attribute__((aligned(16))) float sL[2][64];      // lse of the 32 rows
   __shared__ __attribute__((aligned(16))) float sE[2][64];      // delta of the 32 rows
@@ -295,45 +310,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
   unsigned long long touched = 0ull;
 
-  const uint64_t zero = reinterpret_cast<uint64_t>(g_zero16);
+  const uint64_t zero = reinterpret_cast<uint64_t>(zero_row());
   const int lane_id = lane;
-  // Copies of sub-chunk u into one buffer set; copy ci by wave ci % 4.
+  // Copies of sub-chunk u into one buffer set: Q and dout rows as swizzled
+  // 32-row tiles (36 + 32 copies, 17 per wave), then the token masks, lse and
+  // delta of the 32 rows (one copy each, waves 0, 1, 2).
   auto issue = [&](int u, char* q_dst, char* d_dst, unsigned* m_dst, float* l_dst, float* e_dst) __attribute__((always_inline)) {
     const int2 ce = a.clist[blk * a.G + c_lo + (u >> 1)];  // (group, record start)
-    // The lane's copy offsets are loop invariant; an opaque copy of the lane
-    // id makes them recomputed per sub-chunk instead of held in ~60 registers
-    // across the whole loop (which spilled).
+    // Lane-derived offsets are recomputed per sub-chunk from an opaque copy
+    // of the lane id rather than held in registers across the loop.
     int lane = lane_id;
     asm volatile("" : "+v"(lane));
     const int64_t row0 = (int64_t)ce.x * GROUP_ROWS + DKV_SUB * (u & 1);
-    const uint64_t mbase = reinterpret_cast<uint64_t>(a.krmask + (int64_t)ce.x * a.rcap + ce.y);
-#pragma unroll
-    for (int j = 0; j < (DKV_COPIES + 3) / 4; ++j) {
-      const int ci = wv + 4 * j;
-      if (ci < DKV_Q_COPIES) {
-        const int p = ci * 64 + lane;
-        const int r = p / TILE_STRIDE_CHUNKS, c = p - r * TILE_STRIDE_CHUNKS;
-        const int64_t qr = row0 + r;
-        const uint64_t src = reinterpret_cast<uint64_t>(a.q + qr * D_K + 8 * c);
-        g2lds16(reinterpret_cast<const void*>((r < DKV_SUB && c < ROW_CHUNKS && qr < qrows) ? src : zero),
-                q_dst + ci * 1024);
-      } else if (ci < DKV_Q_COPIES + DKV_DO_COPIES) {
-        const int cd = ci - DKV_Q_COPIES;
-        const int p = cd * 64 + lane;
-        const int r = p / DO_STRIDE_CHUNKS, c = p - r * DO_STRIDE_CHUNKS;
-        const int64_t qr = row0 + r;
-        const uint64_t src = reinterpret_cast<uint64_t>(a.dout + qr * D_V + 8 * c);
-        g2lds16(reinterpret_cast<const void*>((r < DKV_SUB && c < DO_CHUNKS && qr < qrows) ? src : zero),
-                d_dst + cd * 1024);
-      } else if (ci == DKV_Q_COPIES + DKV_DO_COPIES) {
-        g2lds4(reinterpret_cast<const void*>(lane < 2 * T ? mbase + 4u * lane : zero), m_dst);
-      } else if (ci == DKV_Q_COPIES + DKV_DO_COPIES + 1) {
-        const uint64_t src = reinterpret_cast<uint64_t>(a.lse + row0 + lane);
-        g2lds4(reinterpret_cast<const void*>((lane < DKV_SUB && row0 + lane < qrows) ? src : zero), l_dst);
-      } else if (ci == DKV_Q_COPIES + DKV_DO_COPIES + 2) {
-        const uint64_t src = reinterpret_cast<uint64_t>(a.delta + row0 + lane);
-        g2lds4(reinterpret_cast<const void*>((lane < DKV_SUB && row0 + lane < qrows) ? src : zero), e_dst);
-      }
+    const int nvalid = (int)max((int64_t)0, min((int64_t)DKV_SUB, qrows - row0));
+    gather_seq_rows<DKV_SUB, ROW_CHUNKS>(q_dst, a.q + row0 * D_K, nvalid, wv, lane);
+    gather_seq_rows<DKV_SUB, DO_CHUNKS>(d_dst, a.dout + row0 * D_V, nvalid, wv, lane);
+    if (wv == 0) {
+      const uint64_t src = reinterpret_cast<uint64_t>(a.krmask + (int64_t)ce.x * a.rcap + ce.y) + 4u * lane;
+      g2lds4(reinterpret_cast<const void*>(lane < 2 * T ? src : zero), m_dst);
+    } else if (wv == 1) {
+      const uint64_t src = reinterpret_cast<uint64_t>(a.lse + row0 + lane);
+      g2lds4(reinterpret_cast<const void*>((lane < DKV_SUB && row0 + lane < qrows) ? src : zero), l_dst);
+    } else if (wv == 2) {
+      const uint64_t src = reinterpret_cast<uint64_t>(a.delta + row0 + lane);
+      g2lds4(reinterpret_cast<const void*>((lane < DKV_SUB && row0 + lane < qrows) ? src : zero), e_dst);
     }
   };
 
@@ -342,6 +342,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     wait_vmcnt0();
     __syncthreads();
     if (u + 1 < nsub) issue(u + 1, nq, nd, nm, nl, ne);
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int g16 = lane >> 4, r16 = lane & 15;
     const int half = u & 1;
     // rows each token of the chunk selects; this sub-chunk's query rows are
     // 32*half .. 32*half+31 of the group, token slot = row / H
@@ -349,40 +352,68 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     for (int sl2 = 0; sl2 < T; ++sl2)
       touched |= (unsigned long long)sm[2 * sl2] | ((unsigned long long)sm[2 * sl2 + 1] << 32);
 
+    // S and dP for the sub-chunk's 32 query rows (M) against this wave's 16
+    // kv rows (N, the kf fragments): lane (g, r) holds query rows
+    // 16nt + 4g + i of kv row 16w + r.  Q / dout fragments run one k-step
+    // ahead of their MFMAs (the scheduling barriers keep the reads from
+    // sinking onto their uses).
     float4_t st[2], dpt[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       st[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
       dpt[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const short8_t b = ld16_lds(sq + (nt * 16 + r16) * TILE_STRIDE + (4 * ks + g16) * 16);
-        st[nt] = mfma_bf16(kf[ks], b, st[nt]);
-        if (ks < 16) {
-          const short8_t b2 = ld16_lds(sd + (nt * 16 + r16) * DO_STRIDE + (4 * ks + g16) * 16);
-          dpt[nt] = mfma_bf16(kf[ks], b2, dpt[nt]);
-        }
-      }
-    }
+    short8_t qc[2], qn[2], dc[2], dn[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int q = nt * 16 + r16;
-      const int slot = (DKV_SUB * half + q) / H;
+      qc[nt] = ld_b_rs<DKV_SUB>(sq, nt * 16, 0, lane);
+      dc[nt] = ld_b_rs<DKV_SUB>(sd, nt * 16, 0, lane);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      if (ks + 1 < 18) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          qn[nt] = ld_b_rs<DKV_SUB>(sq, nt * 16, 32 * (ks + 1), lane);
+          if (ks + 1 < 16) dn[nt] = ld_b_rs<DKV_SUB>(sd, nt * 16, 32 * (ks + 1), lane);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        st[nt] = mfma_bf16(qc[nt], kf[ks], st[nt]);
+        if (ks < 16) dpt[nt] = mfma_bf16(dc[nt], kf[ks], dpt[nt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        qc[nt] = qn[nt];
+        dc[nt] = dn[nt];
+      }
+    }
+    const int kvl = 16 * wave + r16;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int q0 = nt * 16 + 4 * g16;          // first of the lane's 4 query rows
+      const int slot = (DKV_SUB * half + q0) / H;  // one token for all 4 (H >= 4)
       const unsigned long long m =
           (unsigned long long)sm[2 * slot] | ((unsigned long long)sm[2 * slot + 1] << 32);
-      const float l2 = sl[q] * LOG2E, dl = se[q];
+      const bool v = (m >> kvl) & 1ull;
+      const float4_t l2 = *reinterpret_cast<const float4_t*>(sl + q0);
+      const float4_t dl = *reinterpret_cast<const float4_t*>(se + q0);
+      float p[4], ds[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kvl = 16 * wave + 4 * g16 + i;
-        const bool v = (m >> kvl) & 1ull;
-        const float p = v ? fast_exp2(st[nt][i] * a.scale_log2 - l2) : 0.f;
-        const float ds = p * (dpt[nt][i] - dl) * a.scale;
-        sPT[kvl * SP + q] = f2bf(p);
-        sDST[kvl * SP + q] = f2bf(ds);
+        p[i] = v ? fast_exp2(st[nt][i] * a.scale_log2 - l2[i] * LOG2E) : 0.f;
+        ds[i] = p[i] * (dpt[nt][i] - dl[i]) * a.scale;
       }
+      uint2 pk, dk;
+      pk.x = pack_bf2(p[0], p[1]);
+      pk.y = pack_bf2(p[2], p[3]);
+      dk.x = pack_bf2(ds[0], ds[1]);
+      dk.y = pack_bf2(ds[2], ds[3]);
+      *reinterpret_cast<uint2*>(&sPT[kvl * SP + q0]) = pk;
+      *reinterpret_cast<uint2*>(&sDST[kvl * SP + q0]) = dk;
     }
     __syncthreads();
 
@@ -395,11 +426,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
     for (int n = 0; n < 9; ++n) {
       const int col = 144 * wave + 16 * n;
-      const short8_t bq = ld_b_tr(sq, TILE_STRIDE, 0, col, lane);
+      const short8_t bq = ld_bt_rs<DKV_SUB>(sq, 0, col, lane);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(ad[rb], bq, acc[rb][n]);
       if (col < D_V) {
-        const short8_t bo = ld_b_tr(sd, DO_STRIDE, 0, col, lane);
+        const short8_t bo = ld_bt_rs<DKV_SUB>(sd, 0, col, lane);
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(ap[rb], bo, acc[rb][n]);
       }

@@ -8,10 +8,20 @@
 // The transposing LDS read ds_read_b64_tr_b16 works on groups of 16 lanes:
 // lane i of a group receives, as element j (j = 0..3), the 16-bit element
 // (i & 3) of the 8 bytes addressed by lane (i >> 2) + 4j of the same group.
-// Pointing lane L of a group at row 4*(L>>2 & 3)... of a row-major [k][n]
-// tile (see tr_b_addr) turns row-major storage into a B fragment whose
-// reduction index runs along rows, which is how V, K and Q/dO are consumed
-// when the contraction runs over kv rows or query rows.
+// So if lane i of a group addresses row k0 + (i >> 2) at columns
+// n0 + 4(i & 3) .. +3, lane i receives rows k0 .. k0+3 of column n0 + i: a
+// B fragment whose reduction index runs along stored rows, which is how V, K
+// and Q/dO are consumed when the contraction runs over kv or query rows.
+//
+// Gathered tiles (kv rows, query rows) live in LDS row-major with swizzled
+// 16-byte chunks.  A tile of R rows keeps the first 64 chunks of row r
+// (columns 0..511) at r*1024 + 16 (c ^ swz_lo(r)) and, for 576-column rows,
+// the 8 tail chunks (columns 512..575) at R*1024 + r*128 + 16 ((c-64) ^
+// swz_hi(r)).  One direct global->LDS copy moves the first 1 KB of one row
+// (a coalesced 1 KB read from a wave-uniform row address) or the tails of 8
+// rows.  swz_lo / swz_hi are bit permutations of the row chosen so that a
+// fragment read (16 consecutive rows, one chunk) and a transposing read (rows
+// {0..3, 8..11} + 16m, two adjacent chunks) hit 64 distinct banks.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,8 +40,6 @@ constexpr int D_V = 512;        // value (latent) width
 constexpr int D_T = 64;         // rope tail width
 constexpr int D_K = D_V + D_T;  // key width, 576
 constexpr int ROW_CHUNKS = D_K / 8;          // 72 chunks of 16 bytes per kv/q row
-constexpr int TILE_STRIDE_CHUNKS = ROW_CHUNKS + 1;  // one 16-byte pad per LDS row
-constexpr int TILE_STRIDE = TILE_STRIDE_CHUNKS * 16;  // 1168 bytes
 constexpr int DO_CHUNKS = D_V / 8;           // 64 chunks per dout row
 constexpr int DO_STRIDE_CHUNKS = DO_CHUNKS + 1;
 constexpr int DO_STRIDE = DO_STRIDE_CHUNKS * 16;  // 1040 bytes
@@ -40,6 +48,9 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr float SUMEXP_FLOOR = 1e-30f;
 // Running-max start: finite, so exp2(m_old - m_new) never sees inf - inf.
 constexpr float M_INIT = -1e30f;
+// Online softmax: the reference max of a row moves only when a new score
+// exceeds it by more than this (log2 units); probabilities stay <= 2^8.
+constexpr float RESCALE_SLACK = 8.f;
 
 __device__ __forceinline__ float4_t mfma_bf16(short8_t a, short8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -72,20 +83,53 @@ __device__ __forceinline__ short4_t ld_tr16(const void* lds_addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds_addr));
 }
 
-// B fragment [32 x 16] whose element (k, n) sits at row k0+k, column n0+n of a
-// row-major LDS tile with `stride` bytes per row (bf16 elements).  Two
-// transposing reads give k = 8g..8g+3 and 8g+4..8g+7 for lane column r.
-__device__ __forceinline__ short8_t ld_b_tr(const char* tile, int stride, int k0, int n0, int lane) {
+__device__ __forceinline__ int swz_lo(int r) { return ((r >> 2) & 1) | ((r & 3) << 1) | (r & 8); }
+__device__ __forceinline__ int swz_hi(int r) { return ((r >> 2) & 1) | (r & 2) | ((r >> 1) & 4); }
+
+// Byte offset of chunk `chunk` (0..71) of row `row` in a swizzled tile of R rows.
+template <int R>
+__device__ __forceinline__ int rs_off(int row, int chunk) {
+  return chunk < 64 ? row * 1024 + 16 * (chunk ^ swz_lo(row))
+                    : R * 1024 + row * 128 + 16 * ((chunk - 64) ^ swz_hi(row));
+}
+
+// B fragment [32 x 16] with B[k][n] = tile[n0 + n][k0 + k] (the tile's rows
+// are the fragment's columns): lane (g, r) reads chunk k0/8 + g of row n0 + r.
+template <int R>
+__device__ __forceinline__ short8_t ld_b_rs(const char* tile, int n0, int k0, int lane) {
+  return ld16_lds(tile + rs_off<R>(n0 + (lane & 15), (k0 >> 3) + (lane >> 4)));
+}
+
+// B fragment [32 x 16] with B[k][n] = tile[k0 + k][n0 + n] (reduction over
+// the tile's rows; n0 a multiple of 16): two transposing reads give
+// k = 8g .. 8g+3 and 8g+4 .. 8g+7 of lane column r.
+template <int R>
+__device__ __forceinline__ short8_t ld_bt_rs(const char* tile, int k0, int n0, int lane) {
   const int g = lane >> 4, L = lane & 15;
   const int row = k0 + 8 * g + (L >> 2);
-  const int col = n0 + 4 * (L & 3);
-  const char* p0 = tile + row * stride + col * 2;
-  short4_t lo = ld_tr16(p0);
-  short4_t hi = ld_tr16(p0 + 4 * stride);
-  short8_t r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
+  const int chunk = (n0 >> 3) + ((L >> 1) & 1);
+  const char* p = tile + (L & 1) * 8;
+  short4_t lo = ld_tr16(p + rs_off<R>(row, chunk));
+  short4_t hi = ld_tr16(p + rs_off<R>(row + 4, chunk));
+  short8_t v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return v;
+}
+
+// ld_bt_rs for columns below 512 only (n0 + 16 <= 512): no tail addressing.
+template <int R>
+__device__ __forceinline__ short8_t ld_bt_rs_lo(const char* tile, int k0, int n0, int lane) {
+  const int g = lane >> 4, L = lane & 15;
+  const int row = k0 + 8 * g + (L >> 2);
+  const int chunk = (n0 >> 3) + ((L >> 1) & 1);
+  const char* p = tile + (L & 1) * 8 + 16 * chunk;
+  short4_t lo = ld_tr16(p + row * 1024 + 16 * ((chunk ^ swz_lo(row)) - chunk));
+  short4_t hi = ld_tr16(p + (row + 4) * 1024 + 16 * ((chunk ^ swz_lo(row + 4)) - chunk));
+  short8_t v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return v;
 }
 
 // Asynchronous global -> LDS copies (global_load_lds): lane i writes
@@ -108,6 +152,16 @@ __device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
 __device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(gsrc), "s"(lds_offset(lds_base)) : "memory", "m0");
+}
+// 16-byte copy to LDS byte address lds_u32 (+ 16 per lane) from gsrc.
+__device__ __forceinline__ void g2lds16_u(const void* gsrc, uint32_t lds_u32) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gsrc), "s"(lds_u32) : "memory", "m0");
+}
+// 16-byte copy from the wave-uniform base sbase plus a per-lane byte offset.
+__device__ __forceinline__ void g2lds16_s(const void* sbase, uint32_t voff, uint32_t lds_u32) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_u32) : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(0) (other counters untouched).
@@ -154,55 +208,75 @@ __device__ __forceinline__ int block_exclusive_scan256(int v, int* scratch, int*
   return base + x - v;
 }
 
-// A zero 16-byte chunk that padding lanes of the LDS gathers copy from, so a
-// padding row of a tile holds true zeros and never reaches outside the inputs.
-__device__ __attribute__((aligned(16))) const unsigned g_zero16[4] = {0u, 0u, 0u, 0u};
+// Zeros that padding lanes of the LDS copies read from: a whole 576-column
+// row, so a padding row of a tile holds true zeros and never reaches outside
+// the inputs.
+__device__ __attribute__((aligned(16))) const uint16_t g_zero_row[D_K] = {};
+__device__ __forceinline__ const void* zero_row() { return g_zero_row; }
 
-// Bytes of an LDS tile of `rows` kv rows gathered by gather_kv_tile: the
-// rows at TILE_STRIDE bytes (72 data chunks + 1 pad chunk each), rounded up to
-// whole 1 KB copies.
-__host__ __device__ constexpr int kv_tile_copies(int rows) {
-  return (rows * TILE_STRIDE_CHUNKS + 63) / 64;
-}
-__host__ __device__ constexpr int kv_tile_bytes(int rows) { return kv_tile_copies(rows) * 1024; }
-
-// Gathers `count` (>= 1) union rows, whose kv row indices sit in LDS at
-// `rows` (entries 0..count-1), into an LDS tile of TILE_ROWS rows
-// (kv_tile_bytes(TILE_ROWS) bytes) with direct global->LDS copies of 64 lanes
-// x 16 bytes, copy i issued by wave i % 4.  Rows past `count`, pad chunks and
-// the tail of the last copy read the zero chunk.  Every row index is clamped
-// into [0, s_kv) before it forms an address, so no value in `rows` can reach
-// outside kv.  All indices are read from LDS before the first copy and no
-// memory read sits between copies, so the copies issue back to back.
-// `wv` must be wave-uniform.
-template <int TILE_ROWS>
-__device__ __forceinline__ void gather_kv_tile(char* dst, const uint16_t* kv, int64_t s_kv,
+// Gathers rows into a swizzled tile of R rows whose rows have CH chunks (72:
+// q / kv rows with their tail, 64: dout rows).  Wave wv copies the first 1 KB
+// of rows R/4 * wv .. R/4 * wv + R/4 - 1 (one copy per row, from a
+// wave-uniform row address) and the tails of rows 8j .. 8j+7 for j = wv,
+// wv + 4, ... (one copy per 8 rows, per-lane row addresses).
+//   gather_kv_rows: tile row r < count is kv row rows[r] (rows in LDS); rows
+//     past count, and row indices outside [0, s_kv), read the zero row.
+//   gather_seq_rows: tile row r < nvalid is row r of the contiguous rows at
+//     `first`; rows past nvalid read the zero row.
+template <int R, int CH>
+__device__ __forceinline__ void gather_kv_rows(char* tile, const uint16_t* kv, int64_t s_kv,
                                                const int* rows, int count, int wv, int lane) {
-  constexpr int NCOPY = kv_tile_copies(TILE_ROWS);
-  constexpr int PER_WAVE = (NCOPY + 3) / 4;
-  int rowv[PER_WAVE];
+  constexpr int PER = R / 4;
+  const uint32_t base = lds_offset(tile);
+  const int vrow = rows[PER * wv + (lane & (PER - 1))];
 #pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
-    const int p = (wv + 4 * j) * 64 + lane;
-    const int r = p / TILE_STRIDE_CHUNKS;
-    rowv[j] = rows[r < count ? r : count - 1];
+  for (int i = 0; i < PER; ++i) {
+    const int r = PER * wv + i;
+    const int row = __builtin_amdgcn_readlane(vrow, i);
+    const bool ok = r < count && row >= 0 && row < s_kv;
+    const uint16_t* src = ok ? kv + (int64_t)row * D_K : g_zero_row;
+    g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), base + 1024u * (uint32_t)r);
   }
-  const uint64_t zero = reinterpret_cast<uint64_t>(g_zero16);
-  const uint64_t base = reinterpret_cast<uint64_t>(kv);
+  if constexpr (CH == ROW_CHUNKS) {
 #pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
-    const int i = wv + 4 * j;
-    if (i < NCOPY) {
-      const int p = i * 64 + lane;
-      const int r = p / TILE_STRIDE_CHUNKS, c = p - r * TILE_STRIDE_CHUNKS;
-      int64_t row = rowv[j];
-      row = row < 0 ? 0 : (row >= s_kv ? s_kv - 1 : row);
-      const uint64_t a = base + (uint64_t)(row * D_K + 8 * c) * 2u;
-      g2lds16(reinterpret_cast<const void*>((c < ROW_CHUNKS && r < count) ? a : zero),
-              dst + i * 1024);
+    for (int j = 0; j < R / 32; ++j) {
+      const int jj = wv + 4 * j;
+      const int r = 8 * jj + (lane >> 3);
+      const int row = rows[r];
+      const bool ok = r < count && row >= 0 && row < s_kv;
+      const uint16_t* src = (ok ? kv + (int64_t)row * D_K : g_zero_row) + D_V + 8 * ((lane & 7) ^ swz_hi(r));
+      g2lds16_u(src, base + (uint32_t)(R * 1024 + 1024 * jj));
     }
   }
 }
+template <int R, int CH>
+__device__ __forceinline__ void gather_seq_rows(char* tile, const uint16_t* first, int nvalid,
+                                                int wv, int lane) {
+  constexpr int PER = R / 4;
+  constexpr int W = CH * 8;  // elements per row
+  const uint32_t base = lds_offset(tile);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int r = PER * wv + i;
+    const uint16_t* src = r < nvalid ? first + (int64_t)r * W : g_zero_row;
+    g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), base + 1024u * (uint32_t)r);
+  }
+  if constexpr (CH == ROW_CHUNKS) {
+#pragma unroll
+    for (int j = 0; j < R / 32; ++j) {
+      const int jj = wv + 4 * j;
+      const int r = 8 * jj + (lane >> 3);
+      const uint16_t* src = (r < nvalid ? first + (int64_t)r * W : g_zero_row) + D_V +
+                            8 * ((lane & 7) ^ swz_hi(r));
+      g2lds16_u(src, base + (uint32_t)(R * 1024 + 1024 * jj));
+    }
+  }
+}
+
+// Bytes of swizzled tiles.
+constexpr int KV64_TILE_BYTES = 64 * D_K * 2;   // 73728
+constexpr int KV32_TILE_BYTES = 32 * D_K * 2;   // 36864
+constexpr int DO32_TILE_BYTES = 32 * D_V * 2;   // 32768
 
 // Copies `tile_rows` entries [first, first + tile_rows) of a query group's
 // union (kv row indices, and token masks as 4-byte words of 4 entries each)
@@ -215,7 +289,7 @@ __device__ __forceinline__ void copy_union_entries(int* rows_dst, unsigned char*
                                                    const int32_t* erow, const uint8_t* emask,
                                                    int first, int count, int tile_rows,
                                                    int wv, int wv_rows, int wv_mask, int lane) {
-  const uint64_t zero = reinterpret_cast<uint64_t>(g_zero16);
+  const uint64_t zero = reinterpret_cast<uint64_t>(zero_row());
   if (rows_dst && wv == wv_rows) {
     const bool ok = lane < tile_rows && first + lane < count;
     g2lds4(reinterpret_cast<const void*>(ok ? reinterpret_cast<uint64_t>(erow + first + lane) : zero),

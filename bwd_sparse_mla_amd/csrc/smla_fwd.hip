@@ -30,12 +30,13 @@ template <int H>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
   // Double-buffered kv tiles: the next tile is copied while this one is used.
-  __shared__ __attribute__((aligned(16))) char sK[2][kv_tile_bytes(TILE_KV)];
+  __shared__ __attribute__((aligned(16))) char sK[2][KV64_TILE_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned short sP[GROUP_ROWS * 72];
   __shared__ __attribute__((aligned(16))) unsigned char sMask[2][256];   // token masks (copied as words)
   __shared__ __attribute__((aligned(16))) int sRow[2][64];   // kv row indices of a tile's entries
   __shared__ float sAlpha[GROUP_ROWS];
   __shared__ float sL[GROUP_ROWS];
+  __shared__ int sRescale[4];   // per wave: some row of the wave moved its max
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, r16 = lane & 15;
@@ -60,30 +61,32 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
       for (int ks = 0; ks < 18; ++ks) qf[ks] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  int tl[4];  // group-local token of this lane's C-fragment rows
-#pragma unroll
-  for (int i = 0; i < 4; ++i) tl[i] = (16 * wave + 4 * g16 + i) / H;
-
-  float m2[4], lsum[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m2[i] = M_INIT;
-    lsum[i] = 0.f;
-  }
+  // Scores are computed transposed (S^T = K Q^T): lane (g, r) of wave w holds
+  // row 16w + r of the group and kv entries 16nt + 4g + i.  Softmax state is
+  // per lane (one row; the four lanes g = 0..3 of a row agree).
+  const int tl = (16 * wave + r16) / H;  // group-local token of this lane's row
+  // m_run is the max the probabilities are taken against: it only moves when
+  // a row max exceeds it by more than RESCALE_SLACK (log2 units), so most
+  // tiles need no rescaling of acc; p = exp2(z - m_run) <= 2^RESCALE_SLACK.
+  float m_run = M_INIT, lsum = 0.f;
   float4_t acc[4][8];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  // 64 rows x 73 chunks (72 data + 1 pad) = 73 copies of 64 lanes x 16 bytes.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  // Tile t's kv rows are copied from rows_t (LDS); masks of tile t+1 and row
-  // indices of tile t+2 follow by direct copies, so nothing the copies need is
+  const int lane_id = lane;
+  // kv rows of a tile (count entries at rows_t in LDS) into a swizzled tile:
+  // 64 row copies and 8 tail copies, 18 per wave.
+  auto gather = [&](char* kbuf, const int* rows_t, int count) __attribute__((always_inline)) {
+    gather_kv_rows<TILE_KV, ROW_CHUNKS>(kbuf, a.kv, a.s_kv, rows_t, count, wv, lane_id);
+  };
+  // Tile t's kv rows are copied from rows_t (LDS); masks of tile t and row
+  // indices of tile t+1 follow by direct copies, so nothing the copies need is
   // read from global memory between them.
   auto issue = [&](int tile, char* kbuf, const int* rows_t, unsigned char* mbuf, int* rows_t2) __attribute__((always_inline)) {
-    gather_kv_tile<TILE_KV>(kbuf, a.kv, a.s_kv, rows_t, min(TILE_KV, n_ent - tile * TILE_KV), wv,
-                            lane);
+    gather(kbuf, rows_t, min(TILE_KV, n_ent - tile * TILE_KV));
     copy_union_entries(nullptr, mbuf, erow, emask, tile * TILE_KV, n_ent, TILE_KV, wv, 1, 1, lane);
     if (tile + 1 < ntiles)
       copy_union_entries(rows_t2, nullptr, erow, emask, (tile + 1) * TILE_KV, n_ent, TILE_KV, wv,
@@ -98,66 +101,89 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
     // Prefetch the next tile into the other buffer (free: every wave has
     // passed the barrier above, so the previous tile's reads are done).
     if (tile + 1 < ntiles) issue(tile + 1, knext, rnext, mnext, rcur);
+    // Lane-derived LDS offsets are recomputed per tile from an opaque copy of
+    // the lane id rather than held in registers across the tile loop.
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int g16 = lane >> 4, r16 = lane & 15, wave = wv;
     float4_t s[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) s[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    // K fragments one k-step ahead of the MFMAs that use them; the
+    // scheduling barriers keep the compiler from sinking the reads onto
+    // their uses (which serialises every read with its MFMA).
+    short8_t kc[4], kn[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) kc[nt] = ld_b_rs<TILE_KV>(kt, nt * 16, 0, lane);
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
+      if (ks + 1 < 18) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const short8_t b = ld16_lds(kt + (nt * 16 + r16) * TILE_STRIDE + (4 * ks + g16) * 16);
-        s[nt] = mfma_bf16(qf[ks], b, s[nt]);
+        for (int nt = 0; nt < 4; ++nt) kn[nt] = ld_b_rs<TILE_KV>(kt, nt * 16, 32 * (ks + 1), lane);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) s[nt] = mfma_bf16(kc[nt], qf[ks], s[nt]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) kc[nt] = kn[nt];
     }
 
-    int mk[4];
+    // Online softmax of this lane's row over the tile's 64 entries.
+    float mx = -INFINITY;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) mk[nt] = mkb[nt * 16 + r16];
-    float alpha[4];
+    for (int nt = 0; nt < 4; ++nt) {
+      const unsigned mk = *reinterpret_cast<const unsigned*>(mkb + nt * 16 + 4 * g16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const bool v = (mk[nt] >> tl[i]) & 1;
+      for (int i = 0; i < 4; ++i) {
+        const bool v = (mk >> (8 * i + tl)) & 1u;
         const float x = v ? s[nt][i] * a.scale_log2 : -INFINITY;
         s[nt][i] = x;
         mx = fmaxf(mx, x);
       }
-      mx = max16(mx);
-      const float mn = fmaxf(m2[i], mx);
-      alpha[i] = fast_exp2(m2[i] - mn);
-      m2[i] = mn;
-      float rs = 0.f;
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool move = mx > m_run + RESCALE_SLACK;
+    float alpha = 1.f;
+    if (move) {
+      alpha = fast_exp2(m_run - mx);
+      m_run = mx;
+    }
+    float rs = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float p = fast_exp2(s[nt][i] - mn);
-        s[nt][i] = p;
-        rs += p;
+    for (int nt = 0; nt < 4; ++nt) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(s[nt][i] - m_run);
+        rs += p[i];
       }
-      lsum[i] = lsum[i] * alpha[i] + sum16(rs);
+      uint2 pk;
+      pk.x = pack_bf2(p[0], p[1]);
+      pk.y = pack_bf2(p[2], p[3]);
+      *reinterpret_cast<uint2*>(&sP[(16 * wave + r16) * 72 + nt * 16 + 4 * g16]) = pk;
     }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sP[(16 * wave + 4 * g16 + i) * 72 + nt * 16 + r16] = f2bf(s[nt][i]);
-    if (r16 == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sAlpha[16 * wave + 4 * g16 + i] = alpha[i];
-    }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    lsum = lsum * alpha + rs;
+    if (g16 == 0) sAlpha[16 * wave + r16] = alpha;
+    const bool wave_moved = __ballot(move) != 0ull;
+    if (lane == 0) sRescale[wave] = wave_moved ? 1 : 0;
     __syncthreads();
 
     // PV: this wave's 128 output columns for all 64 rows.
+    if (sRescale[0] | sRescale[1] | sRescale[2] | sRescale[3]) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      float al[4];
+      for (int rb = 0; rb < 4; ++rb) {
+        float al[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = sAlpha[16 * rb + 4 * g16 + i];
+        for (int i = 0; i < 4; ++i) al[i] = sAlpha[16 * rb + 4 * g16 + i];
 #pragma unroll
-      for (int n = 0; n < 8; ++n)
+        for (int n = 0; n < 8; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[rb][n][i] *= al[i];
+          for (int i = 0; i < 4; ++i) acc[rb][n][i] *= al[i];
+      }
     }
     short8_t pa[4][2];
 #pragma unroll
@@ -168,8 +194,8 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       const int col = 128 * wave + 16 * n;
-      const short8_t b0 = ld_b_tr(kt, TILE_STRIDE, 0, col, lane);
-      const short8_t b1 = ld_b_tr(kt, TILE_STRIDE, 32, col, lane);
+      const short8_t b0 = ld_bt_rs_lo<TILE_KV>(kt, 0, col, lane);
+      const short8_t b1 = ld_bt_rs_lo<TILE_KV>(kt, 32, col, lane);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         acc[rb][n] = mfma_bf16(pa[rb][0], b0, acc[rb][n]);
@@ -183,7 +209,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
     if (ntiles > 1) copy_union_entries(sRow[1], nullptr, erow, emask, TILE_KV, n_ent, TILE_KV, wv, 2, 2, lane);
     wait_vmcnt0();
     __syncthreads();
-    gather_kv_tile<TILE_KV>(sK[0], a.kv, a.s_kv, sRow[0], min(TILE_KV, n_ent), wv, lane);
+    gather(sK[0], sRow[0], min(TILE_KV, n_ent));
   }
   for (int tile = 0; tile < ntiles; ++tile) {
     const int b = tile & 1;
@@ -192,16 +218,13 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
 
   // Epilogue: LSE from the row owners, then normalised output through LDS.
   __syncthreads();
-  if (r16 == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * wave + 4 * g16 + i;
-      sL[rr] = lsum[i];
-      const int64_t tok = t0 + rr / H;
-      if (tok < a.s_q) {
-        const float m_eff = lsum[i] > 0.f ? m2[i] : 0.f;
-        a.lse[tok * H + rr % H] = (m_eff + fast_log2(fmaxf(lsum[i], SUMEXP_FLOOR))) * LN2;
-      }
+  if (g16 == 0) {
+    const int rr = 16 * wave + r16;
+    sL[rr] = lsum;
+    const int64_t tok = t0 + rr / H;
+    if (tok < a.s_q) {
+      const float m_eff = lsum > 0.f ? m_run : 0.f;
+      a.lse[tok * H + rr % H] = (m_eff + fast_log2(fmaxf(lsum, SUMEXP_FLOOR))) * LN2;
     }
   }
   __syncthreads();
