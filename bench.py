@@ -177,7 +177,7 @@ def main():
     # the per-kernel averages below come from these same K steps.
     timing = not args.no_kernel_timing
     if timing:
-        smla.timing_start(16 * args.steps)
+        smla.timing_start(32 * args.steps)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -204,7 +204,8 @@ def main():
     kernels = {}
     roofline = None
     if timing:
-        for name in ("fill", "plan", "fwd", "bwd_dq", "bwd_dkv"):
+        for name in ("fill", "plan", "order", "fwd", "bwd_dq", "dkv_schedule", "bwd_dkv",
+                     "dkv_finalize"):
             n, tot = smla.timing_read(name)
             if n:
                 kernels[name] = {"launches": n, "avg_ms": tot / n}

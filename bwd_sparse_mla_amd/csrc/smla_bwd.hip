@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, r16 = lane & 15;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int64_t grp = blockIdx.x;
+  const int64_t grp = a.gorder[blockIdx.x];
   const int64_t t0 = grp * T;
   const int n_ent = a.qcount[grp];
   const int32_t* erow = a.qrow + grp * a.qcap;
@@ -131,19 +131,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  // kv rows of a tile (count entries at rows_t in LDS) into a swizzled
-  // 32-row tile: 32 row copies and 4 tail copies, 9 per wave.
+  // kv rows of tile 0 (count entries at rows_t in LDS) into a swizzled
+  // 32-row tile.
   auto gather = [&](char* kbuf, const int* rows_t, int count) __attribute__((always_inline)) {
     gather_kv_rows<DQ_TILE, ROW_CHUNKS>(kbuf, a.kv, a.s_kv, rows_t, count, wv, lane);
-  };
-  // Tile t's kv rows are copied from rows_t (LDS); masks of tile t and row
-  // indices of tile t+1 follow by direct copies.
-  auto issue = [&](int tile, char* kbuf, const int* rows_t, unsigned char* mbuf, int* rows_t2) __attribute__((always_inline)) {
-    gather(kbuf, rows_t, min(DQ_TILE, n_ent - tile * DQ_TILE));
-    copy_union_entries(nullptr, mbuf, erow, emask, tile * DQ_TILE, n_ent, DQ_TILE, wv, 1, 1, lane);
-    if (tile + 1 < ntiles)
-      copy_union_entries(rows_t2, nullptr, erow, emask, (tile + 1) * DQ_TILE, n_ent, DQ_TILE, wv,
-                         2, 2, lane);
   };
 
   const char* drow = sDO + (16 * wave + r16) * DO_STRIDE + 16 * g16;  // A fragments of dout
@@ -151,9 +142,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
                   unsigned char* mnext, const int* rnext, int* rcur) __attribute__((always_inline)) {
     wait_vmcnt0();
     __syncthreads();
-    // Prefetch the next tile into the other buffer (free: every wave has
-    // passed the barrier above, so the previous tile's reads are done).
-    if (tile + 1 < ntiles) issue(tile + 1, knext, rnext, mnext, rcur);
+    // Prefetch into the other buffers (free: every wave has passed the
+    // barrier above, so the previous tile's reads are done): masks of tile+1
+    // and row indices of tile+2 now, the 9 kv copies of tile+1 spread over
+    // the score loop below (after the last tile they read the zero row into
+    // the spare buffer, which nothing reads).
+    const bool pre = tile + 1 < ntiles;
+    if (pre) {
+      copy_union_entries(nullptr, mnext, erow, emask, (tile + 1) * DQ_TILE, n_ent, DQ_TILE, wv, 1, 1,
+                         lane);
+      if (tile + 2 < ntiles)
+        copy_union_entries(rcur, nullptr, erow, emask, (tile + 2) * DQ_TILE, n_ent, DQ_TILE, wv, 2, 2,
+                           lane);
+    }
+    const KvGather<DQ_TILE> gnext = kv_gather_prepare<DQ_TILE>(
+        knext, a.kv, a.s_kv, rnext, pre ? min(DQ_TILE, n_ent - (tile + 1) * DQ_TILE) : 0, wv, lane);
     float4_t s[2], dp[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -167,24 +170,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) kc[nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 0, lane);
     dc = ld16_lds(drow);
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      if (ks + 1 < 18) {
+    static_for<18>([&](auto KS) __attribute__((always_inline)) {
+      constexpr int ks = decltype(KS)::value;
+      if constexpr (ks + 1 < 18) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) kn[nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * (ks + 1), lane);
-        if (ks + 1 < 16) dn = ld16_lds(drow + 64 * (ks + 1));
+        if constexpr (ks + 1 < 16) dn = ld16_lds(drow + 64 * (ks + 1));
       }
+      if constexpr (ks % 2 == 0) kv_gather_copy<DQ_TILE, ks / 2>(gnext, wv, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         s[nt] = mfma_bf16(kc[nt], qf[ks], s[nt]);
-        if (ks < 16) dp[nt] = mfma_bf16(kc[nt], dc, dp[nt]);
+        if constexpr (ks < 16) dp[nt] = mfma_bf16(kc[nt], dc, dp[nt]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) kc[nt] = kn[nt];
       dc = dn;
-    }
+    });
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const unsigned mk = *reinterpret_cast<const unsigned*>(mkb + nt * 16 + 4 * g16);
@@ -225,7 +229,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   }
 
   // Epilogue: dq = scale * acc, staged through LDS in two halves of 32 rows
-  // (sK[0] holds rows 0..31, sK[1] rows 32..63), then 16-byte stores.
+  // (sK[0] holds rows 0..31, sK[1] rows 32..63), then 16-byte stores (the
+  // spare buffer's last copies are drained first).
+  wait_vmcnt0();
   __syncthreads();
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
@@ -278,8 +284,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, r16 = lane & 15;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int64_t blk = blockIdx.x % a.NB;
-  const int split = (int)(blockIdx.x / a.NB);
+  const int item = a.korder[blockIdx.x];
+  const int64_t blk = item % a.NB;
+  const int split = (int)(item / a.NB);
   const int nch = a.nchunk[blk];
   const int nsplit = dkv_nsplit(nch, a.maxsplit);
   if (split >= nsplit) return;
@@ -474,6 +481,20 @@ __global__ __launch_bounds__(256) void dkv_schedule_kernel(BwdArgs a) {
   if (tid == 0) a.nchunk[blk] = base;
 }
 
+// Work order of the dkv items (split-major index split * NB + block) by
+// decreasing chunk count; items past a block's split count come last (they
+// exit at once).
+__global__ __launch_bounds__(256) void dkv_order_kernel(BwdArgs a) {
+  order_by_cost(a.NB * a.maxsplit, [&](int64_t i) {
+    const int64_t blk = i % a.NB;
+    const int split = (int)(i / a.NB);
+    const int nch = a.nchunk[blk];
+    const int ns = dkv_nsplit(nch, a.maxsplit);
+    if (split >= ns) return 0;
+    return (int)((int64_t)(split + 1) * nch / ns - (int64_t)split * nch / ns);
+  }, a.korder);
+}
+
 // Sum of 256 per-thread values, identical on every thread (fixed order).
 __device__ __forceinline__ float block_sum256(float v, float* red) {
 #pragma unroll
@@ -596,30 +617,36 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream) {
+hipError_t launch_dkv_schedule(const BwdArgs& a, hipStream_t stream) {
   if (a.NB == 0) return hipSuccess;
   dkv_schedule_kernel<<<dim3((unsigned)a.NB), dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  dkv_order_kernel<<<dim3(1), dim3(256), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream) {
+  if (a.NB == 0) return hipSuccess;
   const dim3 grid((unsigned)(a.NB * a.maxsplit)), block(256);
-  const dim3 fgrid((unsigned)(a.NB * 4));
   switch (heads) {
-    case 8:
-      bwd_dkv_kernel<8><<<grid, block, 0, stream>>>(a);
-      dkv_finalize_kernel<8><<<fgrid, block, 0, stream>>>(a);
-      break;
-    case 16:
-      bwd_dkv_kernel<16><<<grid, block, 0, stream>>>(a);
-      dkv_finalize_kernel<16><<<fgrid, block, 0, stream>>>(a);
-      break;
-    case 32:
-      bwd_dkv_kernel<32><<<grid, block, 0, stream>>>(a);
-      dkv_finalize_kernel<32><<<fgrid, block, 0, stream>>>(a);
-      break;
-    case 64:
-      bwd_dkv_kernel<64><<<grid, block, 0, stream>>>(a);
-      dkv_finalize_kernel<64><<<fgrid, block, 0, stream>>>(a);
-      break;
+    case 8: bwd_dkv_kernel<8><<<grid, block, 0, stream>>>(a); break;
+    case 16: bwd_dkv_kernel<16><<<grid, block, 0, stream>>>(a); break;
+    case 32: bwd_dkv_kernel<32><<<grid, block, 0, stream>>>(a); break;
+    case 64: bwd_dkv_kernel<64><<<grid, block, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dkv_finalize(const BwdArgs& a, int heads, hipStream_t stream) {
+  if (a.NB == 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.NB * 4)), block(256);
+  switch (heads) {
+    case 8: dkv_finalize_kernel<8><<<grid, block, 0, stream>>>(a); break;
+    case 16: dkv_finalize_kernel<16><<<grid, block, 0, stream>>>(a); break;
+    case 32: dkv_finalize_kernel<32><<<grid, block, 0, stream>>>(a); break;
+    case 64: dkv_finalize_kernel<64><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -108,6 +108,7 @@ Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward) {
   p.off_xcount = o;  o = align256(o + (size_t)p.G * 4);
   p.off_qrow = o;    o = align256(o + (size_t)p.G * p.qcap * 4);
   p.off_qmask = o;   o = align256(o + (size_t)p.G * p.qcap);
+  p.off_gorder = o;  o = align256(o + (size_t)p.G * 4);
   // xtotal sits directly before ktab so one fill clears both.
   p.off_xtotal = o;  o += 256;
   if (backward) {
@@ -120,6 +121,7 @@ Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward) {
     p.off_clist = o;   o = align256(o + (size_t)p.NB * p.G * 8);
     p.off_nchunk = o;  o = align256(o + (size_t)p.NB * 4);
     p.off_ptouch = o;  o = align256(o + (size_t)p.NB * p.maxsplit * 8);
+    p.off_korder = o;  o = align256(o + (size_t)p.NB * p.maxsplit * 4);
     p.off_part = o;    o = align256(o + (size_t)p.NB * p.maxsplit * TILE_KV * 576 * 4);
   }
   p.bytes = o;
@@ -191,6 +193,8 @@ int smla_fwd(const void* q, const void* kv, const int32_t* indices, int64_t s_q,
   pa.ktab = nullptr;
   if ((st = hip_status(timed("fill", s, [&] { return launch_fill_u32(pa.xtotal, 1, 0u, s); }), "fill"))) return st;
   if ((st = hip_status(timed("plan", s, [&] { return launch_plan(pa, heads, s); }), "plan"))) return st;
+  int* gorder = reinterpret_cast<int*>(ws + p.off_gorder);
+  if ((st = hip_status(timed("order", s, [&] { return launch_order_groups(pa.qcount, p.G, gorder, s); }), "order"))) return st;
 
   FwdArgs fa{};
   fa.q = static_cast<const uint16_t*>(q);
@@ -203,6 +207,7 @@ int smla_fwd(const void* q, const void* kv, const int32_t* indices, int64_t s_q,
   fa.qcount = pa.qcount;
   fa.qrow = pa.qrow;
   fa.qmask = pa.qmask;
+  fa.order = gorder;
   fa.out = static_cast<uint16_t*>(out);
   fa.lse = lse;
   return hip_status(timed("fwd", s, [&] { return launch_fwd(fa, heads, s); }), "fwd");
@@ -258,6 +263,8 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   const size_t clear_words = (256 + (size_t)p.NB * p.G * 8) / 4;
   if ((st = hip_status(timed("fill", s, [&] { return launch_fill_u32(pa.xtotal, clear_words, 0u, s); }), "fill"))) return st;
   if (s_q > 0 && (st = hip_status(timed("plan", s, [&] { return launch_plan(pa, heads, s); }), "plan"))) return st;
+  int* gorder = reinterpret_cast<int*>(ws + p.off_gorder);
+  if (s_q > 0 && (st = hip_status(timed("order", s, [&] { return launch_order_groups(pa.qcount, p.G, gorder, s); }), "order"))) return st;
 
   BwdArgs ba{};
   ba.q = static_cast<const uint16_t*>(q);
@@ -280,6 +287,8 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   ba.qmask = pa.qmask;
   ba.ktab = pa.ktab;
   ba.krmask = pa.krmask;
+  ba.gorder = gorder;
+  ba.korder = reinterpret_cast<int*>(ws + p.off_korder);
   ba.delta = reinterpret_cast<float*>(ws + p.off_delta);
   ba.clist = reinterpret_cast<int2*>(ws + p.off_clist);
   ba.nchunk = reinterpret_cast<int*>(ws + p.off_nchunk);
@@ -291,7 +300,9 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   ba.dkv_f32 = dkv_f32;
   ba.accumulate = (flags & SMLA_DKV_ACCUMULATE) ? 1 : 0;
   if (s_q > 0 && (st = hip_status(timed("bwd_dq", s, [&] { return launch_bwd_dq(ba, heads, s); }), "bwd_dq"))) return st;
-  return hip_status(timed("bwd_dkv", s, [&] { return launch_bwd_dkv(ba, heads, s); }), "bwd_dkv");
+  if ((st = hip_status(timed("dkv_schedule", s, [&] { return launch_dkv_schedule(ba, s); }), "dkv_schedule"))) return st;
+  if ((st = hip_status(timed("bwd_dkv", s, [&] { return launch_bwd_dkv(ba, heads, s); }), "bwd_dkv"))) return st;
+  return hip_status(timed("dkv_finalize", s, [&] { return launch_dkv_finalize(ba, heads, s); }), "dkv_finalize");
 }
 
 int smla_validate_indices(const int32_t* indices, int64_t s_q, int32_t topk, int64_t s_kv,

@@ -164,6 +164,18 @@ __device__ __forceinline__ void g2lds16_s(const void* sbase, uint32_t voff, uint
                :: "v"(voff), "s"(sbase), "s"(lds_u32) : "memory", "m0");
 }
 
+// Compile-time loop: f(Int<0>{}), ..., f(Int<N-1>{}).
+template <int I> struct Int { static constexpr int value = I; };
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_from(F& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_from<0, N>(f); }
+
 // s_waitcnt vmcnt(0) (other counters untouched).
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -206,6 +218,42 @@ __device__ __forceinline__ int block_exclusive_scan256(int v, int* scratch, int*
   __syncthreads();
   *total = tot;
   return base + x - v;
+}
+
+// Work order by decreasing cost (largest first), so the hardware's in-order
+// workgroup dispatch approximates longest-processing-time scheduling: a
+// counting sort on min(cost, ORDER_BUCKETS - 1).  Items of equal cost come in
+// no particular order; each item writes its own outputs, so the order never
+// changes a result.  One workgroup of 256 threads.
+constexpr int ORDER_BUCKETS = 4096;
+template <class Cost>
+__device__ __forceinline__ void order_by_cost(int64_t n, Cost cost, int* order) {
+  __shared__ int pos[ORDER_BUCKETS];
+  __shared__ int scratch[8];
+  const int tid = threadIdx.x;
+  for (int b = tid; b < ORDER_BUCKETS; b += 256) pos[b] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += 256) atomicAdd(&pos[min(cost(i), ORDER_BUCKETS - 1)], 1);
+  __syncthreads();
+  // Thread t owns buckets 4095 - 16t down to 4080 - 16t (descending cost).
+  int cnt[16], sum = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    cnt[k] = pos[ORDER_BUCKETS - 1 - 16 * tid - k];
+    sum += cnt[k];
+  }
+  int total;
+  int base = block_exclusive_scan256(sum, scratch, &total);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    pos[ORDER_BUCKETS - 1 - 16 * tid - k] = base;
+    base += cnt[k];
+  }
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += 256) {
+    const int slot = atomicAdd(&pos[min(cost(i), ORDER_BUCKETS - 1)], 1);
+    order[slot] = (int)i;
+  }
 }
 
 // Zeros that padding lanes of the LDS copies read from: a whole 576-column
@@ -270,6 +318,81 @@ __device__ __forceinline__ void gather_seq_rows(char* tile, const uint16_t* firs
                             8 * ((lane & 7) ^ swz_hi(r));
       g2lds16_u(src, base + (uint32_t)(R * 1024 + 1024 * jj));
     }
+  }
+}
+
+// Incremental form of the gathers: prepare once, then issue copy J (a
+// compile-time index) where it fits in the caller's instruction stream.
+// For a kv gather of R rows, wave wv issues R/4 row copies (J < R/4) and
+// R/32 tail copies (J = R/4 + j); a kv tile thus takes R/4 + R/32 copies per
+// wave (18 for R = 64, 9 for R = 32).  Row selection is branch-free: rows
+// past `count` and indices outside [0, s_kv) read the zero row.
+template <int R>
+struct KvGather {
+  const uint16_t* kv;
+  const uint16_t* zero;
+  uint32_t base;      // LDS byte address of the tile
+  uint32_t s_kv;
+  int count;
+  int vrow;           // lane i < R/4: row index of tile row R/4 * wv + i
+  int vtail[R / 32];  // tail copy j: row index of tile row 8 (wv + 4j) + lane / 8
+};
+template <int R>
+__device__ __forceinline__ KvGather<R> kv_gather_prepare(char* tile, const uint16_t* kv, int64_t s_kv,
+                                                         const int* rows, int count, int wv, int lane) {
+  KvGather<R> g;
+  g.kv = kv;
+  g.zero = g_zero_row;
+  g.base = lds_offset(tile);
+  g.s_kv = (uint32_t)s_kv;
+  g.count = count;
+  g.vrow = rows[(R / 4) * wv + (lane & (R / 4 - 1))];
+#pragma unroll
+  for (int j = 0; j < R / 32; ++j) g.vtail[j] = rows[8 * (wv + 4 * j) + (lane >> 3)];
+  return g;
+}
+template <int R, int J>
+__device__ __forceinline__ void kv_gather_copy(const KvGather<R>& g, int wv, int lane) {
+  constexpr int PER = R / 4;
+  if constexpr (J < PER) {
+    const int r = PER * wv + J;
+    const int row = __builtin_amdgcn_readlane(g.vrow, J);
+    const bool ok = r < g.count && (uint32_t)row < g.s_kv;
+    const uint16_t* src = (ok ? g.kv : g.zero) + (uint32_t)(ok ? row : 0) * (uint32_t)D_K;
+    g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), g.base + 1024u * (uint32_t)r);
+  } else if constexpr (J < PER + R / 32) {
+    constexpr int j = J - PER;
+    const int jj = wv + 4 * j;
+    const int r = 8 * jj + (lane >> 3);
+    const int row = g.vtail[j];
+    const bool ok = r < g.count && (uint32_t)row < g.s_kv;
+    const uint16_t* src = (ok ? g.kv + (uint64_t)(uint32_t)row * D_K : g.zero) + D_V +
+                          8 * ((lane & 7) ^ swz_hi(r));
+    g2lds16_u(src, g.base + (uint32_t)(R * 1024 + 1024 * jj));
+  }
+}
+// Copy J of a gather of R contiguous rows of CH chunks starting at `first`
+// (rows >= nvalid read the zero row): J < R/4 row copies, then R/32 tail
+// copies when CH = 72.
+template <int R, int CH, int J>
+__device__ __forceinline__ void seq_gather_copy(char* tile, const uint16_t* first, int nvalid,
+                                                int wv, int lane) {
+  constexpr int PER = R / 4;
+  constexpr int W = CH * 8;
+  const uint32_t base = lds_offset(tile);
+  if constexpr (J < PER) {
+    const int r = PER * wv + J;
+    const bool ok = r < nvalid;
+    const uint16_t* src = (ok ? first : g_zero_row) + (uint32_t)(ok ? r : 0) * (uint32_t)W;
+    g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), base + 1024u * (uint32_t)r);
+  } else if constexpr (CH == ROW_CHUNKS && J < PER + R / 32) {
+    constexpr int j = J - PER;
+    const int jj = wv + 4 * j;
+    const int r = 8 * jj + (lane >> 3);
+    const bool ok = r < nvalid;
+    const uint16_t* src = (ok ? first + (uint32_t)r * (uint32_t)W : g_zero_row) + D_V +
+                          8 * ((lane & 7) ^ swz_hi(r));
+    g2lds16_u(src, base + (uint32_t)(R * 1024 + 1024 * jj));
   }
 }
 

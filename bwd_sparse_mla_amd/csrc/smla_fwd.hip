@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, r16 = lane & 15;
-  const int64_t grp = blockIdx.x;
+  const int64_t grp = a.order[blockIdx.x];
   const int64_t t0 = grp * T;
   const int n_ent = a.qcount[grp];
   const int32_t* erow = a.qrow + grp * a.qcap;

@@ -29,6 +29,7 @@ struct Plan {
   size_t off_qcount = 0, off_xcount = 0, off_xtotal = 0, off_qrow = 0, off_qmask = 0;
   size_t off_ktab = 0, off_krmask = 0, off_delta = 0;
   size_t off_clist = 0, off_nchunk = 0, off_part = 0, off_ptouch = 0;
+  size_t off_gorder = 0, off_korder = 0;
   int maxsplit = 1;   // dkv partial sums per kv block (split over its records)
   size_t bytes = 0;
 };
@@ -58,6 +59,7 @@ struct FwdArgs {
   const int* qcount;
   const int32_t* qrow;
   const uint8_t* qmask;
+  const int* order;   // [G] groups by decreasing union size: workgroup i runs order[i]
   uint16_t* out;
   float* lse;
 };
@@ -78,6 +80,8 @@ struct BwdArgs {
   const uint8_t* qmask;
   const int2* ktab;
   const unsigned long long* krmask;
+  const int* gorder;  // [G] groups by decreasing union size (dq pass)
+  int* korder;        // [NB * maxsplit] dkv items by decreasing chunk count
   float* delta;       // [s_q * H] rowsum(dout * out), written by the dq pass
   int2* clist;        // [NB, G] per block: (group, record start), compacted
   int* nchunk;        // [NB] entries of clist per block
@@ -94,7 +98,12 @@ hipError_t launch_fill_u32(void* ptr, size_t n_words, uint32_t value, hipStream_
 hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream);
+// Work order of the query groups: decreasing union size (largest first).
+hipError_t launch_order_groups(const int* qcount, int64_t G, int* order, hipStream_t stream);
+// dkv pass: schedule (chunk lists and work order), main kernel, finalize.
+hipError_t launch_dkv_schedule(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream);
+hipError_t launch_dkv_finalize(const BwdArgs& a, int heads, hipStream_t stream);
 // dkv split schedule: chunks a split covers at least, and the split count.
 constexpr int DKV_MIN_CHUNKS = 8;
 __host__ __device__ inline int dkv_nsplit(int nchunk, int maxsplit) {

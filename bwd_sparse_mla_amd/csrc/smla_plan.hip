@@ -66,24 +66,29 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   for (int w = tid; w < nxw; w += 256) xflag[w] = 0u;
   __syncthreads();
 
-  // Span of the valid rows this group selects.
-  int lo = 0x7fffffff, hi = -1;
-  for (int s = tid; s < nslots; s += 256) {
-    const int v = ix[s];
-    if (v >= 0 && v < skv) {
-      lo = min(lo, v);
-      hi = max(hi, v);
+  // Span of the valid rows this group selects (one window from row 0 covers
+  // every valid row when s_kv <= WIN_BITS; the scan is skipped then).
+  int lo = 0, hi = skv - 1;
+  if (skv > WIN_BITS) {
+    lo = 0x7fffffff;
+    hi = -1;
+    for (int s = tid; s < nslots; s += 256) {
+      const int v = ix[s];
+      if (v >= 0 && v < skv) {
+        lo = min(lo, v);
+        hi = max(hi, v);
+      }
     }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if ((tid & 63) == 0) {
+      atomicMin(&s_lo, lo);
+      atomicMax(&s_hi, hi);
+    }
+    __syncthreads();
+    lo = s_lo;
+    hi = s_hi;
   }
-  lo = wave_min(lo);
-  hi = wave_max(hi);
-  if ((tid & 63) == 0) {
-    atomicMin(&s_lo, lo);
-    atomicMax(&s_hi, hi);
-  }
-  __syncthreads();
-  lo = s_lo;
-  hi = s_hi;
 
   int32_t* qrow = a.qrow + g * a.qcap;
   uint8_t* qmask = a.qmask + g * a.qcap;
@@ -104,15 +109,18 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     }
     __syncthreads();
 
-    // Union entries, ascending row order: thread tid owns words 2tid, 2tid+1.
-    unsigned U[2];
+    // Union entries, ascending row order: thread tid owns words 2tid, 2tid+1
+    // (the T token words of each are read into registers once).
+    unsigned W[2][T], U[2];
     int c = 0;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int w = 2 * tid + k;
       unsigned u = 0;
 #pragma unroll
-      for (int t = 0; t < T; ++t) u |= bm[t][w];
+      for (int t = 0; t < T; ++t) {
+        W[k][t] = bm[t][2 * tid + k];
+        u |= W[k][t];
+      }
       U[k] = u;
       c += __popc(u);
     }
@@ -120,15 +128,15 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     int pos = qbase + block_exclusive_scan256(c, scratch, &total);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int w = 2 * tid + k;
+      const int row0 = w0 + 32 * (2 * tid + k);
       unsigned u = U[k];
       while (u) {
         const int b = __ffs(u) - 1;
         u &= u - 1;
         unsigned mask = 0;
 #pragma unroll
-        for (int t = 0; t < T; ++t) mask |= ((bm[t][w] >> b) & 1u) << t;
-        qrow[pos] = w0 + 32 * w + b;
+        for (int t = 0; t < T; ++t) mask |= ((W[k][t] >> b) & 1u) << t;
+        qrow[pos] = row0 + b;
         qmask[pos] = (uint8_t)mask;
         ++pos;
       }
@@ -191,6 +199,10 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   if (tid < 64 && n_all + tid < ((n_all + 63) & ~63)) qmask[n_all + tid] = 0;
 }
 
+__global__ __launch_bounds__(256) void order_groups_kernel(const int* qcount, int64_t G, int* order) {
+  order_by_cost(G, [&](int64_t g) { return (qcount[g] + 31) >> 5; }, order);
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -212,6 +224,12 @@ __global__ void validate_kernel(const int32_t* idx, int64_t n, int64_t s_kv,
 }
 
 }  // namespace
+
+hipError_t launch_order_groups(const int* qcount, int64_t G, int* order, hipStream_t stream) {
+  if (G == 0) return hipSuccess;
+  order_groups_kernel<<<1, 256, 0, stream>>>(qcount, G, order);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream) {
   if (a.G == 0) return hipSuccess;

@@ -118,13 +118,15 @@ int smla_validate_indices(const int32_t* indices, int64_t s_q, int32_t topk, int
                           unsigned long long* n_bad, void* stream);
 
 /* Kernel timing, for benchmarks (not thread-safe).  Between
- * smla_timing_start(max_launches) and smla_timing_stop(), every kernel this
- * library launches is bracketed by two HIP events recorded on its stream (at
- * most max_launches kernels are recorded; the events are created by
+ * smla_timing_start(max_launches) and smla_timing_stop(), every launch step
+ * of this library is bracketed by two HIP events recorded on its stream (at
+ * most max_launches steps are recorded; the events are created by
  * smla_timing_start and destroyed by the next start).  smla_timing_read waits
- * for the recorded events of the kernels named `kernel` ("fill", "plan",
- * "fwd", "bwd_dq", "bwd_dkv", "validate") and returns how many were recorded
- * and their summed duration in milliseconds. */
+ * for the recorded events of the steps named `kernel` and returns how many
+ * were recorded and their summed duration in milliseconds.  Step names:
+ * "fill", "plan", "order" (work order of the query groups), "fwd",
+ * "bwd_dq", "dkv_schedule" (chunk lists and dkv work order: two small
+ * kernels), "bwd_dkv" (the dkv kernel alone), "dkv_finalize", "validate". */
 int smla_timing_start(int max_launches);
 int smla_timing_stop(void);
 int smla_timing_read(const char* kernel, int* launches, double* total_ms);
