@@ -36,10 +36,14 @@ SM_SCALE = 1.0 / math.sqrt(192.0)
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest, ties to even); return the bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    rounding = np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))
-    out = ((b + rounding) >> np.uint64(16)).astype(np.uint16)
-    return out
+    flat = x.reshape(-1).view(np.uint32)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    step = 1 << 24
+    for i in range(0, flat.size, step):           # bounded temporaries on large tensors
+        b = flat[i:i + step].astype(np.uint64)
+        rounding = np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))
+        out[i:i + step] = ((b + rounding) >> np.uint64(16)).astype(np.uint16)
+    return out.reshape(x.shape)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -86,11 +90,33 @@ class Workload:
         return int(np.count_nonzero((self.idx >= 0) & (self.idx < self.S_kv)))
 
 
+_CHUNK = 1 << 22   # values per independently seeded chunk of a large tensor
+
+
 def _normal_bf16(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if sigma != 1.0:
-        x *= np.float32(sigma)
-    return f32_to_bf16_bits(x)
+    """N(0, sigma^2) values rounded to bf16.  The tensor is cut into chunks of
+    _CHUNK values, each drawn from its own generator seeded from `rng` (so the
+    result depends only on the seed), generated on a few threads."""
+    n = int(np.prod(shape))
+    nchunk = (n + _CHUNK - 1) // _CHUNK
+    seeds = rng.integers(0, 2**63 - 1, size=nchunk, dtype=np.int64)
+    out = np.empty(n, dtype=np.uint16)
+
+    def work(i):
+        g = np.random.default_rng(int(seeds[i]))
+        lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        x = g.standard_normal(size=hi - lo, dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        out[lo:hi] = f32_to_bf16_bits(x)
+
+    if nchunk == 1:
+        work(0)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(8, nchunk)) as ex:
+            list(ex.map(work, range(nchunk)))
+    return out.reshape(shape)
 
 
 def _tensors(rng, S, H, S_kv, sigma=1.0):
@@ -118,40 +144,62 @@ def causal_full_rows(rng, seqlens, K) -> np.ndarray:
     return idx
 
 
+def _uniform_picks(rng, cand: np.ndarray, k: int, batch: int = 256) -> np.ndarray:
+    """Row i: min(k, cand[i]) distinct values of range(cand[i]) drawn uniformly,
+    in random order, then -1.  Random-key sampling: every candidate gets an
+    independent uniform key, the k smallest keys are kept, in key order."""
+    n = len(cand)
+    out = np.full((n, k), -1, dtype=np.int64)
+    for b in range(0, n, batch):
+        c = np.asarray(cand[b:b + batch], dtype=np.int64)
+        m = int(c.max()) if c.size else 0
+        if m == 0:
+            continue
+        keys = rng.random((len(c), m))
+        keys[np.arange(m)[None, :] >= c[:, None]] = np.inf
+        kk = min(k, m)
+        part = np.argpartition(keys, kk - 1, axis=1)[:, :kk]
+        pk = np.take_along_axis(keys, part, 1)
+        order = np.argsort(pk, axis=1)
+        sel = np.take_along_axis(part, order, 1)
+        ok = np.take_along_axis(pk, order, 1) < np.inf
+        out[b:b + len(c), :kk] = np.where(ok, sel, -1)
+    return out
+
+
 def causal_uniform_rows(rng, seqlens, K) -> np.ndarray:
     """Row p picks min(K, p+1) distinct causal in-sequence positions uniformly
     (in random order); the rest of the row is -1."""
     S = int(sum(seqlens))
     idx = np.full((S, K), -1, dtype=np.int32)
     for start, n in zip(_starts(seqlens), seqlens):
-        for p in range(n):
-            cand = p + 1
-            if cand <= K:
-                row = rng.permutation(cand)
-            else:
-                row = rng.choice(cand, size=K, replace=False, shuffle=True)
-            idx[start + p, : len(row)] = row.astype(np.int32) + np.int32(start)
+        picks = _uniform_picks(rng, np.arange(1, n + 1), K)
+        idx[start:start + n] = np.where(picks >= 0, picks + start, -1).astype(np.int32)
     return idx
 
 
 def causal_recency_rows(rng, seqlens, K, recent=512) -> np.ndarray:
     """Rows with at least K candidates take every one of the last `recent`
-    positions plus K-`recent` distinct uniform picks from the older positions;
-    shorter rows list every causal position.  (One reading of "half the picks
-    from the last 512 positions": half of K=2048 cannot be met with distinct
-    picks out of 512 positions, so all 512 are taken and the rest are uniform.)"""
+    positions plus K-`recent` distinct uniform picks from the older positions
+    (all in random order); shorter rows list every causal position.  (One
+    reading of "half the picks from the last 512 positions": half of K=2048
+    cannot be met with distinct picks out of 512 positions, so all 512 are
+    taken and the rest are uniform.)"""
     S = int(sum(seqlens))
     idx = np.full((S, K), -1, dtype=np.int32)
     for start, n in zip(_starts(seqlens), seqlens):
-        for p in range(n):
-            cand = p + 1
-            if cand <= K:
-                row = rng.permutation(cand)
-            else:
-                old = rng.choice(cand - recent, size=K - recent, replace=False, shuffle=False)
-                row = np.concatenate([np.arange(cand - recent, cand), old])
-                row = row[rng.permutation(K)]
-            idx[start + p, : len(row)] = row.astype(np.int32) + np.int32(start)
+        cand = np.arange(1, n + 1)
+        short = cand <= K
+        rows = np.full((n, K), -1, dtype=np.int64)
+        rows[short] = _uniform_picks(rng, cand[short], K)
+        longr = np.nonzero(~short)[0]
+        if longr.size:
+            old = _uniform_picks(rng, cand[longr] - recent, K - recent)
+            recent_rows = (cand[longr] - recent)[:, None] + np.arange(recent)[None, :]
+            full = np.concatenate([recent_rows, old], axis=1)
+            perm = np.argsort(rng.random(full.shape), axis=1)
+            rows[longr] = np.take_along_axis(full, perm, 1)
+        idx[start:start + n] = np.where(rows >= 0, rows + start, -1).astype(np.int32)
     return idx
 
 
