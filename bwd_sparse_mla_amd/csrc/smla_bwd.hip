@@ -506,29 +506,30 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
   return r;
 }
 
-// Writes dkv for 16 rows of a block (4 workgroups per block): the block's
-// split partials added in split order, plus -- only when some index row
-// repeats an entry -- the extra slots' contributions, each computed directly
-// in (group, slot) order.  Output semantics (bf16, fp32, accumulate, rows no
-// slot selects) are applied here.  Bitwise reproducible.
+// Writes dkv for FIN_ROWS rows of a block (64 / FIN_ROWS workgroups per
+// block): the block's split partials added in split order, plus -- only when
+// some index row repeats an entry -- the extra slots' contributions, each
+// computed directly in (group, slot) order.  Output semantics (bf16, fp32,
+// accumulate, rows no slot selects) are applied here.  Bitwise reproducible.
+constexpr int FIN_ROWS = 4;
+constexpr int FIN_PARTS = TILE_KV / FIN_ROWS;   // workgroups per block
 template <int H>
 __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
-  __shared__ float sX[16 * D_K];   // extra-slot contributions of the 16 rows
+  __shared__ float sX[FIN_ROWS * D_K];   // extra-slot contributions of the rows
   __shared__ float red[4];
-  __shared__ int sHave;
   const int tid = threadIdx.x;
-  const int64_t blk = blockIdx.x >> 2;
-  const int quarter = blockIdx.x & 3;
-  const int64_t r0 = blk * TILE_KV + 16 * quarter;  // first row of this workgroup
+  const int64_t blk = blockIdx.x / FIN_PARTS;
+  const int part = blockIdx.x % FIN_PARTS;
+  const int64_t r0 = blk * TILE_KV + FIN_ROWS * part;  // first row of this workgroup
   const int nsplit = dkv_nsplit(a.nchunk[blk], a.maxsplit);
   unsigned long long touched = 0ull;
   for (int sp = 0; sp < nsplit; ++sp) touched |= a.ptouch[blk * a.maxsplit + sp];
-  touched = (touched >> (16 * quarter)) & 0xFFFFull;
+  touched = (touched >> (FIN_ROWS * part)) & ((1ull << FIN_ROWS) - 1ull);
 
   const bool extras = *a.xtotal > 0;
   if (extras) {
-    for (int e = tid; e < 16 * D_K; e += 256) sX[e] = 0.f;
+    for (int e = tid; e < FIN_ROWS * D_K; e += 256) sX[e] = 0.f;
     __syncthreads();
     for (int64_t g = 0; g < a.G; ++g) {
       const int xc = a.xcount[g];
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
       const int n_main = a.qcount[g] - xc;
       for (int x = 0; x < xc; ++x) {
         const int64_t row = a.qrow[g * a.qcap + n_main + x];
-        if (row < r0 || row >= r0 + 16 || row >= a.s_kv) continue;
+        if (row < r0 || row >= r0 + FIN_ROWS || row >= a.s_kv) continue;
         int64_t t = g * T + (__ffs((unsigned)a.qmask[g * a.qcap + n_main + x]) - 1);
         t = t < 0 ? 0 : (t >= a.s_q ? a.s_q - 1 : t);
         const int rl = (int)(row - r0);
@@ -567,12 +568,24 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  const float* src = a.part + (blk * a.maxsplit * TILE_KV + 16 * quarter) * D_K;
-  constexpr int N4 = 16 * D_K / 4;  // float4 elements of 16 rows
+  const float* src = a.part + (blk * a.maxsplit * TILE_KV + FIN_ROWS * part) * D_K;
+  constexpr int N4 = FIN_ROWS * D_K / 4;  // float4 elements of the rows
+  constexpr int64_t SPLIT = (int64_t)TILE_KV * D_K;
   for (int e = tid; e < N4; e += 256) {
-    float4_t v = *reinterpret_cast<const float4_t*>(src + 4 * e);
-    for (int sp = 1; sp < nsplit; ++sp)
-      v += *reinterpret_cast<const float4_t*>(src + (int64_t)sp * TILE_KV * D_K + 4 * e);
+    // Split partials summed left to right in split order; loads go out four
+    // at a time (indices clamped into range, extra ones unused).
+    const float* pe = src + 4 * e;
+    float4_t v = *reinterpret_cast<const float4_t*>(pe);
+    for (int sp = 1; sp < nsplit; sp += 4) {
+      const float4_t p0 = *reinterpret_cast<const float4_t*>(pe + sp * SPLIT);
+      const float4_t p1 = *reinterpret_cast<const float4_t*>(pe + min(sp + 1, nsplit - 1) * SPLIT);
+      const float4_t p2 = *reinterpret_cast<const float4_t*>(pe + min(sp + 2, nsplit - 1) * SPLIT);
+      const float4_t p3 = *reinterpret_cast<const float4_t*>(pe + min(sp + 3, nsplit - 1) * SPLIT);
+      v += p0;
+      if (sp + 1 < nsplit) v += p1;
+      if (sp + 2 < nsplit) v += p2;
+      if (sp + 3 < nsplit) v += p3;
+    }
     if (extras) v += *reinterpret_cast<const float4_t*>(sX + 4 * e);
     const int kvl = (4 * e) / D_K;
     const int col = (4 * e) % D_K;
@@ -641,7 +654,7 @@ hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream) {
 
 hipError_t launch_dkv_finalize(const BwdArgs& a, int heads, hipStream_t stream) {
   if (a.NB == 0) return hipSuccess;
-  const dim3 grid((unsigned)(a.NB * 4)), block(256);
+  const dim3 grid((unsigned)(a.NB * FIN_PARTS)), block(256);
   switch (heads) {
     case 8: dkv_finalize_kernel<8><<<grid, block, 0, stream>>>(a); break;
     case 16: dkv_finalize_kernel<16><<<grid, block, 0, stream>>>(a); break;

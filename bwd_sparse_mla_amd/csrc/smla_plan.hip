@@ -97,51 +97,56 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   for (int w0 = (hi >= 0 ? (lo & ~63) : 1); w0 <= hi; w0 += WIN_BITS) {
     for (int i = tid; i < T * WIN_WORDS; i += 256) (&bm[0][0])[i] = 0u;
     __syncthreads();
-    for (int s = tid; s < nslots; s += 256) {
-      const int v = ix[s];
-      if (v >= w0 && v < w0 + WIN_BITS && v < skv) {
-        const int t = s / K;
-        const int bit = v - w0;
-        const unsigned m = 1u << (bit & 31);
-        const unsigned old = atomicOr(&bm[t][bit >> 5], m);
-        if (old & m) atomicOr(&xflag[s >> 5], 1u << (s & 31));
+    // 16 index loads in flight per thread before their bitmap updates.
+    for (int s0 = tid; s0 < nslots; s0 += 256 * 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int s = s0 + 256 * j;
+        v[j] = s < nslots ? ix[s] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int s = s0 + 256 * j;
+        if (v[j] >= w0 && v[j] < w0 + WIN_BITS && v[j] < skv) {
+          const int t = s / K;
+          const int bit = v[j] - w0;
+          const unsigned m = 1u << (bit & 31);
+          const unsigned old = atomicOr(&bm[t][bit >> 5], m);
+          if (old & m) atomicOr(&xflag[s >> 5], 1u << (s & 31));
+        }
       }
     }
     __syncthreads();
 
-    // Union entries, ascending row order: thread tid owns words 2tid, 2tid+1
-    // (the T token words of each are read into registers once).
-    unsigned W[2][T], U[2];
-    int c = 0;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      unsigned u = 0;
+    // Union entries, ascending row order.  Thread tid owns bytes tid + 256k
+    // (k = 0..7) of the window's bitmap, so a contiguous union spreads over
+    // many threads; each round k is one block-wide scan in row order.
+#pragma unroll 1
+    for (int k = 0; k < WIN_WORDS * 4 / 256; ++k) {
+      const int byte = tid + 256 * k;
+      const int w = byte >> 2, sh = 8 * (byte & 3);
+      unsigned tb[T], u = 0;
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        W[k][t] = bm[t][2 * tid + k];
-        u |= W[k][t];
+        tb[t] = (bm[t][w] >> sh) & 0xFFu;
+        u |= tb[t];
       }
-      U[k] = u;
-      c += __popc(u);
-    }
-    int total;
-    int pos = qbase + block_exclusive_scan256(c, scratch, &total);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int row0 = w0 + 32 * (2 * tid + k);
-      unsigned u = U[k];
+      int total;
+      int pos = qbase + block_exclusive_scan256(__popc(u), scratch, &total);
+      const int row0 = w0 + 8 * byte;
       while (u) {
         const int b = __ffs(u) - 1;
         u &= u - 1;
         unsigned mask = 0;
 #pragma unroll
-        for (int t = 0; t < T; ++t) mask |= ((W[k][t] >> b) & 1u) << t;
+        for (int t = 0; t < T; ++t) mask |= ((tb[t] >> b) & 1u) << t;
         qrow[pos] = row0 + b;
         qmask[pos] = (uint8_t)mask;
         ++pos;
       }
+      qbase += total;
     }
-    qbase += total;
 
     if (a.ktab) {
       // kv-block records: thread tid owns block (w0 >> 6) + tid.  A block any
