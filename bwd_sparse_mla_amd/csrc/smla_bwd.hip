@@ -269,8 +269,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 // split-major, so every block's first split goes first.
 constexpr int DKV_SUB = 32;                                 // query rows per sub-chunk
 
+constexpr int DKV_NW = 8;                                   // waves per workgroup
+
 template <int H>
-__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
   constexpr int SP = DKV_SUB + 8;  // P^T / dS^T row stride (bf16): 80 bytes
   __shared__ __attribute__((aligned(16))) char sQ[2][KV32_TILE_BYTES];
@@ -281,9 +283,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned short sPT[TILE_KV * SP];
   __shared__ __attribute__((aligned(16))) unsigned short sDST[TILE_KV * SP];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g16 = lane >> 4, r16 = lane & 15;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int tid = threadIdx.x, lane_id = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int item = a.korder[blockIdx.x];
   const int64_t blk = item % a.NB;
   const int split = (int)(item / a.NB);
@@ -296,13 +297,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
   const int64_t kb0 = blk * TILE_KV;
   const int64_t qrows = a.s_q * H;   // rows of q / dout / lse / delta
 
-  // This wave's 16 kv rows as A fragments (K for S^T; their first 512
-  // columns, ks < 16, are V for dP^T).
+  // Scores / dP: wave w takes kv rows 16 (w & 3) + r (their K fragments stay
+  // in registers: the B operand, K^T; the first 512 columns, ks < 16, are V
+  // for dP) against query rows 16 (w >> 2) .. +15 of the sub-chunk.
+  const int skb = wv & 3, sqh = wv >> 2;
+  // dK / dV: wave w accumulates kv rows 32 (w & 1) .. +31 (two 16-row
+  // blocks) x columns 144 (w >> 1) .. +143.
+  const int drh = wv & 1, dcq = wv >> 1;
   short8_t kf[18];
   {
-    const int64_t row = kb0 + 16 * wave + r16;
+    const int64_t row = kb0 + 16 * skb + (lane_id & 15);
     if (row < a.s_kv) {
-      const uint16_t* kr = a.kv + row * D_K + 8 * g16;
+      const uint16_t* kr = a.kv + row * D_K + 8 * (lane_id >> 4);
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) kf[ks] = ld16_global(kr + 32 * ks);
     } else {
@@ -310,35 +316,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
       for (int ks = 0; ks < 18; ++ks) kf[ks] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  float4_t acc[4][9];
+  float4_t acc[2][9];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
   unsigned long long touched = 0ull;
 
   const uint64_t zero = reinterpret_cast<uint64_t>(zero_row());
-  const int lane_id = lane;
   // Copies of sub-chunk u into one buffer set: Q and dout rows as swizzled
-  // 32-row tiles (36 + 32 copies, 17 per wave), then the token masks, lse and
-  // delta of the 32 rows (one copy each, waves 0, 1, 2).
+  // 32-row tiles (36 + 32 copies, 8-9 per wave), then the token masks, lse
+  // and delta of the 32 rows (one copy each, waves 5, 6, 7).
   auto issue = [&](int u, char* q_dst, char* d_dst, unsigned* m_dst, float* l_dst, float* e_dst) __attribute__((always_inline)) {
     const int2 ce = a.clist[blk * a.G + c_lo + (u >> 1)];  // (group, record start)
-    // Lane-derived offsets are recomputed per sub-chunk from an opaque copy
-    // of the lane id rather than held in registers across the loop.
     int lane = lane_id;
-    asm volatile("" : "+v"(lane));
+    asm volatile("" : "+v"(lane));   // offsets recomputed per sub-chunk, not kept live
     const int64_t row0 = (int64_t)ce.x * GROUP_ROWS + DKV_SUB * (u & 1);
     const int nvalid = (int)max((int64_t)0, min((int64_t)DKV_SUB, qrows - row0));
-    gather_seq_rows<DKV_SUB, ROW_CHUNKS>(q_dst, a.q + row0 * D_K, nvalid, wv, lane);
-    gather_seq_rows<DKV_SUB, DO_CHUNKS>(d_dst, a.dout + row0 * D_V, nvalid, wv, lane);
-    if (wv == 0) {
+    gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW>(q_dst, a.q + row0 * D_K, nvalid, wv, lane);
+    gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW>(d_dst, a.dout + row0 * D_V, nvalid, wv, lane);
+    if (wv == 5) {
       const uint64_t src = reinterpret_cast<uint64_t>(a.krmask + (int64_t)ce.x * a.rcap + ce.y) + 4u * lane;
       g2lds4(reinterpret_cast<const void*>(lane < 2 * T ? src : zero), m_dst);
-    } else if (wv == 1) {
+    } else if (wv == 6) {
       const uint64_t src = reinterpret_cast<uint64_t>(a.lse + row0 + lane);
       g2lds4(reinterpret_cast<const void*>((lane < DKV_SUB && row0 + lane < qrows) ? src : zero), l_dst);
-    } else if (wv == 2) {
+    } else if (wv == 7) {
       const uint64_t src = reinterpret_cast<uint64_t>(a.delta + row0 + lane);
       g2lds4(reinterpret_cast<const void*>((lane < DKV_SUB && row0 + lane < qrows) ? src : zero), e_dst);
     }
@@ -359,50 +362,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     for (int sl2 = 0; sl2 < T; ++sl2)
       touched |= (unsigned long long)sm[2 * sl2] | ((unsigned long long)sm[2 * sl2 + 1] << 32);
 
-    // S and dP for the sub-chunk's 32 query rows (M) against this wave's 16
-    // kv rows (N, the kf fragments): lane (g, r) holds query rows
-    // 16nt + 4g + i of kv row 16w + r.  Q / dout fragments run one k-step
-    // ahead of their MFMAs (the scheduling barriers keep the reads from
-    // sinking onto their uses).
-    float4_t st[2], dpt[2];
+    // S and dP for query rows 16 sqh .. +15 (M) against kv rows 16 skb .. +15
+    // (N): lane (g, r) holds query rows 16 sqh + 4g + i of kv row 16 skb + r.
+    // Q / dout fragments run KPF k-steps ahead of their MFMAs.
+    float4_t st = (float4_t){0.f, 0.f, 0.f, 0.f}, dpt = (float4_t){0.f, 0.f, 0.f, 0.f};
+    constexpr int KPF = 3;
+    short8_t qb[KPF + 1], db[KPF + 1];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      st[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
-      dpt[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    }
-    short8_t qc[2], qn[2], dc[2], dn[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      qc[nt] = ld_b_rs<DKV_SUB>(sq, nt * 16, 0, lane);
-      dc[nt] = ld_b_rs<DKV_SUB>(sd, nt * 16, 0, lane);
+    for (int d = 0; d < KPF; ++d) {
+      qb[d] = ld_b_rs<DKV_SUB>(sq, 16 * sqh, 32 * d, lane);
+      db[d] = ld_b_rs<DKV_SUB>(sd, 16 * sqh, 32 * d, lane);
     }
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      if (ks + 1 < 18) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          qn[nt] = ld_b_rs<DKV_SUB>(sq, nt * 16, 32 * (ks + 1), lane);
-          if (ks + 1 < 16) dn[nt] = ld_b_rs<DKV_SUB>(sd, nt * 16, 32 * (ks + 1), lane);
-        }
+      if (ks + KPF < 18) {
+        qb[(ks + KPF) % (KPF + 1)] = ld_b_rs<DKV_SUB>(sq, 16 * sqh, 32 * (ks + KPF), lane);
+        if (ks + KPF < 16) db[(ks + KPF) % (KPF + 1)] = ld_b_rs<DKV_SUB>(sd, 16 * sqh, 32 * (ks + KPF), lane);
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        st[nt] = mfma_bf16(qc[nt], kf[ks], st[nt]);
-        if (ks < 16) dpt[nt] = mfma_bf16(dc[nt], kf[ks], dpt[nt]);
-      }
+      st = mfma_bf16(qb[ks % (KPF + 1)], kf[ks], st);
+      if (ks < 16) dpt = mfma_bf16(db[ks % (KPF + 1)], kf[ks], dpt);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        qc[nt] = qn[nt];
-        dc[nt] = dn[nt];
-      }
     }
-    const int kvl = 16 * wave + r16;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int q0 = nt * 16 + 4 * g16;          // first of the lane's 4 query rows
-      const int slot = (DKV_SUB * half + q0) / H;  // one token for all 4 (H >= 4)
+    {
+      const int kvl = 16 * skb + r16;
+      const int q0 = 16 * sqh + 4 * g16;            // first of the lane's 4 query rows
+      const int slot = (DKV_SUB * half + q0) / H;   // one token for all 4 (H >= 4)
       const unsigned long long m =
           (unsigned long long)sm[2 * slot] | ((unsigned long long)sm[2 * slot + 1] << 32);
       const bool v = (m >> kvl) & 1ull;
@@ -411,8 +396,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
       float p[4], ds[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[i] = v ? fast_exp2(st[nt][i] * a.scale_log2 - l2[i] * LOG2E) : 0.f;
-        ds[i] = p[i] * (dpt[nt][i] - dl[i]) * a.scale;
+        p[i] = v ? fast_exp2(st[i] * a.scale_log2 - l2[i] * LOG2E) : 0.f;
+        ds[i] = p[i] * (dpt[i] - dl[i]) * a.scale;
       }
       uint2 pk, dk;
       pk.x = pack_bf2(p[0], p[1]);
@@ -424,22 +409,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    short8_t ad[4], ap[4];
+    // dK / dV for kv rows 32 drh .. +31, columns 144 dcq .. +143.
+    short8_t ad[2], ap[2];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      ad[rb] = ld16_lds(&sDST[(16 * rb + r16) * SP + 8 * g16]);
-      ap[rb] = ld16_lds(&sPT[(16 * rb + r16) * SP + 8 * g16]);
+    for (int rb = 0; rb < 2; ++rb) {
+      ad[rb] = ld16_lds(&sDST[(32 * drh + 16 * rb + r16) * SP + 8 * g16]);
+      ap[rb] = ld16_lds(&sPT[(32 * drh + 16 * rb + r16) * SP + 8 * g16]);
     }
 #pragma unroll
     for (int n = 0; n < 9; ++n) {
-      const int col = 144 * wave + 16 * n;
+      const int col = 144 * dcq + 16 * n;
       const short8_t bq = ld_bt_rs<DKV_SUB>(sq, 0, col, lane);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(ad[rb], bq, acc[rb][n]);
+      for (int rb = 0; rb < 2; ++rb) acc[rb][n] = mfma_bf16(ad[rb], bq, acc[rb][n]);
       if (col < D_V) {
         const short8_t bo = ld_bt_rs<DKV_SUB>(sd, 0, col, lane);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(ap[rb], bo, acc[rb][n]);
+        for (int rb = 0; rb < 2; ++rb) acc[rb][n] = mfma_bf16(ap[rb], bo, acc[rb][n]);
       }
     }
   };
@@ -450,14 +436,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     step(u, sQ[b], sD[b], sM[b], sL[b], sE[b], sQ[b ^ 1], sD[b ^ 1], sM[b ^ 1], sL[b ^ 1], sE[b ^ 1]);
   }
 
-  // Partial sum of this item: rows 16rb+4g16+i, columns 144*wave + 16n + r16.
-  float* dst = a.part + ((blk * a.maxsplit + split) * TILE_KV + 4 * g16) * D_K + 144 * wave + r16;
+  // Partial sum of this item: rows 32 drh + 16 rb + 4 g + i, columns
+  // 144 dcq + 16 n + r.
+  {
+    const int g16 = lane_id >> 4, r16 = lane_id & 15;
+    float* dst = a.part + ((blk * a.maxsplit + split) * TILE_KV + 32 * drh + 4 * g16) * D_K +
+                 144 * dcq + r16;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int n = 0; n < 9; ++n) dst[(16 * rb + i) * D_K + 16 * n] = acc[rb][n][i];
+        for (int n = 0; n < 9; ++n) dst[(16 * rb + i) * D_K + 16 * n] = acc[rb][n][i];
+  }
   if (tid == 0) a.ptouch[blk * a.maxsplit + split] = touched;
 }
 
@@ -641,7 +632,7 @@ hipError_t launch_dkv_schedule(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream) {
   if (a.NB == 0) return hipSuccess;
-  const dim3 grid((unsigned)(a.NB * a.maxsplit)), block(256);
+  const dim3 grid((unsigned)(a.NB * a.maxsplit)), block(DKV_NW * 64);
   switch (heads) {
     case 8: bwd_dkv_kernel<8><<<grid, block, 0, stream>>>(a); break;
     case 16: bwd_dkv_kernel<16><<<grid, block, 0, stream>>>(a); break;

@@ -321,6 +321,62 @@ __device__ __forceinline__ void gather_seq_rows(char* tile, const uint16_t* firs
   }
 }
 
+// gather_kv_rows for a workgroup of NW waves (NW >= 4, R / NW rows each):
+// wave wv copies rows R/NW * wv .. +R/NW-1 and, for wv < R/8, the tails of
+// rows 8 wv .. 8 wv + 7.
+template <int R, int CH, int NW>
+__device__ __forceinline__ void gather_kv_rows_nw(char* tile, const uint16_t* kv, int64_t s_kv,
+                                                  const int* rows, int count, int wv, int lane) {
+  constexpr int PER = R / NW;
+  static_assert(PER >= 1 && (PER & (PER - 1)) == 0, "rows per wave must be a power of two");
+  const uint32_t base = lds_offset(tile);
+  const int vrow = rows[PER * wv + (lane & (PER - 1))];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int r = PER * wv + i;
+    const int row = __builtin_amdgcn_readlane(vrow, i);
+    const bool ok = r < count && (uint32_t)row < (uint32_t)s_kv;
+    const uint16_t* src = (ok ? kv : g_zero_row) + (uint32_t)(ok ? row : 0) * (uint32_t)D_K;
+    g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), base + 1024u * (uint32_t)r);
+  }
+  if constexpr (CH == ROW_CHUNKS) {
+    if (wv < R / 8) {
+      const int r = 8 * wv + (lane >> 3);
+      const int row = rows[r];
+      const bool ok = r < count && (uint32_t)row < (uint32_t)s_kv;
+      const uint16_t* src = (ok ? kv + (uint64_t)(uint32_t)row * D_K : g_zero_row) + D_V +
+                            8 * ((lane & 7) ^ swz_hi(r));
+      g2lds16_u(src, base + (uint32_t)(R * 1024 + 1024 * wv));
+    }
+  }
+}
+
+// gather_seq_rows for a workgroup of NW waves: wave wv copies rows
+// R/NW * wv .. +R/NW-1 and, for wv < R/8, the tails of rows 8 wv .. 8 wv + 7.
+template <int R, int CH, int NW>
+__device__ __forceinline__ void gather_seq_rows_nw(char* tile, const uint16_t* first, int nvalid,
+                                                   int wv, int lane) {
+  constexpr int PER = R / NW;
+  constexpr int W = CH * 8;  // elements per row
+  const uint32_t base = lds_offset(tile);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int r = PER * wv + i;
+    const bool ok = r < nvalid;
+    const uint16_t* src = (ok ? first : g_zero_row) + (uint32_t)(ok ? r : 0) * (uint32_t)W;
+    g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), base + 1024u * (uint32_t)r);
+  }
+  if constexpr (CH == ROW_CHUNKS) {
+    if (wv < R / 8) {
+      const int r = 8 * wv + (lane >> 3);
+      const bool ok = r < nvalid;
+      const uint16_t* src = (ok ? first + (uint32_t)r * (uint32_t)W : g_zero_row) + D_V +
+                            8 * ((lane & 7) ^ swz_hi(r));
+      g2lds16_u(src, base + (uint32_t)(R * 1024 + 1024 * wv));
+    }
+  }
+}
+
 // Incremental form of the gathers: prepare once, then issue copy J (a
 // compile-time index) where it fits in the caller's instruction stream.
 // For a kv gather of R rows, wave wv issues R/4 row copies (J < R/4) and
