@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsmla.so"
 SMLA_OK = 0
 SMLA_DKV_ACCUMULATE = 1
 SMLA_DKV_ATOMIC = 2
+SMLA_PLAN_READY = 4
 
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_ALIGN",
                 4: "SMLA_ERR_WORKSPACE", 5: "SMLA_ERR_FLAGS", 6: "SMLA_ERR_HIP",
@@ -22,6 +23,9 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "smla_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, ctypes.c_float,
                                 _P, _P, _P, _SZ, _P]),
+    "smla_fwd_ex": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, ctypes.c_float,
+                                   _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
+    "smla_plan": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _SZ, _P]),
     "smla_fwd_workspace_size": (_SZ, [_I64, _I64, _I32, _I32]),
     "smla_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, ctypes.c_float,
                                 _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),

@@ -115,9 +115,10 @@ Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward) {
     p.off_ktab = o;    o = align256(o + (size_t)p.NB * p.G * 8);
     p.off_krmask = o;  o = align256(o + (size_t)p.G * p.rcap * 8);
     p.off_delta = o;   o = align256(o + (size_t)s_q * heads * 4);
-    // Split the per-block dkv reduction so that about 1024 workgroups run.
-    int64_t ms = (1024 + p.NB - 1) / p.NB;
-    p.maxsplit = (int)(ms < 1 ? 1 : (ms > 16 ? 16 : ms));
+    // Split the per-block dkv reduction so that about DKV_TARGET_ITEMS
+    // workgroups run (at most 64 splits per block).
+    int64_t ms = (DKV_TARGET_ITEMS + p.NB - 1) / p.NB;
+    p.maxsplit = (int)(ms < 1 ? 1 : (ms > 64 ? 64 : ms));
     p.off_clist = o;   o = align256(o + (size_t)p.NB * p.G * 8);
     p.off_nchunk = o;  o = align256(o + (size_t)p.NB * 4);
     p.off_ptouch = o;  o = align256(o + (size_t)p.NB * p.maxsplit * 8);
@@ -156,26 +157,9 @@ size_t smla_bwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t
   return make_plan(s_q, s_kv, heads, topk, true).bytes;
 }
 
-int smla_fwd(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,
-             int32_t heads, int32_t topk, float sm_scale, void* out, float* lse,
-             void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
-  int st = check_shape(s_q, s_kv, heads, topk);
-  if (st) return st;
-  if (!kv || (s_q > 0 && (!q || !indices || !out || !lse)))
-    return fail(SMLA_ERR_NULL, "null tensor pointer");
-  if (!aligned16(q) || !aligned16(kv) || !aligned16(indices) || !aligned16(out) || !aligned16(lse))
-    return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  const Plan p = make_plan(s_q, s_kv, heads, topk, false);
-  if (!workspace || workspace_bytes < p.bytes)
-    return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_fwd_workspace_size()");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(SMLA_ERR_ALIGN, "workspace must be 256-byte aligned");
-  if ((st = check_device())) return st;
-  if (s_q == 0) return SMLA_OK;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-
+// Fills the planner's arguments for a workspace laid out by make_plan.
+static PlanArgs plan_args(const Plan& p, const int32_t* indices, int64_t s_q, int64_t s_kv,
+                          int topk, char* ws, bool backward) {
   PlanArgs pa{};
   pa.idx = indices;
   pa.s_q = s_q;
@@ -190,11 +174,67 @@ int smla_fwd(const void* q, const void* kv, const int32_t* indices, int64_t s_q,
   pa.xtotal = reinterpret_cast<int*>(ws + p.off_xtotal);
   pa.qrow = reinterpret_cast<int32_t*>(ws + p.off_qrow);
   pa.qmask = reinterpret_cast<uint8_t*>(ws + p.off_qmask);
-  pa.ktab = nullptr;
-  if ((st = hip_status(timed("fill", s, [&] { return launch_fill_u32(pa.xtotal, 1, 0u, s); }), "fill"))) return st;
+  pa.ktab = backward ? reinterpret_cast<int2*>(ws + p.off_ktab) : nullptr;
+  pa.krmask = backward ? reinterpret_cast<unsigned long long*>(ws + p.off_krmask) : nullptr;
+  return pa;
+}
+
+// Clear, plan, order: the index plan of a workspace (backward layout when
+// `backward`, which adds the kv-block records).
+static int run_plan(const Plan& p, const PlanArgs& pa, int heads, bool backward, hipStream_t s) {
+  int st;
+  // xtotal (one 256-byte slot) and, in the backward layout, ktab are
+  // contiguous: one fill clears both.
+  const size_t clear_words = (256 + (backward ? (size_t)p.NB * p.G * 8 : 0)) / 4;
+  if ((st = hip_status(timed("fill", s, [&] { return launch_fill_u32(pa.xtotal, clear_words, 0u, s); }), "fill"))) return st;
+  if (pa.s_q == 0) return SMLA_OK;
   if ((st = hip_status(timed("plan", s, [&] { return launch_plan(pa, heads, s); }), "plan"))) return st;
-  int* gorder = reinterpret_cast<int*>(ws + p.off_gorder);
-  if ((st = hip_status(timed("order", s, [&] { return launch_order_groups(pa.qcount, p.G, gorder, s); }), "order"))) return st;
+  int* gorder = reinterpret_cast<int*>(reinterpret_cast<char*>(pa.qcount) - p.off_qcount + p.off_gorder);
+  return hip_status(timed("order", s, [&] { return launch_order_groups(pa.qcount, p.G, gorder, s); }), "order");
+}
+
+int smla_plan(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = check_shape(s_q, s_kv, heads, topk);
+  if (st) return st;
+  if (s_q > 0 && !indices) return fail(SMLA_ERR_NULL, "indices is null");
+  if (!aligned16(indices)) return fail(SMLA_ERR_ALIGN, "indices must be 16-byte aligned");
+  const Plan p = make_plan(s_q, s_kv, heads, topk, true);
+  if (!workspace || workspace_bytes < p.bytes)
+    return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_bwd_workspace_size()");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SMLA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if ((st = check_device())) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  return run_plan(p, plan_args(p, indices, s_q, s_kv, topk, ws, true), heads, true, s);
+}
+
+int smla_fwd_ex(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,
+                int32_t heads, int32_t topk, float sm_scale, void* out, float* lse, uint32_t flags,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = check_shape(s_q, s_kv, heads, topk);
+  if (st) return st;
+  if (flags & ~SMLA_PLAN_READY) return fail(SMLA_ERR_FLAGS, "unknown flag bits");
+  if (!kv || (s_q > 0 && (!q || !indices || !out || !lse)))
+    return fail(SMLA_ERR_NULL, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(indices) || !aligned16(out) || !aligned16(lse))
+    return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  // The forward fields of the workspace are a prefix of the backward layout,
+  // so a plan built by smla_plan serves here too.
+  const Plan p = make_plan(s_q, s_kv, heads, topk, false);
+  if (!workspace || workspace_bytes < p.bytes)
+    return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_fwd_workspace_size()");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SMLA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if ((st = check_device())) return st;
+  if (s_q == 0) return SMLA_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, ws, false);
+  if (!(flags & SMLA_PLAN_READY) && (st = run_plan(p, pa, heads, false, s))) return st;
 
   FwdArgs fa{};
   fa.q = static_cast<const uint16_t*>(q);
@@ -207,10 +247,17 @@ int smla_fwd(const void* q, const void* kv, const int32_t* indices, int64_t s_q,
   fa.qcount = pa.qcount;
   fa.qrow = pa.qrow;
   fa.qmask = pa.qmask;
-  fa.order = gorder;
+  fa.order = reinterpret_cast<int*>(ws + p.off_gorder);
   fa.out = static_cast<uint16_t*>(out);
   fa.lse = lse;
   return hip_status(timed("fwd", s, [&] { return launch_fwd(fa, heads, s); }), "fwd");
+}
+
+int smla_fwd(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,
+             int32_t heads, int32_t topk, float sm_scale, void* out, float* lse,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  return smla_fwd_ex(q, kv, indices, s_q, s_kv, heads, topk, sm_scale, out, lse, 0u, workspace,
+                     workspace_bytes, stream);
 }
 
 int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
@@ -223,7 +270,7 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   if (!kv || (s_q > 0 && (!q || !out || !dout || !indices || !lse || !dq)))
     return fail(SMLA_ERR_NULL, "null tensor pointer");
   if (!dkv && !dkv_f32) return fail(SMLA_ERR_NULL, "dkv and dkv_f32 are both null");
-  if (flags & ~(SMLA_DKV_ACCUMULATE | SMLA_DKV_ATOMIC))
+  if (flags & ~(SMLA_DKV_ACCUMULATE | SMLA_DKV_ATOMIC | SMLA_PLAN_READY))
     return fail(SMLA_ERR_FLAGS, "unknown flag bits");
   if ((flags & SMLA_DKV_ACCUMULATE) && !dkv_f32)
     return fail(SMLA_ERR_FLAGS, "SMLA_DKV_ACCUMULATE needs dkv_f32");
@@ -243,28 +290,9 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
-  PlanArgs pa{};
-  pa.idx = indices;
-  pa.s_q = s_q;
-  pa.s_kv = s_kv;
-  pa.topk = topk;
-  pa.G = p.G;
-  pa.NB = p.NB;
-  pa.qcap = p.qcap;
-  pa.rcap = p.rcap;
-  pa.qcount = reinterpret_cast<int*>(ws + p.off_qcount);
-  pa.xcount = reinterpret_cast<int*>(ws + p.off_xcount);
-  pa.xtotal = reinterpret_cast<int*>(ws + p.off_xtotal);
-  pa.qrow = reinterpret_cast<int32_t*>(ws + p.off_qrow);
-  pa.qmask = reinterpret_cast<uint8_t*>(ws + p.off_qmask);
-  pa.ktab = reinterpret_cast<int2*>(ws + p.off_ktab);
-  pa.krmask = reinterpret_cast<unsigned long long*>(ws + p.off_krmask);
-  // xtotal (one 256-byte slot) and ktab are contiguous: clear both at once.
-  const size_t clear_words = (256 + (size_t)p.NB * p.G * 8) / 4;
-  if ((st = hip_status(timed("fill", s, [&] { return launch_fill_u32(pa.xtotal, clear_words, 0u, s); }), "fill"))) return st;
-  if (s_q > 0 && (st = hip_status(timed("plan", s, [&] { return launch_plan(pa, heads, s); }), "plan"))) return st;
+  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, ws, true);
+  if (!(flags & SMLA_PLAN_READY) && (st = run_plan(p, pa, heads, true, s))) return st;
   int* gorder = reinterpret_cast<int*>(ws + p.off_gorder);
-  if (s_q > 0 && (st = hip_status(timed("order", s, [&] { return launch_order_groups(pa.qcount, p.G, gorder, s); }), "order"))) return st;
 
   BwdArgs ba{};
   ba.q = static_cast<const uint16_t*>(q);

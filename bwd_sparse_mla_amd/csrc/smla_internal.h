@@ -105,7 +105,14 @@ hipError_t launch_dkv_schedule(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream);
 hipError_t launch_dkv_finalize(const BwdArgs& a, int heads, hipStream_t stream);
 // dkv split schedule: chunks a split covers at least, and the split count.
-constexpr int DKV_MIN_CHUNKS = 8;
+#ifndef SMLA_DKV_MIN_CHUNKS
+#define SMLA_DKV_MIN_CHUNKS 8
+#endif
+#ifndef SMLA_DKV_TARGET_ITEMS
+#define SMLA_DKV_TARGET_ITEMS 512
+#endif
+constexpr int DKV_MIN_CHUNKS = SMLA_DKV_MIN_CHUNKS;
+constexpr int DKV_TARGET_ITEMS = SMLA_DKV_TARGET_ITEMS;   // dkv work items aimed for
 __host__ __device__ inline int dkv_nsplit(int nchunk, int maxsplit) {
   int n = (nchunk + DKV_MIN_CHUNKS - 1) / DKV_MIN_CHUNKS;
   return n < 1 ? 1 : (n > maxsplit ? maxsplit : n);

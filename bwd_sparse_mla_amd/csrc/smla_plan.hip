@@ -174,6 +174,53 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     __syncthreads();  // bm is cleared by the next window
   }
 
+  // Which occurrence of a repeated (token, row) pair the atomics above flag
+  // depends on the order they land in.  Make it canonical -- every occurrence
+  // but the first in slot order -- so the extra entries, and the summation
+  // order they imply, depend on the indices alone.  Only the first occurrence
+  // can be flagged wrongly; the wave that owns its flag word hands the flag to
+  // the one later occurrence the atomics left unflagged.  Flags of one pair
+  // change only in that wave, and a flag set meanwhile in a word another wave
+  // has already read belongs to a non-first occurrence, which needs no change.
+  {
+    int anyx = 0;
+    for (int w = tid; w < nxw; w += 256) anyx |= (xflag[w] != 0u);
+    if (__syncthreads_or(anyx)) {
+      const int wv = tid >> 6, lane = tid & 63;
+      for (int w = wv; w < nxw; w += 4) {
+        unsigned f = __builtin_amdgcn_readfirstlane(xflag[w]);
+        while (f) {
+          const int b = __ffs(f) - 1;
+          f &= f - 1;
+          const int s = 32 * w + b;
+          const int t = s / K, k = s - t * K;
+          const int32_t* row = ix + (int64_t)t * K;
+          const int v = __builtin_amdgcn_readfirstlane(row[k]);
+          bool earlier = false;
+          for (int i0 = 0; i0 < k && !earlier; i0 += 64) {
+            const int i = i0 + lane;
+            earlier = __ballot(i < k && row[i] == v) != 0ull;
+          }
+          if (earlier) continue;
+          int later = -1;
+          for (int i0 = k + 1; i0 < K && later < 0; i0 += 64) {
+            const int i = i0 + lane;
+            const int si = t * K + i;
+            const bool hit = i < K && row[i] == v && !((xflag[si >> 5] >> (si & 31)) & 1u);
+            const unsigned long long bal = __ballot(hit);
+            if (bal) later = i0 + __ffsll((long long)bal) - 1;
+          }
+          if (lane == 0 && later >= 0) {
+            const int sx = t * K + later;
+            atomicOr(&xflag[sx >> 5], 1u << (sx & 31));
+            atomicAnd(&xflag[w], ~(1u << b));
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
   // Repeated slots, in slot order: one extra union entry each.
   const int wpt = (nxw + 255) / 256;
   const int wb = min(nxw, tid * wpt), we = min(nxw, wb + wpt);

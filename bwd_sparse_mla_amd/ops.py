@@ -232,19 +232,29 @@ class SparseMLARunner:
             assert dout.shape == (s_q, h, D_V) and dout.dtype == torch.bfloat16
             assert dout.is_contiguous()
 
-    def fwd(self, q, kv, idx, sm_scale):
+    def plan(self, idx):
+        """Build the index plan once (smla_plan) into the backward workspace;
+        fwd / bwd with planned=True then reuse it (same indices)."""
         s_q, s_kv, h, k = self.shape
-        _lib.check(self.lib.smla_fwd(_ptr(q), _ptr(kv), _ptr(idx), s_q, s_kv, h, k,
-                                     float(sm_scale), _ptr(self.out), _ptr(self.lse),
-                                     ctypes.c_void_p(self._fws_addr), self._fb,
-                                     _stream(self.device)))
+        _lib.check(self.lib.smla_plan(_ptr(idx), s_q, s_kv, h, k,
+                                      ctypes.c_void_p(self._bws_addr), self._bb,
+                                      _stream(self.device)))
+
+    def fwd(self, q, kv, idx, sm_scale, planned: bool = False):
+        s_q, s_kv, h, k = self.shape
+        ws, wb = (self._bws_addr, self._bb) if planned else (self._fws_addr, self._fb)
+        _lib.check(self.lib.smla_fwd_ex(_ptr(q), _ptr(kv), _ptr(idx), s_q, s_kv, h, k,
+                                        float(sm_scale), _ptr(self.out), _ptr(self.lse),
+                                        _lib.SMLA_PLAN_READY if planned else 0, ctypes.c_void_p(ws), wb,
+                                        _stream(self.device)))
         return self.out, self.lse
 
-    def bwd(self, q, kv, dout, idx, sm_scale):
+    def bwd(self, q, kv, dout, idx, sm_scale, planned: bool = False):
         s_q, s_kv, h, k = self.shape
         _lib.check(self.lib.smla_bwd(_ptr(q), _ptr(kv), _ptr(self.out), _ptr(dout), _ptr(idx),
                                      _ptr(self.lse), s_q, s_kv, h, k, float(sm_scale),
-                                     _ptr(self.dq), _ptr(self.dkv), ctypes.c_void_p(0), 0,
+                                     _ptr(self.dq), _ptr(self.dkv), ctypes.c_void_p(0),
+                                     _lib.SMLA_PLAN_READY if planned else 0,
                                      ctypes.c_void_p(self._bws_addr), self._bb,
                                      _stream(self.device)))
         return self.dq, self.dkv

@@ -78,6 +78,22 @@ enum smla_status {
                                    are left untouched (bit for bit) */
 #define SMLA_DKV_ATOMIC 2u      /* accumulate dkv with fp32 atomics from the
                                    query-major pass (not bitwise reproducible) */
+#define SMLA_PLAN_READY 4u      /* smla_fwd_ex / smla_bwd: the workspace already
+                                   holds the index plan smla_plan built for the
+                                   same indices and sizes; skip planning */
+
+/* Index plan: which slots are valid (an index is a row iff it is not -1 and
+ * lies in [0, s_kv): miles PR #2079 digest, "fix GLM-5 sparse-MLA kernel -1
+ * index OOB and NaN gradients", 实现拆解 item 1), grouped for the kernels --
+ * per query group the union of its tokens' rows with token masks, per
+ * (64-row kv block, query group) the tokens' row masks, and the work orders.
+ * It depends only on indices and the sizes, so a training step can build it
+ * once and pass SMLA_PLAN_READY to smla_fwd_ex and smla_bwd with the same
+ * workspace.  workspace: at least smla_bwd_workspace_size(...) bytes,
+ * 256-byte aligned, owned by the caller, which must not change indices, the
+ * sizes or the workspace between this call and the calls that use the plan. */
+int smla_plan(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Forward.
  * in:  q, kv, indices, sm_scale (the softmax scale applied to q . k).
@@ -88,6 +104,13 @@ enum smla_status {
 int smla_fwd(const void* q, const void* kv, const int32_t* indices,
              int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk, float sm_scale,
              void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* smla_fwd with flags: 0 (= smla_fwd) or SMLA_PLAN_READY (the workspace
+ * holds smla_plan's plan for these indices and sizes; it is not rebuilt). */
+int smla_fwd_ex(const void* q, const void* kv, const int32_t* indices,
+                int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk, float sm_scale,
+                void* out, float* lse, uint32_t flags, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 size_t smla_fwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk);
 
@@ -101,7 +124,7 @@ size_t smla_fwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t
  *      dkv_f32 [s_kv, 576] fp32 (may be NULL; required with SMLA_DKV_ACCUMULATE).
  *      Rows of dkv that no valid slot selects are exact zeros (without
  *      SMLA_DKV_ACCUMULATE).  dkv and dkv_f32 must not both be NULL.
- * flags: 0, SMLA_DKV_ACCUMULATE and/or SMLA_DKV_ATOMIC.
+ * flags: 0, SMLA_DKV_ACCUMULATE, SMLA_DKV_ATOMIC and/or SMLA_PLAN_READY.
  * workspace: at least smla_bwd_workspace_size(...) bytes, 256-byte aligned. */
 int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
              const int32_t* indices, const float* lse,

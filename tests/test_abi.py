@@ -109,3 +109,18 @@ def test_no_cpu_fallback_in_product_package():
         if fn.endswith(".py"):
             text = open(os.path.join(pkg, fn)).read()
             assert "oracle" not in text.replace("never imports the oracle", ""), fn
+
+
+def test_plan_and_fwd_ex_argument_errors(lib):
+    P = ctypes.c_void_p
+    bws = lib.smla_bwd_workspace_size(16, 16, 8, 4, 0)
+    fws = lib.smla_fwd_workspace_size(16, 16, 8, 4)
+    assert bws > fws > 0
+    assert lib.smla_plan(P(FAKE), 16, 16, 12, 4, P(FAKE), bws, P(0)) == 2      # heads
+    assert lib.smla_plan(P(0), 16, 16, 8, 4, P(FAKE), bws, P(0)) == 1          # indices
+    assert lib.smla_plan(P(FAKE), 16, 16, 8, 4, P(FAKE), fws, P(0)) == 4       # needs the bwd size
+    assert lib.smla_plan(P(FAKE), 16, 16, 8, 4, P(FAKE + 16), bws, P(0)) == 3  # 256-byte alignment
+    args = (P(FAKE), P(FAKE), P(FAKE), 16, 16, 8, 4, 0.1, P(FAKE), P(FAKE))
+    assert lib.smla_fwd_ex(*args, 8, P(FAKE), fws, P(0)) == 5                  # unknown flag
+    assert lib.smla_fwd_ex(*args, 4, P(FAKE), 64, P(0)) == 4                   # workspace
+    assert call_bwd(lib, flags=16) == 5

@@ -1,6 +1,6 @@
 """Parity at the full sizes of the four large workloads, in the launch
-configuration bench.py times (SparseMLARunner: every buffer preallocated, one
-forward and one backward call).
+configuration bench.py times (SparseMLARunner: every buffer preallocated, the
+index plan built once, one forward and one backward call on it).
 
 The oracle cannot run on whole tensors of this size in a test, so it checks
 sampled outputs it computes one by one, and the rest is held to properties
@@ -39,8 +39,9 @@ def _run(w):
     q, kv, dout, idx = gpu_inputs(w)
     run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, q.device)
     run._check(q, kv, idx, dout)
-    run.fwd(q, kv, idx, w.sm_scale)
-    run.bwd(q, kv, dout, idx, w.sm_scale)
+    run.plan(idx)
+    run.fwd(q, kv, idx, w.sm_scale, planned=True)
+    run.bwd(q, kv, dout, idx, w.sm_scale, planned=True)
     torch.cuda.synchronize()
     return run
 

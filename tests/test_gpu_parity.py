@@ -247,3 +247,26 @@ def test_empty_query_batch():
     torch.cuda.synchronize()
     assert out.shape == (0, 8, 512) and dq.shape == (0, 8, 576)
     assert torch.count_nonzero(dkv).item() == 0
+
+
+def test_plan_once_path_is_bitwise_identical():
+    """smla_plan + SMLA_PLAN_READY (the plan built once per step, as the
+    benchmark runs it) gives exactly the outputs of fwd / bwd planning alone."""
+    import torch
+
+    import bwd_sparse_mla_amd as smla
+    for w in (synth.custom(S=70, H=16, K=96, S_kv=300, seed=11, dup_frac=0.1),
+              synth.tiny()):
+        print(f"[parity] plan-once {w.name}", flush=True)
+        q, kv, dout, idx = gpu_inputs(w)
+        a = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, q.device)
+        a.fwd(q, kv, idx, w.sm_scale)
+        a.bwd(q, kv, dout, idx, w.sm_scale)
+        b = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, q.device)
+        b.plan(idx)
+        b.fwd(q, kv, idx, w.sm_scale, planned=True)
+        b.bwd(q, kv, dout, idx, w.sm_scale, planned=True)
+        torch.cuda.synchronize()
+        bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+        for name in ("out", "lse", "dq", "dkv"):
+            assert torch.equal(bits(getattr(a, name)), bits(getattr(b, name))), name
