@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
   constexpr int SDS = DQ_TILE + 8;  // dS row stride (bf16): 80 bytes, conflict-free reads
   __shared__ __attribute__((aligned(16))) char sK[2][KV32_TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char sDO[GROUP_ROWS * DO_STRIDE];
+  __shared__ __attribute__((aligned(16))) char sDO[GROUP_ROWS * D_V * 2];   // swizzled 64-row tile
   __shared__ __attribute__((aligned(16))) unsigned short sdS[GROUP_ROWS * SDS];
   __shared__ __attribute__((aligned(16))) unsigned char sMask[2][256];   // token masks (copied as words)
   __shared__ __attribute__((aligned(16))) int sRow[2][64];   // kv row indices of a tile's entries
@@ -62,20 +62,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   const uint8_t* emask = a.qmask + grp * a.qcap;
   const int ntiles = (n_ent + DQ_TILE - 1) / DQ_TILE;
 
-  // dout rows of the group into LDS (64 rows x 65 chunks = 65 copies).
-  {
-    const uint64_t zero = reinterpret_cast<uint64_t>(zero_row());
-#pragma unroll 1
-    for (int i = wv; i < DO_STRIDE_CHUNKS; i += 4) {
-      const int p = i * 64 + lane;
-      const int row = p / DO_STRIDE_CHUNKS, cc = p - row * DO_STRIDE_CHUNKS;
-      const int64_t tok = t0 + row / H;
-      const uint64_t src =
-          reinterpret_cast<uint64_t>(a.dout + (tok * H + row % H) * D_V + 8 * cc);
-      g2lds16(reinterpret_cast<const void*>((cc < DO_CHUNKS && tok < a.s_q) ? src : zero),
-              sDO + i * 1024);
-    }
-  }
+  // dout rows of the group (contiguous: token-major, then head) into a
+  // swizzled 64-row tile, 16 row copies per wave; rows past the sequence end
+  // read the zero row.
+  gather_seq_rows<GROUP_ROWS, DO_CHUNKS>(sDO, a.dout + t0 * H * D_V,
+                                         (int)min<int64_t>(GROUP_ROWS, (a.s_q - t0) * H), wv, lane);
   // delta = rowsum(dout * out) for the group's 64 rows (4 threads per row).
   {
     const int row = tid >> 2, part = tid & 3;
@@ -137,7 +128,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     gather_kv_rows<DQ_TILE, ROW_CHUNKS>(kbuf, a.kv, a.s_kv, rows_t, count, wv, lane);
   };
 
-  const char* drow = sDO + (16 * wave + r16) * DO_STRIDE + 16 * g16;  // A fragments of dout
   auto step = [&](int tile, const char* kt, const unsigned char* mkb, char* knext,
                   unsigned char* mnext, const int* rnext, int* rcur) __attribute__((always_inline)) {
     wait_vmcnt0();
@@ -169,13 +159,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     short8_t kc[2], kn[2], dc, dn;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) kc[nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 0, lane);
-    dc = ld16_lds(drow);
+    dc = ld_b_rs<GROUP_ROWS>(sDO, 16 * wave, 0, lane);   // A fragments of dout
     static_for<18>([&](auto KS) __attribute__((always_inline)) {
       constexpr int ks = decltype(KS)::value;
       if constexpr (ks + 1 < 18) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) kn[nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * (ks + 1), lane);
-        if constexpr (ks + 1 < 16) dn = ld16_lds(drow + 64 * (ks + 1));
+        if constexpr (ks + 1 < 16) dn = ld_b_rs<GROUP_ROWS>(sDO, 16 * wave, 32 * (ks + 1), lane);
       }
       if constexpr (ks % 2 == 0) kv_gather_copy<DQ_TILE, ks / 2>(gnext, wv, lane);
       __builtin_amdgcn_sched_barrier(0);
@@ -324,17 +314,16 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
   unsigned long long touched = 0ull;
 
   const uint64_t zero = reinterpret_cast<uint64_t>(zero_row());
-  // Copies of sub-chunk u into one buffer set: Q and dout rows as swizzled
-  // 32-row tiles (36 + 32 copies, 8-9 per wave), then the token masks, lse
-  // and delta of the 32 rows (one copy each, waves 5, 6, 7).
-  auto issue = [&](int u, char* q_dst, char* d_dst, unsigned* m_dst, float* l_dst, float* e_dst) __attribute__((always_inline)) {
-    const int2 ce = a.clist[blk * a.G + c_lo + (u >> 1)];  // (group, record start)
-    int lane = lane_id;
-    asm volatile("" : "+v"(lane));   // offsets recomputed per sub-chunk, not kept live
-    const int64_t row0 = (int64_t)ce.x * GROUP_ROWS + DKV_SUB * (u & 1);
-    const int nvalid = (int)max((int64_t)0, min((int64_t)DKV_SUB, qrows - row0));
-    gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW>(q_dst, a.q + row0 * D_K, nvalid, wv, lane);
-    gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW>(d_dst, a.dout + row0 * D_V, nvalid, wv, lane);
+  // Sub-chunk u covers query rows 32 (u & 1) .. +31 of chunk c_lo + u / 2 (a
+  // query group); its buffers hold those rows of Q and dout as swizzled
+  // 32-row tiles, the group's token masks for the block, and the rows' lse and
+  // delta.  Every step first issues the copies of sub-chunk u+1 (4 Q rows,
+  // one Q tail copy for waves 0-3, 4 dout rows and, for waves 5-7, the masks /
+  // lse / delta) into the other buffer set.
+  const int2* clist = a.clist + blk * a.G + c_lo;
+  int2 ce_cur = clist[0];                                  // chunk of the current sub-chunk
+  int2 ce_nxt = clist[min(1, max(0, nsub / 2 - 1))];       // the chunk after it
+  auto small_copy = [&](int2 ce, int64_t row0, unsigned* m_dst, float* l_dst, float* e_dst, int lane) __attribute__((always_inline)) {
     if (wv == 5) {
       const uint64_t src = reinterpret_cast<uint64_t>(a.krmask + (int64_t)ce.x * a.rcap + ce.y) + 4u * lane;
       g2lds4(reinterpret_cast<const void*>(lane < 2 * T ? src : zero), m_dst);
@@ -346,12 +335,26 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
       g2lds4(reinterpret_cast<const void*>((lane < DKV_SUB && row0 + lane < qrows) ? src : zero), e_dst);
     }
   };
+  auto rows_of = [&](int2 ce, int u, int64_t& row0, int& nvalid) __attribute__((always_inline)) {
+    row0 = (int64_t)ce.x * GROUP_ROWS + DKV_SUB * (u & 1);
+    nvalid = (int)max((int64_t)0, min((int64_t)DKV_SUB, qrows - row0));
+  };
 
   auto step = [&](int u, const char* sq, const char* sd, const unsigned* sm, const float* sl,
                   const float* se, char* nq, char* nd, unsigned* nm, float* nl, float* ne) __attribute__((always_inline)) {
     wait_vmcnt0();
     __syncthreads();
-    if (u + 1 < nsub) issue(u + 1, nq, nd, nm, nl, ne);
+    if (u + 1 < nsub) {   // copies of sub-chunk u+1 into the other buffer set
+      int lane = lane_id;
+      asm volatile("" : "+v"(lane));   // offsets recomputed per sub-chunk, not kept live
+      const int2 cen = (u & 1) ? ce_nxt : ce_cur;
+      int64_t nrow0;
+      int nvalid;
+      rows_of(cen, u + 1, nrow0, nvalid);
+      gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW>(nq, a.q + nrow0 * D_K, nvalid, wv, lane);
+      gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW>(nd, a.dout + nrow0 * D_V, nvalid, wv, lane);
+      small_copy(cen, nrow0, nm, nl, ne, lane);
+    }
     int lane = lane_id;
     asm volatile("" : "+v"(lane));
     const int g16 = lane >> 4, r16 = lane & 15;
@@ -365,7 +368,14 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
     // S and dP for query rows 16 sqh .. +15 (M) against kv rows 16 skb .. +15
     // (N): lane (g, r) holds query rows 16 sqh + 4g + i of kv row 16 skb + r.
     // Q / dout fragments run KPF k-steps ahead of their MFMAs.
-    float4_t st = (float4_t){0.f, 0.f, 0.f, 0.f}, dpt = (float4_t){0.f, 0.f, 0.f, 0.f};
+    // Even and odd k-steps accumulate separately (four independent MFMA
+    // chains of depth 9 instead of two of depth 18) and are added at the end.
+    float4_t st2[2], dpt2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      st2[e] = (float4_t){0.f, 0.f, 0.f, 0.f};
+      dpt2[e] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    }
     constexpr int KPF = 3;
     short8_t qb[KPF + 1], db[KPF + 1];
 #pragma unroll
@@ -380,10 +390,11 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
         if (ks + KPF < 16) db[(ks + KPF) % (KPF + 1)] = ld_b_rs<DKV_SUB>(sd, 16 * sqh, 32 * (ks + KPF), lane);
       }
       __builtin_amdgcn_sched_barrier(0);
-      st = mfma_bf16(qb[ks % (KPF + 1)], kf[ks], st);
-      if (ks < 16) dpt = mfma_bf16(db[ks % (KPF + 1)], kf[ks], dpt);
+      st2[ks & 1] = mfma_bf16(qb[ks % (KPF + 1)], kf[ks], st2[ks & 1]);
+      if (ks < 16) dpt2[ks & 1] = mfma_bf16(db[ks % (KPF + 1)], kf[ks], dpt2[ks & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    const float4_t st = st2[0] + st2[1], dpt = dpt2[0] + dpt2[1];
     {
       const int kvl = 16 * skb + r16;
       const int q0 = 16 * sqh + 4 * g16;            // first of the lane's 4 query rows
@@ -409,28 +420,51 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // dK / dV for kv rows 32 drh .. +31, columns 144 dcq .. +143.
+    // dK / dV for kv rows 32 drh .. +31, columns 144 dcq .. +143; the
+    // transposed Q / dout fragments of column block n+1 are read before the
+    // MFMAs of block n.
     short8_t ad[2], ap[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       ad[rb] = ld16_lds(&sDST[(32 * drh + 16 * rb + r16) * SP + 8 * g16]);
       ap[rb] = ld16_lds(&sPT[(32 * drh + 16 * rb + r16) * SP + 8 * g16]);
     }
+    const int col0 = 144 * dcq;
+    short8_t bq = ld_bt_rs<DKV_SUB>(sq, 0, col0, lane);
+    short8_t bo = ld_bt_rs_lo<DKV_SUB>(sd, 0, col0, lane);   // col0 <= 432 < 512
 #pragma unroll
     for (int n = 0; n < 9; ++n) {
-      const int col = 144 * dcq + 16 * n;
-      const short8_t bq = ld_bt_rs<DKV_SUB>(sq, 0, col, lane);
+      const int col = col0 + 16 * n;
+      short8_t bqn = bq, bon = bo;
+      if (n + 1 < 9) {
+        bqn = ld_bt_rs<DKV_SUB>(sq, 0, col + 16, lane);
+        if (col + 16 < D_V) bon = ld_bt_rs_lo<DKV_SUB>(sd, 0, col + 16, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) acc[rb][n] = mfma_bf16(ad[rb], bq, acc[rb][n]);
       if (col < D_V) {
-        const short8_t bo = ld_bt_rs<DKV_SUB>(sd, 0, col, lane);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) acc[rb][n] = mfma_bf16(ap[rb], bo, acc[rb][n]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      bq = bqn;
+      bo = bon;
+    }
+    if (u & 1) {   // the next sub-chunk starts chunk u/2 + 1: load the one after it
+      ce_cur = ce_nxt;
+      if ((u >> 1) + 2 < nsub / 2) ce_nxt = clist[(u >> 1) + 2];
     }
   };
 
-  if (nsub > 0) issue(0, sQ[0], sD[0], sM[0], sL[0], sE[0]);
+  if (nsub > 0) {
+    int64_t row0;
+    int nvalid;
+    rows_of(ce_cur, 0, row0, nvalid);
+    gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW>(sQ[0], a.q + row0 * D_K, nvalid, wv, lane_id);
+    gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW>(sD[0], a.dout + row0 * D_V, nvalid, wv, lane_id);
+    small_copy(ce_cur, row0, sM[0], sL[0], sE[0], lane_id);
+  }
   for (int u = 0; u < nsub; ++u) {
     const int b = u & 1;
     step(u, sQ[b], sD[b], sM[b], sL[b], sE[b], sQ[b ^ 1], sD[b ^ 1], sM[b ^ 1], sL[b ^ 1], sE[b ^ 1]);
