@@ -37,7 +37,8 @@ namespace {
 // Query group of T = 64/H tokens (64 rows), union tiles of 32 kv rows,
 // double buffered.  dout of the group's rows lives in LDS (it is the A operand
 // of dP), Q in registers; per tile each wave computes scores and dP for its 16
-// rows, then dq += dS . K for all 64 rows and its 144 output columns.
+// rows, then dq += dS . K for all 64 rows and its 144 output columns (128
+// main columns and 16 of the 64 tail columns).
 constexpr int DQ_TILE = 32;
 
 template <int H>
@@ -198,9 +199,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     short8_t dsa[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) dsa[rb] = ld16_lds(&sdS[(16 * rb + r16) * SDS + 8 * g16]);
+    // Column blocks n < 8: 128 w + 16 n; block 8: tail columns 512 + 16 w.
 #pragma unroll
     for (int n = 0; n < 9; ++n) {
-      const short8_t b = ld_bt_rs<DQ_TILE>(kt, 0, 144 * wave + 16 * n, lane);
+      const short8_t b = n < 8 ? ld_bt_rs_lo<DQ_TILE>(kt, 0, 128 * wave + 16 * n, lane)
+                               : ld_bt_rs_hi<DQ_TILE>(kt, 0, D_V + 16 * wave, lane);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(dsa[rb], b, acc[rb][n]);
     }
@@ -230,8 +233,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     for (int n = 0; n < 9; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        so[(16 * (rb & 1) + 4 * g16 + i) * D_K + 144 * wave + 16 * n + r16] =
-            f2bf(acc[rb][n][i] * a.scale);
+        so[(16 * (rb & 1) + 4 * g16 + i) * D_K + (n < 8 ? 128 * wave + 16 * n : D_V + 16 * wave) +
+           r16] = f2bf(acc[rb][n][i] * a.scale);
   }
   __syncthreads();
   for (int p = tid; p < GROUP_ROWS * ROW_CHUNKS; p += 256) {
@@ -292,7 +295,8 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
   // for dP) against query rows 16 (w >> 2) .. +15 of the sub-chunk.
   const int skb = wv & 3, sqh = wv >> 2;
   // dK / dV: wave w accumulates kv rows 32 (w & 1) .. +31 (two 16-row
-  // blocks) x columns 144 (w >> 1) .. +143.
+  // blocks) x 9 column blocks of 16: 128 (w >> 1) .. +127 and tail columns
+  // 512 + 16 (w >> 1) .. +15.
   const int drh = wv & 1, dcq = wv >> 1;
   short8_t kf[18];
   {
@@ -420,30 +424,32 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // dK / dV for kv rows 32 drh .. +31, columns 144 dcq .. +143; the
-    // transposed Q / dout fragments of column block n+1 are read before the
-    // MFMAs of block n.
+    // dK / dV for kv rows 32 drh .. +31 and the wave's 9 column blocks:
+    // blocks n < 8 are columns 128 dcq + 16 n (dK and dV), block 8 is tail
+    // columns 512 + 16 dcq (dK only).  The transposed Q / dout fragments of
+    // block n+1 are read before the MFMAs of block n.
     short8_t ad[2], ap[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       ad[rb] = ld16_lds(&sDST[(32 * drh + 16 * rb + r16) * SP + 8 * g16]);
       ap[rb] = ld16_lds(&sPT[(32 * drh + 16 * rb + r16) * SP + 8 * g16]);
     }
-    const int col0 = 144 * dcq;
-    short8_t bq = ld_bt_rs<DKV_SUB>(sq, 0, col0, lane);
-    short8_t bo = ld_bt_rs_lo<DKV_SUB>(sd, 0, col0, lane);   // col0 <= 432 < 512
+    const int col0 = 128 * dcq;
+    short8_t bq = ld_bt_rs_lo<DKV_SUB>(sq, 0, col0, lane);
+    short8_t bo = ld_bt_rs_lo<DKV_SUB>(sd, 0, col0, lane);
 #pragma unroll
     for (int n = 0; n < 9; ++n) {
-      const int col = col0 + 16 * n;
       short8_t bqn = bq, bon = bo;
-      if (n + 1 < 9) {
-        bqn = ld_bt_rs<DKV_SUB>(sq, 0, col + 16, lane);
-        if (col + 16 < D_V) bon = ld_bt_rs_lo<DKV_SUB>(sd, 0, col + 16, lane);
+      if (n + 1 < 8) {
+        bqn = ld_bt_rs_lo<DKV_SUB>(sq, 0, col0 + 16 * (n + 1), lane);
+        bon = ld_bt_rs_lo<DKV_SUB>(sd, 0, col0 + 16 * (n + 1), lane);
+      } else if (n + 1 == 8) {
+        bqn = ld_bt_rs_hi<DKV_SUB>(sq, 0, D_V + 16 * dcq, lane);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) acc[rb][n] = mfma_bf16(ad[rb], bq, acc[rb][n]);
-      if (col < D_V) {
+      if (n < 8) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) acc[rb][n] = mfma_bf16(ap[rb], bo, acc[rb][n]);
       }
@@ -471,17 +477,17 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
   }
 
   // Partial sum of this item: rows 32 drh + 16 rb + 4 g + i, columns
-  // 144 dcq + 16 n + r.
+  // 128 dcq + 16 n + r (n < 8) and 512 + 16 dcq + r (n = 8).
   {
     const int g16 = lane_id >> 4, r16 = lane_id & 15;
-    float* dst = a.part + ((blk * a.maxsplit + split) * TILE_KV + 32 * drh + 4 * g16) * D_K +
-                 144 * dcq + r16;
+    float* dst = a.part + ((blk * a.maxsplit + split) * TILE_KV + 32 * drh + 4 * g16) * D_K + r16;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int n = 0; n < 9; ++n) dst[(16 * rb + i) * D_K + 16 * n] = acc[rb][n][i];
+        for (int n = 0; n < 9; ++n)
+          dst[(16 * rb + i) * D_K + (n < 8 ? 128 * dcq + 16 * n : D_V + 16 * dcq)] = acc[rb][n][i];
   }
   if (tid == 0) a.ptouch[blk * a.maxsplit + split] = touched;
 }

@@ -137,6 +137,21 @@ __device__ __forceinline__ short8_t ld_bt_rs_lo(const char* tile, int k0, int n0
   return v;
 }
 
+// ld_bt_rs for columns 512..575 only (n0 >= 512): tail addressing.
+template <int R>
+__device__ __forceinline__ short8_t ld_bt_rs_hi(const char* tile, int k0, int n0, int lane) {
+  const int g = (lane >> 4) & 3, L = lane & 15;
+  const int row = k0 + 8 * g + (L >> 2);
+  const int ct = ((n0 - D_V) >> 3) + ((L >> 1) & 1);   // tail chunk, 0..7
+  const char* p = tile + R * 1024 + (L & 1) * 8;
+  short4_t lo = ld_tr16(p + row * 128 + 16 * (ct ^ swz_hi(row)));
+  short4_t hi = ld_tr16(p + (row + 4) * 128 + 16 * (ct ^ swz_hi(row + 4)));
+  short8_t v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return v;
+}
+
 // Asynchronous global -> LDS copies (global_load_lds): lane i writes
 // lds_base + size*i; lds_base must be wave-uniform.  They are issued through
 // inline asm on purpose: the compiler then inserts no vmcnt wait for them
