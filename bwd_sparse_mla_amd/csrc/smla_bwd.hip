@@ -68,34 +68,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   // read the zero row.
   gather_seq_rows<GROUP_ROWS, DO_CHUNKS>(sDO, a.dout + t0 * H * D_V,
                                          (int)min<int64_t>(GROUP_ROWS, (a.s_q - t0) * H), wv, lane);
-  // delta = rowsum(dout * out) for the group's 64 rows (4 threads per row).
-  {
-    const int row = tid >> 2, part = tid & 3;
-    const int64_t tok = t0 + row / H;
-    float d = 0.f;
-    if (tok < a.s_q) {
-      const int64_t o = (tok * H + row % H) * D_V + 128 * part;
-#pragma unroll 4
-      for (int c = 0; c < 16; ++c) {
-        const short8_t x = ld16_global(a.dout + o + 8 * c);
-        const short8_t y = ld16_global(a.out + o + 8 * c);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) d += bf2f((unsigned short)x[j]) * bf2f((unsigned short)y[j]);
-      }
-    }
-    d += __shfl_xor(d, 1);
-    d += __shfl_xor(d, 2);
-    if (part == 0) {
-      sDelta[row] = d;
-      float l2 = 0.f;
-      if (tok < a.s_q) {
-        a.delta[tok * H + row % H] = d;
-        l2 = a.lse[tok * H + row % H] * LOG2E;
-      }
-      sLse2[row] = l2;
-    }
+  // Row indices and masks of tile 0 and the row indices of tile 1, in the
+  // same round trip.
+  if (ntiles > 0) {
+    copy_union_entries(sRow[0], sMask[0], erow, emask, 0, n_ent, DQ_TILE, wv, 0, 1, lane);
+    if (ntiles > 1) copy_union_entries(sRow[1], nullptr, erow, emask, DQ_TILE, n_ent, DQ_TILE, wv, 2, 2, lane);
   }
-
   short8_t qf[18];
   {
     const int rr = 16 * wave + r16;
@@ -107,6 +85,38 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     } else {
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) qf[ks] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  // delta = rowsum(dout * out) for the group's 64 rows: 4 threads per row,
+  // thread p of a row takes chunks p, p+4, ... (four threads read 64
+  // contiguous bytes per load); all 32 loads are issued before the sums.
+  {
+    const int row = tid >> 2, part = tid & 3;
+    const int64_t tok = t0 + row / H;
+    float d = 0.f;
+    if (tok < a.s_q) {
+      const int64_t o = (tok * H + row % H) * D_V + 8 * part;
+      short8_t x[16], y[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        x[c] = ld16_global(a.dout + o + 32 * c);
+        y[c] = ld16_global(a.out + o + 32 * c);
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d += bf2f((unsigned short)x[c][j]) * bf2f((unsigned short)y[c][j]);
+    }
+    d += __shfl_xor(d, 1);
+    d += __shfl_xor(d, 2);
+    if (part == 0) {
+      sDelta[row] = d;
+      float l2 = 0.f;
+      if (tok < a.s_q) {
+        a.delta[tok * H + row % H] = d;
+        l2 = a.lse[tok * H + row % H] * LOG2E;
+      }
+      sLse2[row] = l2;
     }
   }
   wait_vmcnt0();
@@ -209,13 +219,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  if (ntiles > 0) {
-    copy_union_entries(sRow[0], sMask[0], erow, emask, 0, n_ent, DQ_TILE, wv, 0, 1, lane);
-    if (ntiles > 1) copy_union_entries(sRow[1], nullptr, erow, emask, DQ_TILE, n_ent, DQ_TILE, wv, 2, 2, lane);
-    wait_vmcnt0();
-    __syncthreads();
-    gather(sK[0], sRow[0], min(DQ_TILE, n_ent));
-  }
+  if (ntiles > 0) gather(sK[0], sRow[0], min(DQ_TILE, n_ent));   // indices landed before the barrier above
   for (int tile = 0; tile < ntiles; ++tile) {
     const int b = tile & 1;
     step(tile, sK[b], sMask[b], sK[b ^ 1], sMask[b ^ 1], sRow[b ^ 1], sRow[b]);
