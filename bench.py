@@ -212,8 +212,7 @@ def main():
     kernels = {}
     roofline = None
     if timing:
-        for name in ("fill", "plan", "order", "fwd", "bwd_dq", "dkv_schedule", "bwd_dkv",
-                     "dkv_finalize"):
+        for name in ("plan", "order", "fwd", "bwd_dq", "dkv_schedule", "bwd_dkv", "dkv_finalize"):
             n, tot = smla.timing_read(name)
             if n:
                 kernels[name] = {"launches": n, "avg_ms": tot / n}

@@ -109,7 +109,6 @@ Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward) {
   p.off_qrow = o;    o = align256(o + (size_t)p.G * p.qcap * 4);
   p.off_qmask = o;   o = align256(o + (size_t)p.G * p.qcap);
   p.off_gorder = o;  o = align256(o + (size_t)p.G * 4);
-  // xtotal sits directly before ktab so one fill clears both.
   p.off_xtotal = o;  o += 256;
   if (backward) {
     p.off_ktab = o;    o = align256(o + (size_t)p.NB * p.G * 8);
@@ -179,18 +178,17 @@ static PlanArgs plan_args(const Plan& p, const int32_t* indices, int64_t s_q, in
   return pa;
 }
 
-// Clear, plan, order: the index plan of a workspace (backward layout when
-// `backward`, which adds the kv-block records).
+// Plan and order: the index plan of a workspace (backward layout when
+// `backward`, which adds the kv-block records).  Nothing needs clearing
+// first: the planner writes every entry of its structures, the order kernel
+// the extra-entry total.
 static int run_plan(const Plan& p, const PlanArgs& pa, int heads, bool backward, hipStream_t s) {
   int st;
-  // xtotal (one 256-byte slot) and, in the backward layout, ktab are
-  // contiguous: one fill clears both.
-  const size_t clear_words = (256 + (backward ? (size_t)p.NB * p.G * 8 : 0)) / 4;
-  if ((st = hip_status(timed("fill", s, [&] { return launch_fill_u32(pa.xtotal, clear_words, 0u, s); }), "fill"))) return st;
-  if (pa.s_q == 0) return SMLA_OK;
+  (void)backward;
+  if (pa.s_q == 0) return hip_status(launch_fill_u32(pa.xtotal, 1, 0u, s), "fill");
   if ((st = hip_status(timed("plan", s, [&] { return launch_plan(pa, heads, s); }), "plan"))) return st;
   int* gorder = reinterpret_cast<int*>(reinterpret_cast<char*>(pa.qcount) - p.off_qcount + p.off_gorder);
-  return hip_status(timed("order", s, [&] { return launch_order_groups(pa.qcount, p.G, gorder, s); }), "order");
+  return hip_status(timed("order", s, [&] { return launch_order_groups(pa.qcount, pa.xcount, p.G, gorder, pa.xtotal, s); }), "order");
 }
 
 int smla_plan(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,

@@ -43,7 +43,7 @@ struct PlanArgs {
   int64_t G, NB, qcap, rcap;
   int* qcount;        // [G]   union entries (main + extra) per group
   int* xcount;        // [G]   extra entries (repeated slots) per group
-  int* xtotal;        // [1]   sum of xcount
+  int* xtotal;        // [1]   sum of xcount (written by the order kernel)
   int32_t* qrow;      // [G, qcap] kv row of each union entry
   uint8_t* qmask;     // [G, qcap] mask of the group's tokens that select it
   int2* ktab;         // [NB, G] (record start within the group, T) or (0, 0); may be null
@@ -99,7 +99,8 @@ hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream);
 // Work order of the query groups: decreasing union size (largest first).
-hipError_t launch_order_groups(const int* qcount, int64_t G, int* order, hipStream_t stream);
+hipError_t launch_order_groups(const int* qcount, const int* xcount, int64_t G, int* order, int* xtotal,
+                               hipStream_t stream);
 // dkv pass: schedule (chunk lists and work order), main kernel, finalize.
 hipError_t launch_dkv_schedule(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream);

@@ -93,6 +93,16 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   int32_t* qrow = a.qrow + g * a.qcap;
   uint8_t* qmask = a.qmask + g * a.qcap;
   int qbase = 0, rbase = 0;
+  if (a.ktab) {
+    // This group's column of the [block, group] table is written whole (no
+    // clearing pass before the planner): blocks the windows below do not
+    // cover get (0, 0) here, the windows write every block they cover.
+    const int64_t cover_lo = hi >= 0 ? (int64_t)(lo & ~63) >> 6 : a.NB;
+    const int64_t cover_hi =
+        hi >= 0 ? ((int64_t)(lo & ~63) + ((int64_t)(hi - (lo & ~63)) / WIN_BITS + 1) * WIN_BITS) >> 6 : a.NB;
+    for (int64_t b = tid; b < a.NB; b += 256)
+      if (b < cover_lo || b >= cover_hi) a.ktab[b * a.G + g] = make_int2(0, 0);
+  }
   // Windows start on a 64-row block boundary so kv blocks never straddle two.
   for (int w0 = (hi >= 0 ? (lo & ~63) : 1); w0 <= hi; w0 += WIN_BITS) {
     for (int i = tid; i < T * WIN_WORDS; i += 256) (&bm[0][0])[i] = 0u;
@@ -162,9 +172,9 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
       }
       int rtotal;
       const int rpos = rbase + block_exclusive_scan256(any ? T : 0, scratch, &rtotal);
+      const int64_t b = (int64_t)(w0 >> 6) + tid;   // a set bit is a row < s_kv, so any => b < NB
+      if (b < a.NB) a.ktab[b * a.G + g] = any ? make_int2(rpos, T) : make_int2(0, 0);
       if (any) {
-        const int64_t b = (int64_t)(w0 >> 6) + tid;  // < NB: a set bit is a row < s_kv
-        a.ktab[b * a.G + g] = make_int2(rpos, T);
         const int64_t r = g * a.rcap + rpos;
 #pragma unroll
         for (int t = 0; t < T; ++t) a.krmask[r + t] = mk[t];
@@ -243,7 +253,6 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   if (tid == 0) {
     a.qcount[g] = qbase + xtot;
     a.xcount[g] = xtot;
-    if (xtot) atomicAdd(a.xtotal, xtot);
   }
   // Zero the masks of the last tile's unused entries (up to the next multiple
   // of 64; qcap is a multiple of 64): the compute kernels copy masks in words.
@@ -251,8 +260,18 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   if (tid < 64 && n_all + tid < ((n_all + 63) & ~63)) qmask[n_all + tid] = 0;
 }
 
-__global__ __launch_bounds__(256) void order_groups_kernel(const int* qcount, int64_t G, int* order) {
-  order_by_cost(G, [&](int64_t g) { return (qcount[g] + 31) >> 5; }, order);
+// Work order of the query groups (largest union first) and the total count
+// of extra entries (repeated slots) over all groups.
+__global__ __launch_bounds__(256) void order_groups_kernel(const int* qcount, const int* xcount, int64_t G,
+                                                           int* order, int* xtotal) {
+  __shared__ int s_x[4];
+  int x = 0;
+  for (int64_t g = threadIdx.x; g < G; g += 256) x += xcount[g];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = x;
+  order_by_cost(G, [&](int64_t g) { return (qcount[g] + 31) >> 5; }, order);   // syncs the block
+  if (threadIdx.x == 0) *xtotal = s_x[0] + s_x[1] + s_x[2] + s_x[3];
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
@@ -277,9 +296,10 @@ __global__ void validate_kernel(const int32_t* idx, int64_t n, int64_t s_kv,
 
 }  // namespace
 
-hipError_t launch_order_groups(const int* qcount, int64_t G, int* order, hipStream_t stream) {
+hipError_t launch_order_groups(const int* qcount, const int* xcount, int64_t G, int* order, int* xtotal,
+                               hipStream_t stream) {
   if (G == 0) return hipSuccess;
-  order_groups_kernel<<<1, 256, 0, stream>>>(qcount, G, order);
+  order_groups_kernel<<<1, 256, 0, stream>>>(qcount, xcount, G, order, xtotal);
   return hipGetLastError();
 }
 

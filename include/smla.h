@@ -147,7 +147,7 @@ int smla_validate_indices(const int32_t* indices, int64_t s_q, int32_t topk, int
  * smla_timing_start and destroyed by the next start).  smla_timing_read waits
  * for the recorded events of the steps named `kernel` and returns how many
  * were recorded and their summed duration in milliseconds.  Step names:
- * "fill", "plan", "order" (work order of the query groups), "fwd",
+ * "plan", "order" (work order of the query groups), "fwd",
  * "bwd_dq", "dkv_schedule" (chunk lists and dkv work order: two small
  * kernels), "bwd_dkv" (the dkv kernel alone), "dkv_finalize", "validate". */
 int smla_timing_start(int max_launches);
