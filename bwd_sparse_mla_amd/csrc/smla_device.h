@@ -199,6 +199,25 @@ __device__ __forceinline__ void static_for(F&& f) { static_for_from<0, N>(f); }
 // s_waitcnt vmcnt(0) (other counters untouched).
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Reductions across the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
+// with the gfx950 row-swap instructions (VALU, no LDS round trip).
+// v_permlane16_swap with both operands v gives (v of row 2k, v of row 2k+1)
+// in rows 2k and 2k+1; v_permlane32_swap gives (v of lanes 0-31, v of lanes
+// 32-63) in both halves.  Every lane combines the same pair in the same
+// order, so all four lanes of a column get bitwise the same result.
+__device__ __forceinline__ float max_rows(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_rows(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Reductions across the 16 lanes that share l >> 4 (one C-fragment row group).
 __device__ __forceinline__ float max16(float v) {
   v = fmaxf(v, __shfl_xor(v, 1));
