@@ -254,43 +254,52 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dkv pass
 // ---------------------------------------------------------------------------
-// Work item: kv block `blk` (64 rows) and split `split` of the block's chunk
-// list; a chunk is one query group with records for the block (T tokens, 64
-// query rows, contiguous in q / dout / lse / delta).  Chunks are processed as
-// two sub-chunks of 32 query rows, double buffered: every step first issues
-// the direct global->LDS copies of the next sub-chunk (Q, dout, its tokens'
-// row masks, lse, delta -- all addresses computed, no memory read on the way)
-// and then computes the current one.  The item accumulates dkv for the
-// block's 64 rows in registers and writes its fp32 partial sum;
-// dkv_finalize_kernel adds a block's partials in split order.  Launch order is
-// split-major, so every block's first split goes first.
+// kv-major: a kv block (64 rows) has a chunk list, one chunk per query group
+// with records for the block (T tokens, 64 query rows, contiguous in q / dout
+// / lse / delta); a chunk is processed as two sub-chunks of 32 query rows.
+// DKV_WGS workgroups (one per CU) each take an equal share of all blocks'
+// sub-chunks in block order (stream-K style: the work is even whatever the
+// blocks' sizes), as one segment per block they meet.  A segment keeps the
+// block's rows in registers, walks its sub-chunks double buffered (every
+// step first issues the direct global->LDS copies of the next sub-chunk: Q,
+// dout, its tokens' row masks, lse, delta -- all addresses computed, no
+// memory read on the way -- then computes the current one), accumulates dkv
+// in registers and writes an fp32 partial; dkv_finalize_kernel adds a
+// block's partials in workgroup order.
 constexpr int DKV_SUB = 32;                                 // query rows per sub-chunk
 
 constexpr int DKV_NW = 8;                                   // waves per workgroup
 
-template <int H>
-__global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
-  constexpr int T = GROUP_ROWS / H;
-  constexpr int SP = DKV_SUB + 8;  // P^T / dS^T row stride (bf16): 80 bytes
-  __shared__ __attribute__((aligned(16))) char sQ[2][KV32_TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char sD[2][DO32_TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned sM[2][64];   // T row masks (2 words each)
-  __shared__ __attribute__((aligned(16))) float sL[2][64];      // lse of the 32 rows
-  __shared__ __attribute__((aligned(16))) float sE[2][64];      // delta of the 32 rows
-  __shared__ __attribute__((aligned(16))) unsigned short sPT[TILE_KV * SP];
-  __shared__ __attribute__((aligned(16))) unsigned short sDST[TILE_KV * SP];
+// LDS of a dkv workgroup (double-buffered sub-chunks, P^T and dS^T tiles).
+constexpr int DKV_SP = DKV_SUB + 8;  // P^T / dS^T row stride (bf16): 80 bytes
+struct DkvLds {
+  __attribute__((aligned(16))) char sQ[2][KV32_TILE_BYTES];
+  __attribute__((aligned(16))) char sD[2][DO32_TILE_BYTES];
+  __attribute__((aligned(16))) unsigned sM[2][64];   // T row masks (2 words each)
+  __attribute__((aligned(16))) float sL[2][64];      // lse of the 32 rows
+  __attribute__((aligned(16))) float sE[2][64];      // delta of the 32 rows
+  __attribute__((aligned(16))) unsigned short sPT[TILE_KV * DKV_SP];
+  __attribute__((aligned(16))) unsigned short sDST[TILE_KV * DKV_SP];
+};
 
+// Sub-chunks u0 .. u1-1 of kv block `blk` (sub-chunk u is query rows
+// 32 (u & 1) .. +31 of the block's chunk u / 2); the fp32 partial dkv of the
+// block's 64 rows goes to partial slot `slot`.
+template <int H>
+__device__ __forceinline__ void dkv_segment(const BwdArgs& a, int64_t blk, int u0, int u1, int64_t slot,
+                                            DkvLds& lds) {
+  constexpr int T = GROUP_ROWS / H;
+  constexpr int SP = DKV_SP;
+  auto& sQ = lds.sQ;
+  auto& sD = lds.sD;
+  auto& sM = lds.sM;
+  auto& sL = lds.sL;
+  auto& sE = lds.sE;
+  auto& sPT = lds.sPT;
+  auto& sDST = lds.sDST;
   const int tid = threadIdx.x, lane_id = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int item = a.korder[blockIdx.x];
-  const int64_t blk = item % a.NB;
-  const int split = (int)(item / a.NB);
   const int nch = a.nchunk[blk];
-  const int nsplit = dkv_nsplit(nch, a.maxsplit);
-  if (split >= nsplit) return;
-  const int c_lo = (int)((int64_t)split * nch / nsplit);
-  const int c_hi = (int)((int64_t)(split + 1) * nch / nsplit);
-  const int nsub = 2 * (c_hi - c_lo);
   const int64_t kb0 = blk * TILE_KV;
   const int64_t qrows = a.s_q * H;   // rows of q / dout / lse / delta
 
@@ -322,15 +331,15 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
   unsigned long long touched = 0ull;
 
   const uint64_t zero = reinterpret_cast<uint64_t>(zero_row());
-  // Sub-chunk u covers query rows 32 (u & 1) .. +31 of chunk c_lo + u / 2 (a
+  // Sub-chunk u covers query rows 32 (u & 1) .. +31 of chunk u / 2 (a
   // query group); its buffers hold those rows of Q and dout as swizzled
   // 32-row tiles, the group's token masks for the block, and the rows' lse and
   // delta.  Every step first issues the copies of sub-chunk u+1 (4 Q rows,
   // one Q tail copy for waves 0-3, 4 dout rows and, for waves 5-7, the masks /
   // lse / delta) into the other buffer set.
-  const int2* clist = a.clist + blk * a.G + c_lo;
-  int2 ce_cur = clist[0];                                  // chunk of the current sub-chunk
-  int2 ce_nxt = clist[min(1, max(0, nsub / 2 - 1))];       // the chunk after it
+  const int2* clist = a.clist + blk * a.G;
+  int2 ce_cur = clist[u0 >> 1];                            // chunk of the current sub-chunk
+  int2 ce_nxt = clist[min((u0 >> 1) + 1, nch - 1)];        // the chunk after it
   auto small_copy = [&](int2 ce, int64_t row0, unsigned* m_dst, float* l_dst, float* e_dst, int lane) __attribute__((always_inline)) {
     if (wv == 5) {
       const uint64_t src = reinterpret_cast<uint64_t>(a.krmask + (int64_t)ce.x * a.rcap + ce.y) + 4u * lane;
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
                   const float* se, char* nq, char* nd, unsigned* nm, float* nl, float* ne) __attribute__((always_inline)) {
     wait_vmcnt0();
     __syncthreads();
-    if (u + 1 < nsub) {   // copies of sub-chunk u+1 into the other buffer set
+    if (u + 1 < u1) {   // copies of sub-chunk u+1 into the other buffer set
       int lane = lane_id;
       asm volatile("" : "+v"(lane));   // offsets recomputed per sub-chunk, not kept live
       const int2 cen = (u & 1) ? ce_nxt : ce_cur;
@@ -463,28 +472,28 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
     }
     if (u & 1) {   // the next sub-chunk starts chunk u/2 + 1: load the one after it
       ce_cur = ce_nxt;
-      if ((u >> 1) + 2 < nsub / 2) ce_nxt = clist[(u >> 1) + 2];
+      if ((u >> 1) + 2 < nch) ce_nxt = clist[(u >> 1) + 2];
     }
   };
 
-  if (nsub > 0) {
+  {
     int64_t row0;
     int nvalid;
-    rows_of(ce_cur, 0, row0, nvalid);
+    rows_of(ce_cur, u0, row0, nvalid);
     gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW>(sQ[0], a.q + row0 * D_K, nvalid, wv, lane_id);
     gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW>(sD[0], a.dout + row0 * D_V, nvalid, wv, lane_id);
     small_copy(ce_cur, row0, sM[0], sL[0], sE[0], lane_id);
   }
-  for (int u = 0; u < nsub; ++u) {
-    const int b = u & 1;
+  for (int u = u0; u < u1; ++u) {
+    const int b = (u - u0) & 1;
     step(u, sQ[b], sD[b], sM[b], sL[b], sE[b], sQ[b ^ 1], sD[b ^ 1], sM[b ^ 1], sL[b ^ 1], sE[b ^ 1]);
   }
 
-  // Partial sum of this item: rows 32 drh + 16 rb + 4 g + i, columns
+  // Partial sum of the segment: rows 32 drh + 16 rb + 4 g + i, columns
   // 128 dcq + 16 n + r (n < 8) and 512 + 16 dcq + r (n = 8).
   {
     const int g16 = lane_id >> 4, r16 = lane_id & 15;
-    float* dst = a.part + ((blk * a.maxsplit + split) * TILE_KV + 32 * drh + 4 * g16) * D_K + r16;
+    float* dst = a.part + (slot * TILE_KV + 32 * drh + 4 * g16) * D_K + r16;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -493,7 +502,28 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
         for (int n = 0; n < 9; ++n)
           dst[(16 * rb + i) * D_K + (n < 8 ? 128 * dcq + 16 * n : D_V + 16 * dcq)] = acc[rb][n][i];
   }
-  if (tid == 0) a.ptouch[blk * a.maxsplit + split] = touched;
+  if (tid == 0) a.ptouch[slot] = touched;
+}
+
+// The dkv pass: workgroup w takes sub-chunks [w per, (w+1) per) of all
+// blocks' sub-chunks in block order (per = ceil(total / DKV_WGS)), as one
+// segment per block it meets, starting from block wstart[w].
+template <int H>
+__global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
+  __shared__ DkvLds lds;
+  const int total = a.spre[a.NB];
+  const int per = max(1, (total + DKV_WGS - 1) / DKV_WGS);
+  int lo = min(total, (int)blockIdx.x * per);
+  const int hi = min(total, lo + per);
+  if (lo >= hi) return;
+  for (int64_t blk = a.wstart[blockIdx.x]; lo < hi; ++blk) {
+    const int sb = a.spre[blk], se = a.spre[blk + 1];
+    if (se <= lo) continue;   // a block with no records
+    const int end = min(hi, se);
+    dkv_segment<H>(a, blk, lo - sb, end - sb, (int64_t)blockIdx.x + blk, lds);
+    lo = end;
+    __syncthreads();   // the next segment refills the LDS buffers
+  }
 }
 
 // Compacts each kv block's row of the [block, group] record table into the
@@ -516,18 +546,38 @@ __global__ __launch_bounds__(256) void dkv_schedule_kernel(BwdArgs a) {
   if (tid == 0) a.nchunk[blk] = base;
 }
 
-// Work order of the dkv items (split-major index split * NB + block) by
-// decreasing chunk count; items past a block's split count come last (they
-// exit at once).
-__global__ __launch_bounds__(256) void dkv_order_kernel(BwdArgs a) {
-  order_by_cost(a.NB * a.maxsplit, [&](int64_t i) {
-    const int64_t blk = i % a.NB;
-    const int split = (int)(i / a.NB);
-    const int nch = a.nchunk[blk];
-    const int ns = dkv_nsplit(nch, a.maxsplit);
-    if (split >= ns) return 0;
-    return (int)((int64_t)(split + 1) * nch / ns - (int64_t)split * nch / ns);
-  }, a.korder);
+// Sub-chunk prefix over the blocks (spre[b] = sub-chunks of blocks before b,
+// spre[NB] = total) and the first block of each dkv workgroup's range.  Two
+// passes of the same scan: the second finds, for every block, the
+// workgroups whose range starts inside it.
+__global__ __launch_bounds__(256) void dkv_prefix_kernel(BwdArgs a) {
+  __shared__ int scratch[8];
+  __shared__ int s_total;
+  int base = 0;
+  for (int64_t b0 = 0; b0 < a.NB; b0 += 256) {
+    const int64_t b = b0 + threadIdx.x;
+    const int v = b < a.NB ? 2 * a.nchunk[b] : 0;
+    int tot;
+    const int pos = base + block_exclusive_scan256(v, scratch, &tot);
+    if (b < a.NB) a.spre[b] = pos;
+    base += tot;
+  }
+  if (threadIdx.x == 0) {
+    a.spre[a.NB] = base;
+    s_total = base;
+  }
+  __syncthreads();
+  const int per = max(1, (s_total + DKV_WGS - 1) / DKV_WGS);
+  base = 0;
+  for (int64_t b0 = 0; b0 < a.NB; b0 += 256) {
+    const int64_t b = b0 + threadIdx.x;
+    const int v = b < a.NB ? 2 * a.nchunk[b] : 0;
+    int tot;
+    const int pos = base + block_exclusive_scan256(v, scratch, &tot);
+    if (v > 0)
+      for (int w = (pos + per - 1) / per; w < DKV_WGS && w * per < pos + v; ++w) a.wstart[w] = (int)b;
+    base += tot;
+  }
 }
 
 // Sum of 256 per-thread values, identical on every thread (fixed order).
@@ -542,7 +592,7 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 }
 
 // Writes dkv for FIN_ROWS rows of a block (64 / FIN_ROWS workgroups per
-// block): the block's split partials added in split order, plus -- only when
+// block): the block's partials added in workgroup order, plus -- only when
 // some index row repeats an entry -- the extra slots' contributions, each
 // computed directly in (group, slot) order.  Output semantics (bf16, fp32,
 // accumulate, rows no slot selects) are applied here.  Bitwise reproducible.
@@ -557,9 +607,15 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
   const int64_t blk = blockIdx.x / FIN_PARTS;
   const int part = blockIdx.x % FIN_PARTS;
   const int64_t r0 = blk * TILE_KV + FIN_ROWS * part;  // first row of this workgroup
-  const int nsplit = dkv_nsplit(a.nchunk[blk], a.maxsplit);
+  // The block's partials: slots w + blk of the workgroups w whose ranges
+  // cover its sub-chunks, added in w order.
+  const int total = a.spre[a.NB];
+  const int per = max(1, (total + DKV_WGS - 1) / DKV_WGS);
+  const int sb = a.spre[blk], se = a.spre[blk + 1];
+  const int w0 = sb / per;
+  const int nsplit = se > sb ? (se - 1) / per - w0 + 1 : 0;
   unsigned long long touched = 0ull;
-  for (int sp = 0; sp < nsplit; ++sp) touched |= a.ptouch[blk * a.maxsplit + sp];
+  for (int sp = 0; sp < nsplit; ++sp) touched |= a.ptouch[w0 + sp + blk];
   touched = (touched >> (FIN_ROWS * part)) & ((1ull << FIN_ROWS) - 1ull);
 
   const bool extras = *a.xtotal > 0;
@@ -603,14 +659,15 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  const float* src = a.part + (blk * a.maxsplit * TILE_KV + FIN_ROWS * part) * D_K;
+  const float* src = a.part + ((w0 + blk) * TILE_KV + FIN_ROWS * part) * D_K;
   constexpr int N4 = FIN_ROWS * D_K / 4;  // float4 elements of the rows
   constexpr int64_t SPLIT = (int64_t)TILE_KV * D_K;
   for (int e = tid; e < N4; e += 256) {
-    // Split partials summed left to right in split order; loads go out four
-    // at a time (indices clamped into range, extra ones unused).
+    // Partials summed left to right in workgroup order; loads go out four
+    // at a time (indices clamped into range, extra ones unused).  A block no
+    // record touches has no partial: zeros.
     const float* pe = src + 4 * e;
-    float4_t v = *reinterpret_cast<const float4_t*>(pe);
+    float4_t v = nsplit > 0 ? *reinterpret_cast<const float4_t*>(pe) : (float4_t){0.f, 0.f, 0.f, 0.f};
     for (int sp = 1; sp < nsplit; sp += 4) {
       const float4_t p0 = *reinterpret_cast<const float4_t*>(pe + sp * SPLIT);
       const float4_t p1 = *reinterpret_cast<const float4_t*>(pe + min(sp + 1, nsplit - 1) * SPLIT);
@@ -670,13 +727,13 @@ hipError_t launch_dkv_schedule(const BwdArgs& a, hipStream_t stream) {
   dkv_schedule_kernel<<<dim3((unsigned)a.NB), dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dkv_order_kernel<<<dim3(1), dim3(256), 0, stream>>>(a);
+  dkv_prefix_kernel<<<dim3(1), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream) {
   if (a.NB == 0) return hipSuccess;
-  const dim3 grid((unsigned)(a.NB * a.maxsplit)), block(DKV_NW * 64);
+  const dim3 grid((unsigned)DKV_WGS), block(DKV_NW * 64);
   switch (heads) {
     case 8: bwd_dkv_kernel<8><<<grid, block, 0, stream>>>(a); break;
     case 16: bwd_dkv_kernel<16><<<grid, block, 0, stream>>>(a); break;

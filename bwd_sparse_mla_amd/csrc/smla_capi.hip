@@ -114,15 +114,12 @@ Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward) {
     p.off_ktab = o;    o = align256(o + (size_t)p.NB * p.G * 8);
     p.off_krmask = o;  o = align256(o + (size_t)p.G * p.rcap * 8);
     p.off_delta = o;   o = align256(o + (size_t)s_q * heads * 4);
-    // Split the per-block dkv reduction so that about DKV_TARGET_ITEMS
-    // workgroups run (at most 64 splits per block).
-    int64_t ms = (DKV_TARGET_ITEMS + p.NB - 1) / p.NB;
-    p.maxsplit = (int)(ms < 1 ? 1 : (ms > 64 ? 64 : ms));
     p.off_clist = o;   o = align256(o + (size_t)p.NB * p.G * 8);
     p.off_nchunk = o;  o = align256(o + (size_t)p.NB * 4);
-    p.off_ptouch = o;  o = align256(o + (size_t)p.NB * p.maxsplit * 8);
-    p.off_korder = o;  o = align256(o + (size_t)p.NB * p.maxsplit * 4);
-    p.off_part = o;    o = align256(o + (size_t)p.NB * p.maxsplit * TILE_KV * 576 * 4);
+    p.off_ptouch = o;  o = align256(o + (size_t)(DKV_WGS + p.NB) * 8);
+    p.off_spre = o;    o = align256(o + (size_t)(p.NB + 1) * 4);
+    p.off_wstart = o;  o = align256(o + (size_t)DKV_WGS * 4);
+    p.off_part = o;    o = align256(o + (size_t)(DKV_WGS + p.NB) * TILE_KV * 576 * 4);
   }
   p.bytes = o;
   return p;
@@ -314,11 +311,11 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   ba.ktab = pa.ktab;
   ba.krmask = pa.krmask;
   ba.gorder = gorder;
-  ba.korder = reinterpret_cast<int*>(ws + p.off_korder);
+  ba.spre = reinterpret_cast<int*>(ws + p.off_spre);
+  ba.wstart = reinterpret_cast<int*>(ws + p.off_wstart);
   ba.delta = reinterpret_cast<float*>(ws + p.off_delta);
   ba.clist = reinterpret_cast<int2*>(ws + p.off_clist);
   ba.nchunk = reinterpret_cast<int*>(ws + p.off_nchunk);
-  ba.maxsplit = p.maxsplit;
   ba.part = reinterpret_cast<float*>(ws + p.off_part);
   ba.ptouch = reinterpret_cast<unsigned long long*>(ws + p.off_ptouch);
   ba.dq = static_cast<uint16_t*>(dq);

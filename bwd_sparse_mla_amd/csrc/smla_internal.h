@@ -29,8 +29,7 @@ struct Plan {
   size_t off_qcount = 0, off_xcount = 0, off_xtotal = 0, off_qrow = 0, off_qmask = 0;
   size_t off_ktab = 0, off_krmask = 0, off_delta = 0;
   size_t off_clist = 0, off_nchunk = 0, off_part = 0, off_ptouch = 0;
-  size_t off_gorder = 0, off_korder = 0;
-  int maxsplit = 1;   // dkv partial sums per kv block (split over its records)
+  size_t off_gorder = 0, off_spre = 0, off_wstart = 0;
   size_t bytes = 0;
 };
 
@@ -81,13 +80,13 @@ struct BwdArgs {
   const int2* ktab;
   const unsigned long long* krmask;
   const int* gorder;  // [G] groups by decreasing union size (dq pass)
-  int* korder;        // [NB * maxsplit] dkv items by decreasing chunk count
+  int* spre;          // [NB + 1] dkv sub-chunks before each block (exclusive prefix; [NB] = total)
+  int* wstart;        // [DKV_WGS] first kv block of each dkv workgroup's range
   float* delta;       // [s_q * H] rowsum(dout * out), written by the dq pass
   int2* clist;        // [NB, G] per block: (group, record start), compacted
   int* nchunk;        // [NB] entries of clist per block
-  int maxsplit;       // splits per kv block at most
-  float* part;        // [NB * maxsplit, 64, 576] fp32 partial dkv of each split
-  unsigned long long* ptouch;  // [NB * maxsplit] rows each split touched
+  float* part;        // [DKV_WGS + NB, 64, 576] fp32 partial dkv per (workgroup w, block b): slot w + b
+  unsigned long long* ptouch;  // [DKV_WGS + NB] rows each partial touched
   uint16_t* dq;
   uint16_t* dkv;      // may be null
   float* dkv_f32;     // may be null
@@ -106,18 +105,10 @@ hipError_t launch_dkv_schedule(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream);
 hipError_t launch_dkv_finalize(const BwdArgs& a, int heads, hipStream_t stream);
 // dkv split schedule: chunks a split covers at least, and the split count.
-#ifndef SMLA_DKV_MIN_CHUNKS
-#define SMLA_DKV_MIN_CHUNKS 8
-#endif
-#ifndef SMLA_DKV_TARGET_ITEMS
-#define SMLA_DKV_TARGET_ITEMS 512
-#endif
-constexpr int DKV_MIN_CHUNKS = SMLA_DKV_MIN_CHUNKS;
-constexpr int DKV_TARGET_ITEMS = SMLA_DKV_TARGET_ITEMS;   // dkv work items aimed for
-__host__ __device__ inline int dkv_nsplit(int nchunk, int maxsplit) {
-  int n = (nchunk + DKV_MIN_CHUNKS - 1) / DKV_MIN_CHUNKS;
-  return n < 1 ? 1 : (n > maxsplit ? maxsplit : n);
-}
+// The dkv pass runs DKV_WGS workgroups (one per CU of the part), each over an
+// equal share of all sub-chunks in block order (stream-K style); a workgroup
+// w that covers sub-chunks of block b leaves its partial in slot w + b.
+constexpr int DKV_WGS = 256;
 hipError_t launch_validate(const int32_t* idx, int64_t n, int64_t s_kv,
                            unsigned long long* n_bad, hipStream_t stream);
 
