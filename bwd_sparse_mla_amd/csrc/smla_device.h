@@ -361,24 +361,26 @@ __device__ __forceinline__ void gather_seq_rows(char* tile, const uint16_t* firs
 }
 
 // gather_kv_rows for a workgroup of NW waves (NW >= 4, R / NW rows each):
-// wave wv copies rows R/NW * wv .. +R/NW-1 and, for wv < R/8, the tails of
-// rows 8 wv .. 8 wv + 7.
-template <int R, int CH, int NW>
+// wave wv copies rows R/NW * wv .. +R/NW-1 (ROWS) and, for wv < R/8, the tails
+// of rows 8 wv .. 8 wv + 7 (TAILS).
+template <int R, int CH, int NW, bool ROWS = true, bool TAILS = true>
 __device__ __forceinline__ void gather_kv_rows_nw(char* tile, const uint16_t* kv, int64_t s_kv,
                                                   const int* rows, int count, int wv, int lane) {
   constexpr int PER = R / NW;
   static_assert(PER >= 1 && (PER & (PER - 1)) == 0, "rows per wave must be a power of two");
   const uint32_t base = lds_offset(tile);
-  const int vrow = rows[PER * wv + (lane & (PER - 1))];
+  if constexpr (ROWS) {
+    const int vrow = rows[PER * wv + (lane & (PER - 1))];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int r = PER * wv + i;
-    const int row = __builtin_amdgcn_readlane(vrow, i);
-    const bool ok = r < count && (uint32_t)row < (uint32_t)s_kv;
-    const uint16_t* src = (ok ? kv : g_zero_row) + (uint32_t)(ok ? row : 0) * (uint32_t)D_K;
-    g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), base + 1024u * (uint32_t)r);
+    for (int i = 0; i < PER; ++i) {
+      const int r = PER * wv + i;
+      const int row = __builtin_amdgcn_readlane(vrow, i);
+      const bool ok = r < count && (uint32_t)row < (uint32_t)s_kv;
+      const uint16_t* src = (ok ? kv : g_zero_row) + (uint32_t)(ok ? row : 0) * (uint32_t)D_K;
+      g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), base + 1024u * (uint32_t)r);
+    }
   }
-  if constexpr (CH == ROW_CHUNKS) {
+  if constexpr (CH == ROW_CHUNKS && TAILS) {
     if (wv < R / 8) {
       const int r = 8 * wv + (lane >> 3);
       const int row = rows[r];

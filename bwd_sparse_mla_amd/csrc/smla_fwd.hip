@@ -11,9 +11,9 @@
 //            row softmax, and leaves P (bf16) and the rescale factors in LDS;
 //   PV waves 4-7:    wave 4+c accumulates out[:, 128c .. 128c+127] for all 64
 //            rows from the previous tile's P and V (32 MFMA).
-// Per step the PV waves wait for their copies and the workgroup syncs once;
-// then the PV waves issue the next tile's copies (9-10 per wave) and take
-// tile j-1 while the score waves take tile j.  Two waves share each SIMD, so
+// Per step every wave waits for its copies and the workgroup syncs once; then
+// the next tile's copies are issued (8-9 per PV wave, one per score wave) and
+// the PV waves take tile j-1 while the score waves take tile j.  Two waves share each SIMD, so
 // one's softmax, copies and LDS waits overlap the other's MFMAs.
 //
 // The running max starts at a finite -1e30, so a tile with no valid entry
@@ -83,14 +83,18 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   const int tl = (16 * wv + (lane_id & 15)) / H;
   float m_run = M_INIT, lsum = 0.f;
 
-  // Copies of tile t (its rows' indices are in sRow[t % 3]), all issued by
-  // the PV waves (the score waves carry the longer per-tile work): kv rows 8
-  // per wave plus one tail copy each, the token masks by wave 4, the row
-  // indices of tile t + 1 by wave 5.
+  // Copies of tile t (its rows' indices are in sRow[t % 3]): the first 1 KB
+  // of 8 kv rows per PV wave, the rope tails of 8 rows per score wave (the
+  // score waves carry more of the per-tile work), the token masks by wave 4,
+  // the row indices of tile t + 1 by wave 5.
   auto issue = [&](int t) __attribute__((always_inline)) {
     const int b = t % FNB;
-    gather_kv_rows_nw<FT, ROW_CHUNKS, 4>(sK[b], a.kv, a.s_kv, sRow[b], min(FT, n_ent - t * FT),
-                                         wv - 4, lane_id);
+    if (score_wave)
+      gather_kv_rows_nw<FT, ROW_CHUNKS, 4, false, true>(sK[b], a.kv, a.s_kv, sRow[b],
+                                                        min(FT, n_ent - t * FT), wv, lane_id);
+    else
+      gather_kv_rows_nw<FT, ROW_CHUNKS, 4, true, false>(sK[b], a.kv, a.s_kv, sRow[b],
+                                                        min(FT, n_ent - t * FT), wv - 4, lane_id);
     copy_union_entries(nullptr, sMask[b], erow, emask, t * FT, n_ent, FT, wv, 5, 4, lane_id);
     if (t + 1 < ntiles)
       copy_union_entries(sRow[(t + 1) % FNB], nullptr, erow, emask, (t + 1) * FT, n_ent, FT, wv, 5,
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
     copy_union_entries(sRow[0], nullptr, erow, emask, 0, n_ent, FT, wv, 5, 4, lane_id);
     wait_vmcnt0();
     __syncthreads();
-    if (!score_wave) issue(0);
+    issue(0);
   }
   // Step j: the score waves take tile j, the PV waves tile j - 1; tile j + 1
   // is copied meanwhile into the buffer tile j - 2 used.  The two roles run
@@ -220,7 +224,9 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   // same count of workgroup barriers, one per step.
   if (score_wave) {
     for (int j = 0; j <= ntiles; ++j) {
+      wait_vmcnt0();
       __syncthreads();
+      if (j + 1 < ntiles) issue(j + 1);
       if (j < ntiles) score(j);
     }
   } else {
