@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dkv-mode", default="deterministic", choices=["deterministic", "atomic"],
+                    help="dkv reduction: the bitwise-reproducible per-row reduction (default) or "
+                         "fp32 atomic adds")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel HIP events")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -162,7 +165,7 @@ def main():
         torch.bfloat16).to(dev)
     q, kv, dout = to_bf16(w.q), to_bf16(w.kv), to_bf16(w.dout)
     idx = torch.from_numpy(np.ascontiguousarray(w.idx)).to(dev)
-    run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, dev)
+    run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, dev, dkv_atomic=args.dkv_mode == "atomic")
     run._check(q, kv, idx, dout)
 
     def step():
@@ -212,7 +215,8 @@ def main():
     kernels = {}
     roofline = None
     if timing:
-        for name in ("plan", "order", "fwd", "bwd_dq", "dkv_schedule", "bwd_dkv", "dkv_finalize"):
+        for name in ("plan", "order", "fwd", "bwd_dq", "dkv_schedule", "dkv_clear", "bwd_dkv",
+                     "dkv_finalize"):
             n, tot = smla.timing_read(name)
             if n:
                 kernels[name] = {"launches": n, "avg_ms": tot / n}
@@ -251,7 +255,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "S": w.S, "S_kv": w.S_kv, "H": w.H, "topk": w.K,
                    "seqlens": w.seqlens, "valid_pairs": nv, "useful_gflop": useful / 1e9,
-                   "parallelism": "none (one GPU)", "dkv_mode": "deterministic"},
+                   "parallelism": "none (one GPU)", "dkv_mode": args.dkv_mode},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
         "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kernels.items()},
         "kernel_timing": ("per-launch HIP events on the library's stream, in a second pass of "

@@ -490,8 +490,22 @@ __device__ __forceinline__ void dkv_segment(const BwdArgs& a, int64_t blk, int u
   }
 
   // Partial sum of the segment: rows 32 drh + 16 rb + 4 g + i, columns
-  // 128 dcq + 16 n + r (n < 8) and 512 + 16 dcq + r (n = 8).
-  {
+  // 128 dcq + 16 n + r (n < 8) and 512 + 16 dcq + r (n = 8).  The atomic mode
+  // adds it into the block's rows of the fp32 accumulator with no-return
+  // fp32 atomics instead (the order the segments' adds land in varies, so
+  // that mode is not bitwise reproducible).
+  if (a.acc32) {
+    const int g16 = lane_id >> 4, r16 = lane_id & 15;
+    float* dst = a.acc32 + (kb0 + 32 * drh + 4 * g16) * D_K + r16;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 9; ++n)
+          unsafeAtomicAdd(&dst[(16 * rb + i) * D_K + (n < 8 ? 128 * dcq + 16 * n : D_V + 16 * dcq)],
+                          acc[rb][n][i]);
+  } else {
     const int g16 = lane_id >> 4, r16 = lane_id & 15;
     float* dst = a.part + (slot * TILE_KV + 32 * drh + 4 * g16) * D_K + r16;
 #pragma unroll
@@ -659,7 +673,10 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  const float* src = a.part + ((w0 + blk) * TILE_KV + FIN_ROWS * part) * D_K;
+  // Atomic mode: one source, the accumulator's rows of the block.
+  const float* src = a.acc32 ? a.acc32 + (blk * TILE_KV + FIN_ROWS * part) * D_K
+                             : a.part + ((w0 + blk) * TILE_KV + FIN_ROWS * part) * D_K;
+  const int nsrc = a.acc32 ? (nsplit > 0 ? 1 : 0) : nsplit;
   constexpr int N4 = FIN_ROWS * D_K / 4;  // float4 elements of the rows
   constexpr int64_t SPLIT = (int64_t)TILE_KV * D_K;
   for (int e = tid; e < N4; e += 256) {
@@ -667,16 +684,16 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
     // at a time (indices clamped into range, extra ones unused).  A block no
     // record touches has no partial: zeros.
     const float* pe = src + 4 * e;
-    float4_t v = nsplit > 0 ? *reinterpret_cast<const float4_t*>(pe) : (float4_t){0.f, 0.f, 0.f, 0.f};
-    for (int sp = 1; sp < nsplit; sp += 4) {
+    float4_t v = nsrc > 0 ? *reinterpret_cast<const float4_t*>(pe) : (float4_t){0.f, 0.f, 0.f, 0.f};
+    for (int sp = 1; sp < nsrc; sp += 4) {
       const float4_t p0 = *reinterpret_cast<const float4_t*>(pe + sp * SPLIT);
-      const float4_t p1 = *reinterpret_cast<const float4_t*>(pe + min(sp + 1, nsplit - 1) * SPLIT);
-      const float4_t p2 = *reinterpret_cast<const float4_t*>(pe + min(sp + 2, nsplit - 1) * SPLIT);
-      const float4_t p3 = *reinterpret_cast<const float4_t*>(pe + min(sp + 3, nsplit - 1) * SPLIT);
+      const float4_t p1 = *reinterpret_cast<const float4_t*>(pe + min(sp + 1, nsrc - 1) * SPLIT);
+      const float4_t p2 = *reinterpret_cast<const float4_t*>(pe + min(sp + 2, nsrc - 1) * SPLIT);
+      const float4_t p3 = *reinterpret_cast<const float4_t*>(pe + min(sp + 3, nsrc - 1) * SPLIT);
       v += p0;
-      if (sp + 1 < nsplit) v += p1;
-      if (sp + 2 < nsplit) v += p2;
-      if (sp + 3 < nsplit) v += p3;
+      if (sp + 1 < nsrc) v += p1;
+      if (sp + 2 < nsrc) v += p2;
+      if (sp + 3 < nsrc) v += p3;
     }
     if (extras) v += *reinterpret_cast<const float4_t*>(sX + 4 * e);
     const int kvl = (4 * e) / D_K;

@@ -91,7 +91,7 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
 
 }  // namespace
 
-Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward) {
+Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward, bool atomic) {
   Plan p;
   p.s_q = s_q;
   p.s_kv = s_kv;
@@ -120,6 +120,12 @@ Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward) {
     p.off_spre = o;    o = align256(o + (size_t)(p.NB + 1) * 4);
     p.off_wstart = o;  o = align256(o + (size_t)DKV_WGS * 4);
     p.off_part = o;    o = align256(o + (size_t)(DKV_WGS + p.NB) * TILE_KV * 576 * 4);
+    // Atomic dkv mode: the fp32 accumulator goes last, so the rest of the
+    // layout (and a plan smla_plan built) is the same in both modes.
+    if (atomic) {
+      p.off_acc32 = o;
+      o = align256(o + (size_t)p.NB * TILE_KV * 576 * 4);
+    }
   }
   p.bytes = o;
   return p;
@@ -148,9 +154,8 @@ size_t smla_fwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t
 
 size_t smla_bwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
                                uint32_t flags) {
-  (void)flags;
   if (check_shape(s_q, s_kv, heads, topk) != SMLA_OK) return 0;
-  return make_plan(s_q, s_kv, heads, topk, true).bytes;
+  return make_plan(s_q, s_kv, heads, topk, true, (flags & SMLA_DKV_ATOMIC) != 0).bytes;
 }
 
 // Fills the planner's arguments for a workspace laid out by make_plan.
@@ -269,16 +274,15 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
     return fail(SMLA_ERR_FLAGS, "unknown flag bits");
   if ((flags & SMLA_DKV_ACCUMULATE) && !dkv_f32)
     return fail(SMLA_ERR_FLAGS, "SMLA_DKV_ACCUMULATE needs dkv_f32");
-  if (flags & SMLA_DKV_ATOMIC)
-    return fail(SMLA_ERR_FLAGS, "SMLA_DKV_ATOMIC is not available in this build");
   const void* ptrs[] = {q, kv, out, dout, indices, lse, dq};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   if ((dkv && !aligned16(dkv)) || (dkv_f32 && !aligned16(dkv_f32)))
     return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  const Plan p = make_plan(s_q, s_kv, heads, topk, true);
+  const bool atomic = (flags & SMLA_DKV_ATOMIC) != 0;
+  const Plan p = make_plan(s_q, s_kv, heads, topk, true, atomic);
   if (!workspace || workspace_bytes < p.bytes)
-    return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_bwd_workspace_size()");
+    return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_bwd_workspace_size(flags)");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(SMLA_ERR_ALIGN, "workspace must be 256-byte aligned");
   if ((st = check_device())) return st;
@@ -318,12 +322,17 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   ba.nchunk = reinterpret_cast<int*>(ws + p.off_nchunk);
   ba.part = reinterpret_cast<float*>(ws + p.off_part);
   ba.ptouch = reinterpret_cast<unsigned long long*>(ws + p.off_ptouch);
+  ba.acc32 = atomic ? reinterpret_cast<float*>(ws + p.off_acc32) : nullptr;
   ba.dq = static_cast<uint16_t*>(dq);
   ba.dkv = static_cast<uint16_t*>(dkv);
   ba.dkv_f32 = dkv_f32;
   ba.accumulate = (flags & SMLA_DKV_ACCUMULATE) ? 1 : 0;
   if (s_q > 0 && (st = hip_status(timed("bwd_dq", s, [&] { return launch_bwd_dq(ba, heads, s); }), "bwd_dq"))) return st;
   if ((st = hip_status(timed("dkv_schedule", s, [&] { return launch_dkv_schedule(ba, s); }), "dkv_schedule"))) return st;
+  if (atomic && (st = hip_status(timed("dkv_clear", s, [&] {
+                   return launch_fill_u32(ba.acc32, (size_t)p.NB * TILE_KV * 576, 0u, s);
+                 }), "dkv_clear")))
+    return st;
   if ((st = hip_status(timed("bwd_dkv", s, [&] { return launch_bwd_dkv(ba, heads, s); }), "bwd_dkv"))) return st;
   return hip_status(timed("dkv_finalize", s, [&] { return launch_dkv_finalize(ba, heads, s); }), "dkv_finalize");
 }

@@ -30,10 +30,11 @@ struct Plan {
   size_t off_ktab = 0, off_krmask = 0, off_delta = 0;
   size_t off_clist = 0, off_nchunk = 0, off_part = 0, off_ptouch = 0;
   size_t off_gorder = 0, off_spre = 0, off_wstart = 0;
+  size_t off_acc32 = 0;   // atomic dkv mode only: [NB * 64, 576] fp32 accumulator
   size_t bytes = 0;
 };
 
-Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward);
+Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward, bool atomic = false);
 
 struct PlanArgs {
   const int32_t* idx;
@@ -87,6 +88,7 @@ struct BwdArgs {
   int* nchunk;        // [NB] entries of clist per block
   float* part;        // [DKV_WGS + NB, 64, 576] fp32 partial dkv per (workgroup w, block b): slot w + b
   unsigned long long* ptouch;  // [DKV_WGS + NB] rows each partial touched
+  float* acc32;       // atomic mode: [NB * 64, 576] fp32 dkv accumulated with atomics; else null
   uint16_t* dq;
   uint16_t* dkv;      // may be null
   float* dkv_f32;     // may be null

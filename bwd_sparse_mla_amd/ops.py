@@ -130,12 +130,14 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_
 def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
                    indices: torch.Tensor, lse: torch.Tensor, sm_scale: float, *,
                    dkv_f32: torch.Tensor | None = None, accumulate: bool = False,
+                   atomic: bool = False,
                    want_bf16_dkv: bool = True):
     """Backward: returns (dq like q, dkv like kv in bf16 or None).
 
     dkv_f32, if given, is an fp32 [S_kv, 576] tensor that receives the fp32
     dkv (overwritten, or added to with accumulate=True).  The default mode is
-    the deterministic per-row reduction."""
+    the deterministic per-row reduction; atomic=True scatters dkv with fp32
+    atomic adds (not bitwise reproducible)."""
     lib = _lib.load()
     q3 = _prep(_flat_q(q), torch.bfloat16, "q")
     kv2 = _prep(_flat_kv(kv), torch.bfloat16, "kv")
@@ -152,7 +154,7 @@ def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, out: torch.Tensor, dout: t
     K = ix.shape[1]
     S_kv = kv2.shape[0]
     dev = q3.device
-    flags = 0
+    flags = _lib.SMLA_DKV_ATOMIC if atomic else 0
     if accumulate:
         if dkv_f32 is None:
             raise ValueError("accumulate=True needs dkv_f32")
@@ -208,16 +210,18 @@ class SparseMLARunner:
     nothing.  Inputs must already be contiguous bf16/int32 GPU tensors of the
     shapes given here."""
 
-    def __init__(self, s_q: int, s_kv: int, heads: int, topk: int, device="cuda"):
+    def __init__(self, s_q: int, s_kv: int, heads: int, topk: int, device="cuda",
+                 dkv_atomic: bool = False):
         self.lib = _lib.load()
         self.shape = (s_q, s_kv, heads, topk)
+        self._bflags = _lib.SMLA_DKV_ATOMIC if dkv_atomic else 0
         dev = torch.device(device)
         self.out = torch.empty(s_q, heads, D_V, dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty(s_q, heads, dtype=torch.float32, device=dev)
         self.dq = torch.empty(s_q, heads, D_K, dtype=torch.bfloat16, device=dev)
         self.dkv = torch.empty(s_kv, D_K, dtype=torch.bfloat16, device=dev)
         fb = fwd_workspace_bytes(s_q, s_kv, heads, topk)
-        bb = bwd_workspace_bytes(s_q, s_kv, heads, topk)
+        bb = bwd_workspace_bytes(s_q, s_kv, heads, topk, self._bflags)
         self._fws, self._fws_addr = _workspace(fb, dev)
         self._bws, self._bws_addr = _workspace(bb, dev)
         self._fb, self._bb = fb, bb
@@ -254,7 +258,7 @@ class SparseMLARunner:
         _lib.check(self.lib.smla_bwd(_ptr(q), _ptr(kv), _ptr(self.out), _ptr(dout), _ptr(idx),
                                      _ptr(self.lse), s_q, s_kv, h, k, float(sm_scale),
                                      _ptr(self.dq), _ptr(self.dkv), ctypes.c_void_p(0),
-                                     _lib.SMLA_PLAN_READY if planned else 0,
+                                     self._bflags | (_lib.SMLA_PLAN_READY if planned else 0),
                                      ctypes.c_void_p(self._bws_addr), self._bb,
                                      _stream(self.device)))
         return self.dq, self.dkv

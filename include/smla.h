@@ -76,8 +76,16 @@ enum smla_status {
 #define SMLA_DKV_ACCUMULATE 1u  /* add into the caller's fp32 dkv_f32 instead of
                                    overwriting it; rows no valid slot selects
                                    are left untouched (bit for bit) */
-#define SMLA_DKV_ATOMIC 2u      /* accumulate dkv with fp32 atomics from the
-                                   query-major pass (not bitwise reproducible) */
+#define SMLA_DKV_ATOMIC 2u      /* scatter dkv with fp32 atomic adds (the
+                                   pages' default mode: slime issue #2201,
+                                   "GLM-5.2 SparseMLA TileLang backward returns
+                                   NaN gradients from finite inputs", Suspected
+                                   area): each kv-block partial of the kv-major
+                                   pass is added into an fp32 accumulator with
+                                   no-return atomics, so results vary in the
+                                   last bits run to run; the workspace must be
+                                   smla_bwd_workspace_size(..., SMLA_DKV_ATOMIC)
+                                   bytes */
 #define SMLA_PLAN_READY 4u      /* smla_fwd_ex / smla_bwd: the workspace already
                                    holds the index plan smla_plan built for the
                                    same indices and sizes; skip planning */
@@ -148,8 +156,9 @@ int smla_validate_indices(const int32_t* indices, int64_t s_q, int32_t topk, int
  * for the recorded events of the steps named `kernel` and returns how many
  * were recorded and their summed duration in milliseconds.  Step names:
  * "plan", "order" (work order of the query groups), "fwd",
- * "bwd_dq", "dkv_schedule" (chunk lists and dkv work order: two small
- * kernels), "bwd_dkv" (the dkv kernel alone), "dkv_finalize", "validate". */
+ * "bwd_dq", "dkv_schedule" (chunk lists and the dkv work split: two small
+ * kernels), "dkv_clear" (atomic mode: zeroing the accumulator), "bwd_dkv"
+ * (the dkv kernel alone), "dkv_finalize", "validate". */
 int smla_timing_start(int max_launches);
 int smla_timing_stop(void);
 int smla_timing_read(const char* kernel, int* launches, double* total_ms);

@@ -93,6 +93,12 @@ def test_bwd_argument_errors(lib):
     assert call_bwd(lib, flags=1, dkv32=0) == 5
     assert call_bwd(lib, dkv32=FAKE + 4) == 3
     assert call_bwd(lib, ws_bytes=64) == 4
+    # the atomic dkv mode needs its fp32 accumulator: a workspace sized for
+    # the deterministic mode is too small for it
+    det = lib.smla_bwd_workspace_size(16, 16, 8, 4, 0)
+    atom = lib.smla_bwd_workspace_size(16, 16, 8, 4, 2)
+    assert atom >= det + 64 * 576 * 4
+    assert call_bwd(lib, flags=2, ws_bytes=det) == 4
 
 
 def test_validate_argument_errors(lib):

@@ -270,3 +270,43 @@ def test_plan_once_path_is_bitwise_identical():
         bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
         for name in ("out", "lse", "dq", "dkv"):
             assert torch.equal(bits(getattr(a, name)), bits(getattr(b, name))), name
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged_dups", "multi_block"])
+def test_atomic_dkv_mode(case):
+    """SMLA_DKV_ATOMIC (fp32 atomic adds of the kv-block partials): dq is the
+    deterministic mode's bit for bit, dkv differs only by the order of fp32
+    additions, matches the oracle, and rows no slot selects stay exact zeros
+    (or keep their sign bit when accumulating)."""
+    import bwd_sparse_mla_amd as smla
+    w = {"tiny": synth.tiny,
+         "ragged_dups": lambda: synth.custom(S=70, H=16, K=96, S_kv=300, seed=21, dup_frac=0.1,
+                                             pad_frac=0.2, empty_frac=0.05),
+         "multi_block": lambda: synth.custom(S=96, H=8, K=512, S_kv=1500, seed=22,
+                                             pad_frac=0.1)}[case]()
+    print(f"[parity] atomic dkv {w.name}", flush=True)
+    q, kv, dout, idx = gpu_inputs(w)
+    out, lse = smla.sparse_mla_fwd(q, kv, idx, w.sm_scale)
+    d32 = torch.empty(w.S_kv, 576, dtype=torch.float32, device="cuda")
+    dq_d, _ = smla.sparse_mla_bwd(q, kv, out, dout, idx, lse, w.sm_scale, dkv_f32=d32)
+    a32 = torch.empty(w.S_kv, 576, dtype=torch.float32, device="cuda")
+    dq_a, dkv_a = smla.sparse_mla_bwd(q, kv, out, dout, idx, lse, w.sm_scale, dkv_f32=a32,
+                                      atomic=True)
+    acc = torch.full((w.S_kv, 576), -0.0, dtype=torch.float32, device="cuda")
+    smla.sparse_mla_bwd(q, kv, out, dout, idx, lse, w.sm_scale, dkv_f32=acc, accumulate=True,
+                        atomic=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq_a, dq_d)
+    scale = float(d32.abs().max())
+    assert float((a32 - d32).abs().max()) <= 1e-5 * max(scale, 1e-30)
+    touched = touched_rows(w.idx, w.S_kv)
+    t_gpu = torch.from_numpy(touched).cuda()
+    assert float(a32[~t_gpu].abs().sum()) == 0.0 and float(dkv_a.float()[~t_gpu].abs().sum()) == 0.0
+    bits = acc.view(torch.int32).cpu().numpy()
+    assert np.array_equal(np.all(bits == np.int32(-2 ** 31), axis=1), ~touched)
+    q64, kv64, do64 = oracle_inputs(w)
+    _, s_dkv = o_bwd(q64, kv64, do64, w.idx, w.sm_scale, out=bf16_to_np64(out),
+                     lse=lse.cpu().numpy().astype(np.float64))
+    err = rel_err(bf16_to_np64(dkv_a), s_dkv)
+    print(f"[parity] atomic dkv {w.name} rel error {err:.3e}", flush=True)
+    assert err <= TOL
