@@ -55,6 +55,8 @@ def parse():
                          "fp32 atomic adds")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel HIP events")
+    ap.add_argument("--no-topk", action="store_true",
+                    help="skip the index-production (top-k) measurement")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (three times) and "
                          "exit: the calibration run for the HBM byte counters")
@@ -100,6 +102,43 @@ def copy_probe(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
+TOPK_S, TOPK_K = 8192, 2048
+
+
+def topk_measure(steps: int):
+    """The index-production step on one causal sequence of TOPK_S tokens,
+    K = TOPK_K, fp32 logits (seeded normal): mean time per call over `steps`
+    calls, and its bytes against HBM.  Rows no longer than K read no logits;
+    a longer row reads its range once, and every row writes K indices."""
+    import torch
+
+    import bwd_sparse_mla_amd as smla
+    from workloads.synth import causal_ranges
+    gen = torch.Generator(device="cuda").manual_seed(20)
+    lg = torch.randn(TOPK_S, TOPK_S, device="cuda", generator=gen, dtype=torch.float32)
+    ks_np, ke_np = causal_ranges([TOPK_S])
+    ks, ke = torch.from_numpy(ks_np).cuda(), torch.from_numpy(ke_np).cuda()
+    out = torch.empty(TOPK_S, TOPK_K, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        smla.topk_indices(lg, ks, ke, TOPK_K, out=out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        smla.topk_indices(lg, ks, ke, TOPK_K, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n = (ke_np - ks_np).astype(np.int64)
+    nbytes = int(4 * n[n > TOPK_K].sum() + 4 * TOPK_S * TOPK_K)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"one causal sequence, S={TOPK_S}, K={TOPK_K}, fp32 logits",
+            "ms": round(ms, 5), "bytes_per_call": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
 def cpu_baseline(w, target_s: float):
@@ -235,6 +274,11 @@ def main():
                 rec["bytes_per_launch"] / (kernels[dom]["avg_ms"] * 1e-3) / 1e9, 1)
         print(f"[bench] kernels {kernels}", file=sys.stderr, flush=True)
 
+    topk = None
+    if not args.no_topk:
+        print("[bench] index production (top-k) ...", file=sys.stderr, flush=True)
+        topk = topk_measure(max(5, args.steps // 2))
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
@@ -262,6 +306,7 @@ def main():
                           "the same steps after the timed region" if timing else None),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "index_topk": topk,
     }
     print(json.dumps(line), flush=True)
 

@@ -1,4 +1,5 @@
-"""DSA sparse-MLA attention (forward and backward) on AMD Instinct MI355X.
+"""DSA sparse-MLA attention (forward and backward) and its index-production
+top-k step on AMD Instinct MI355X.
 
 The computation runs in hand-written HIP kernels for gfx950 behind the C ABI
 of libsmla.so (include/smla.h); this package only marshals arguments.
@@ -6,8 +7,8 @@ of libsmla.so (include/smla.h); this package only marshals arguments.
 from ._lib import SmlaError, load as load_library
 from .ops import (SparseMLA, SparseMLARunner, bwd_workspace_bytes, fwd_workspace_bytes,
                   sparse_mla_bwd, sparse_mla_fwd, timing_read, timing_start, timing_stop,
-                  validate_indices)
+                  topk_indices, validate_indices)
 
 __all__ = ["SmlaError", "SparseMLA", "SparseMLARunner", "bwd_workspace_bytes",
            "fwd_workspace_bytes", "load_library", "sparse_mla_bwd", "sparse_mla_fwd",
-           "timing_read", "timing_start", "timing_stop", "validate_indices"]
+           "timing_read", "timing_start", "timing_stop", "topk_indices", "validate_indices"]

@@ -31,6 +31,7 @@ SIGNATURES = {
                                 _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "smla_bwd_workspace_size": (_SZ, [_I64, _I64, _I32, _I32, ctypes.c_uint32]),
     "smla_validate_indices": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _P]),
+    "smla_topk_indices": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _P]),
     "smla_timing_start": (ctypes.c_int, [ctypes.c_int]),
     "smla_timing_stop": (ctypes.c_int, []),
     "smla_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int),

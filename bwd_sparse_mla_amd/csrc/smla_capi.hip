@@ -337,6 +337,32 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   return hip_status(timed("dkv_finalize", s, [&] { return launch_dkv_finalize(ba, heads, s); }), "dkv_finalize");
 }
 
+int smla_topk_indices(const float* logits, int64_t s_q, int64_t s_kv, int64_t ld,
+                      const int32_t* ks, const int32_t* ke, int32_t topk, int32_t* indices,
+                      void* stream) {
+  g_last_error.clear();
+  if (s_q < 0 || s_kv < 1 || ld < s_kv || topk < 1 || topk > MAX_TOPK)
+    return fail(SMLA_ERR_SHAPE, "need s_q >= 0, s_kv >= 1, ld >= s_kv, 1 <= topk <= 16384");
+  if (s_q > 0 && (!logits || !ks || !ke || !indices)) return fail(SMLA_ERR_NULL, "null pointer");
+  const void* ptrs[] = {logits, ks, ke, indices};
+  for (const void* ptr : ptrs)
+    if ((reinterpret_cast<uintptr_t>(ptr) & 3u) != 0)
+      return fail(SMLA_ERR_ALIGN, "pointers must be 4-byte aligned");
+  int st = check_device();
+  if (st) return st;
+  TopkArgs ta{};
+  ta.logits = logits;
+  ta.s_q = s_q;
+  ta.s_kv = s_kv;
+  ta.ld = ld;
+  ta.ks = ks;
+  ta.ke = ke;
+  ta.topk = topk;
+  ta.out = indices;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(timed("topk", s, [&] { return launch_topk(ta, s); }), "topk");
+}
+
 int smla_validate_indices(const int32_t* indices, int64_t s_q, int32_t topk, int64_t s_kv,
                           unsigned long long* n_bad, void* stream) {
   g_last_error.clear();

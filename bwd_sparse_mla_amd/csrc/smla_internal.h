@@ -95,7 +95,17 @@ struct BwdArgs {
   int accumulate;
 };
 
+struct TopkArgs {
+  const float* logits;   // [s_q, ld] fp32, row s holds the logits of query s over kv rows 0..s_kv-1
+  int64_t s_q, s_kv, ld;
+  const int32_t* ks;     // [s_q] first kv row of each query's range
+  const int32_t* ke;     // [s_q] one past its last
+  int topk;
+  int32_t* out;          // [s_q, topk]
+};
+
 hipError_t launch_fill_u32(void* ptr, size_t n_words, uint32_t value, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream);

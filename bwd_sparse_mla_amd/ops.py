@@ -187,6 +187,26 @@ def validate_indices(indices: torch.Tensor, s_kv: int) -> int:
     return int(cnt.item())
 
 
+def topk_indices(logits: torch.Tensor, ks: torch.Tensor, ke: torch.Tensor, topk: int,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """Index production: int32 [S, topk] top-k kv positions of each query's
+    fp32 indexer logits [S, S_kv] inside its range [ks, ke), k capped at the
+    range length, ascending, padded with -1 (the layout sparse_mla_fwd takes)."""
+    lib = _lib.load()
+    if logits.dim() != 2 or logits.dtype != torch.float32 or logits.stride(1) != 1:
+        raise ValueError("logits must be fp32 [S, S_kv] with contiguous rows")
+    S, S_kv = logits.shape
+    ks = _prep(ks.to(torch.int32), torch.int32, "ks")
+    ke = _prep(ke.to(torch.int32), torch.int32, "ke")
+    if ks.shape != (S,) or ke.shape != (S,):
+        raise ValueError("ks and ke must be [S]")
+    if out is None:
+        out = torch.empty(S, topk, dtype=torch.int32, device=logits.device)
+    _lib.check(lib.smla_topk_indices(_ptr(logits), S, S_kv, logits.stride(0), _ptr(ks), _ptr(ke),
+                                     topk, _ptr(out), _stream(logits.device)))
+    return out
+
+
 class SparseMLA(torch.autograd.Function):
     """out = SparseMLA.apply(q, kv, indices, sm_scale): differentiable in q and kv."""
 

@@ -143,6 +143,23 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
 size_t smla_bwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
                                uint32_t flags);
 
+/* Index production, the step before the attention: for every query row s,
+ * the top-k kv positions of its indexer logits inside its key range
+ * [ks[s], ke[s]) (clipped to [0, s_kv)), with k capped at the range length
+ * and the row padded back to the fixed width topk with -1 -- Megatron-Bridge
+ * PR #17, "GLM-5 DSA option: tilelang (2/2)", Bug fixes.  The chosen
+ * positions are written in ascending order; among equal logits the smaller
+ * position wins.
+ * in:  logits [s_q, ld] fp32 (row s at logits + s * ld; columns 0..s_kv-1
+ *      are read, only inside the row's range; values must be finite);
+ *      ks, ke [s_q] int32 (ke <= ks is an empty range: a row of -1).
+ * out: indices [s_q, topk] int32, ready for smla_fwd / smla_bwd.
+ * Errors: SMLA_ERR_NULL, SMLA_ERR_SHAPE (s_q < 0, s_kv < 1, ld < s_kv, topk
+ * outside 1..16384), SMLA_ERR_ALIGN (pointers must be 4-byte aligned). */
+int smla_topk_indices(const float* logits, int64_t s_q, int64_t s_kv, int64_t ld,
+                      const int32_t* ks, const int32_t* ke, int32_t topk, int32_t* indices,
+                      void* stream);
+
 /* Counts index entries that are neither -1 nor in [0, s_kv) and stores the
  * count in *n_bad (a device pointer to one uint64, overwritten). */
 int smla_validate_indices(const int32_t* indices, int64_t s_q, int32_t topk, int64_t s_kv,

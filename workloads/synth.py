@@ -295,6 +295,18 @@ WORKLOADS = {
 }
 
 
+def causal_ranges(seqlens):
+    """Key ranges [ks, ke) of packed causal sequences (input structure for the
+    index-production step): token p of a sequence starting at row c sees kv
+    rows c .. c + p."""
+    ks, ke, c = [], [], 0
+    for L in seqlens:
+        ks.extend([c] * int(L))
+        ke.extend(range(c + 1, c + int(L) + 1))
+        c += int(L)
+    return np.asarray(ks, dtype=np.int32), np.asarray(ke, dtype=np.int32)
+
+
 def custom(S, H, K, S_kv=None, seed=0, sigma=1.0, pad_frac=0.3, empty_frac=0.1,
            dup_frac=0.0, scatter_pad=True, oob_frac=0.0) -> Workload:
     """Small free-form workload for edge-case tests: random rows of kv (not
