@@ -13,9 +13,13 @@
 //
 // One workgroup per query row.  A row no longer than K is the whole range.  A
 // longer row finds the K-th largest key by an MSB-first radix select over
-// order-preserving 32-bit keys (four 8-bit digits; per-wave LDS histograms),
-// then writes, in position order, every key above it and the first keys equal
-// to it.  The row's keys are read from HBM once and kept in LDS when they fit.
+// order-preserving 32-bit keys (8-bit digits; per-wave LDS histograms), then
+// writes, in position order, every key above it and the first keys equal to
+// it.  The row's logits are read from HBM once, with 16-byte loads several in
+// flight per thread, and their keys kept in LDS when the row fits the cache
+// (sized at launch from s_kv, so short-context launches run several
+// workgroups per CU).  The select stops early once the keys sharing the
+// selected digits are exactly the ones still needed.
 #include "smla_device.h"
 #include "smla_internal.h"
 
@@ -24,7 +28,10 @@ namespace smla {
 namespace {
 
 constexpr int TOPK_THREADS = 256;
-constexpr int TOPK_LDS_KEYS = 32768;   // rows up to this long keep their keys in LDS
+constexpr int TOPK_SMALL_CACHE = 8192;    // keys cached per row when s_kv <= 8192
+constexpr int TOPK_LARGE_CACHE = 32768;   // otherwise rows up to this long are cached
+constexpr int TOPK_LOADS = 8;             // 16-byte loads in flight per thread
+constexpr int TOPK_BATCH = 8;             // keys read ahead per thread in the LDS passes
 
 // Unsigned keys that order like the floats (finite values); -0 and +0 get the
 // same key, as they compare equal.
@@ -34,14 +41,26 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <int CACHE>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
-  __shared__ uint32_t keys[TOPK_LDS_KEYS];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[CACHE + 4];
   __shared__ int hist[4][256];
   __shared__ int scratch[8];
-  __shared__ int s_digit, s_rank;
+  __shared__ int s_digit, s_rank, s_count;
+  __shared__ int s_wave[4][2];
 
   const int64_t s = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = a.topk;
   const int64_t lo = max<int64_t>(0, a.ks[s]);
   const int64_t hi = min<int64_t>(a.s_kv, a.ke[s]);
@@ -54,31 +73,76 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
   }
 
   const float* row = a.logits + s * a.ld + lo;
-  const bool cached = n <= TOPK_LDS_KEYS;
+  const bool cached = n <= CACHE;
+  // Elements before the row's first 16-byte boundary are read one by one;
+  // key i is cached at keys[i + pad], so the body's keys are stored 16 bytes
+  // at a time.
+  const int head = min(n, (int)(((16u - ((uint32_t)reinterpret_cast<uintptr_t>(row) & 15u)) & 15u) >> 2));
+  const int pad = (4 - head) & 3;
   auto key_at = [&](int i) __attribute__((always_inline)) {
-    return cached ? keys[i] : order_key(row[i]);
+    return cached ? keys[i + pad] : order_key(row[i]);
   };
 
+  for (int b = tid; b < 4 * 256; b += TOPK_THREADS) (&hist[0][0])[b] = 0;
+  __syncthreads();
+  // Pass 0 reads the logits: the elements before the first 16-byte boundary
+  // one by one, the body as float4 (TOPK_LOADS per thread in flight), the
+  // tail one by one; each key is cached and counted by its top digit.
+  auto first = [&](int i, float x) __attribute__((always_inline)) {
+    const uint32_t k = order_key(x);
+    if (cached) keys[i + pad] = k;
+    atomicAdd(&hist[wave][k >> 24], 1);
+  };
+  if (tid < head) first(tid, row[tid]);
+  const int nv4 = (n - head) >> 2;
+  const float4* row4 = reinterpret_cast<const float4*>(row + head);
+  for (int base = 0; base < nv4; base += TOPK_LOADS * TOPK_THREADS) {
+    float4 v[TOPK_LOADS];
+#pragma unroll
+    for (int j = 0; j < TOPK_LOADS; ++j) {
+      const int i = base + j * TOPK_THREADS + tid;
+      v[j] = i < nv4 ? row4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < TOPK_LOADS; ++j) {
+      const int i = base + j * TOPK_THREADS + tid;
+      if (i < nv4) {
+        const uint4 k = make_uint4(order_key(v[j].x), order_key(v[j].y), order_key(v[j].z),
+                                   order_key(v[j].w));
+        if (cached) *reinterpret_cast<uint4*>(&keys[head + pad + 4 * i]) = k;
+        atomicAdd(&hist[wave][k.x >> 24], 1);
+        atomicAdd(&hist[wave][k.y >> 24], 1);
+        atomicAdd(&hist[wave][k.z >> 24], 1);
+        atomicAdd(&hist[wave][k.w >> 24], 1);
+      }
+    }
+  }
+  for (int i = head + 4 * nv4 + tid; i < n; i += TOPK_THREADS) first(i, row[i]);
+
   // Radix select: after the pass for digit d, `prefix` holds the K-th largest
-  // key's digits above and at d, and `rank` its rank (1-based, from the top)
-  // among the keys that share them.
+  // key's digits above and at d (`pmask` marks them), and `rank` its rank
+  // (1-based, from the top) among the keys that share them.  When exactly
+  // `rank` keys share them, every one is taken and the select stops.
   uint32_t prefix = 0, pmask = 0;
   int rank = K;
 #pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int b = tid; b < 4 * 256; b += TOPK_THREADS) (&hist[0][0])[b] = 0;
-    __syncthreads();
-    if (pass == 0) {
-      for (int i = tid; i < n; i += TOPK_THREADS) {
-        const uint32_t k = order_key(row[i]);
-        if (cached) keys[i] = k;
-        atomicAdd(&hist[wave][k >> 24], 1);
-      }
-    } else {
-      for (int i = tid; i < n; i += TOPK_THREADS) {
-        const uint32_t k = key_at(i);
-        if ((k & pmask) == prefix) atomicAdd(&hist[wave][(k >> shift) & 255u], 1);
+    if (pass > 0) {
+      for (int b = tid; b < 4 * 256; b += TOPK_THREADS) (&hist[0][0])[b] = 0;
+      __syncthreads();
+      for (int base = 0; base < n; base += TOPK_BATCH * TOPK_THREADS) {
+        uint32_t k[TOPK_BATCH];
+#pragma unroll
+        for (int j = 0; j < TOPK_BATCH; ++j) {
+          const int i = base + j * TOPK_THREADS + tid;
+          k[j] = i < n ? key_at(i) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < TOPK_BATCH; ++j) {
+          const int i = base + j * TOPK_THREADS + tid;
+          if (i < n && (k[j] & pmask) == prefix) atomicAdd(&hist[wave][(k[j] >> shift) & 255u], 1);
+        }
       }
     }
     __syncthreads();
@@ -91,38 +155,71 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
     if (above < rank && rank <= above + c) {
       s_digit = d;
       s_rank = rank - above;
+      s_count = c;
     }
     __syncthreads();
     prefix |= (uint32_t)s_digit << shift;
     pmask |= 255u << shift;
     rank = s_rank;
+    const bool done = s_count == rank;
     __syncthreads();
+    if (done) break;
   }
 
-  // prefix is now the K-th largest key T: the K - rank keys above it and the
-  // first `rank` keys equal to it (in position order) are the selection.
-  const uint32_t T = prefix;
-  const int C = (n + TOPK_THREADS - 1) / TOPK_THREADS;   // positions per thread, contiguous
-  const int b0 = min(n, tid * C), b1 = min(n, b0 + C);
+  // The selection: keys whose selected digits exceed the prefix, and the
+  // first `rank` keys (in position order) whose digits equal it.  Wave w
+  // writes positions [q0, q1), a quarter of the row, in 64-key chunks.
+  const int qlen = (n + 3) / 4;
+  const int q0 = min(n, wave * qlen), q1 = min(n, q0 + qlen);
   int gt = 0, eq = 0;
-  for (int i = b0; i < b1; ++i) {
-    const uint32_t k = key_at(i);
-    gt += k > T;
-    eq += k == T;
-  }
-  int eq_total;
-  const int eq_before = block_exclusive_scan256(eq, scratch, &eq_total);
-  int take_eq = min(eq, max(0, rank - eq_before));
-  int total_sel;
-  int pos = block_exclusive_scan256(gt + take_eq, scratch, &total_sel);
-  for (int i = b0; i < b1; ++i) {
-    const uint32_t k = key_at(i);
-    bool take = k > T;
-    if (k == T && take_eq > 0) {
-      take = true;
-      --take_eq;
+  for (int base = q0; base < q1; base += TOPK_BATCH * 64) {
+    uint32_t k[TOPK_BATCH];
+#pragma unroll
+    for (int j = 0; j < TOPK_BATCH; ++j) {
+      const int i = base + 64 * j + lane;
+      k[j] = i < q1 ? key_at(i) & pmask : 0u;
     }
-    if (take && pos < K) out[pos++] = (int32_t)(lo + i);   // pos < K always: the counts sum to K
+#pragma unroll
+    for (int j = 0; j < TOPK_BATCH; ++j) {
+      const int i = base + 64 * j + lane;
+      gt += i < q1 && k[j] > prefix;
+      eq += i < q1 && k[j] == prefix;
+    }
+  }
+  gt = wave_sum(gt);
+  eq = wave_sum(eq);
+  if (lane == 0) {
+    s_wave[wave][0] = gt;
+    s_wave[wave][1] = eq;
+  }
+  __syncthreads();
+  int pos = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    const int take = min(s_wave[w][1], max(0, rank - eq_before));
+    pos += s_wave[w][0] + take;
+    eq_before += s_wave[w][1];
+  }
+  int eq_left = min(eq, max(0, rank - eq_before));
+  for (int base = q0; base < q1; base += TOPK_BATCH * 64) {
+    uint32_t k[TOPK_BATCH];
+#pragma unroll
+    for (int j = 0; j < TOPK_BATCH; ++j) {
+      const int i = base + 64 * j + lane;
+      k[j] = i < q1 ? key_at(i) & pmask : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < TOPK_BATCH; ++j) {
+      const int i = base + 64 * j + lane;
+      const bool in = i < q1;
+      const bool g = in && k[j] > prefix, e = in && k[j] == prefix;
+      const unsigned long long me = __ballot(e);
+      const bool take = g || (e && lanes_below(me) < eq_left);
+      const unsigned long long mt = __ballot(take);
+      const int p = pos + lanes_below(mt);
+      if (take && p < K) out[p] = (int32_t)(lo + i);   // p < K always: the counts sum to K
+      pos += __popcll(mt);
+      eq_left -= min(eq_left, __popcll(me));
+    }
   }
 }
 
@@ -130,7 +227,10 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.s_q == 0) return hipSuccess;
-  topk_kernel<<<dim3((unsigned)a.s_q), dim3(TOPK_THREADS), 0, stream>>>(a);
+  if (a.s_kv <= TOPK_SMALL_CACHE)
+    topk_kernel<TOPK_SMALL_CACHE><<<dim3((unsigned)a.s_q), dim3(TOPK_THREADS), 0, stream>>>(a);
+  else
+    topk_kernel<TOPK_LARGE_CACHE><<<dim3((unsigned)a.s_q), dim3(TOPK_THREADS), 0, stream>>>(a);
   return hipGetLastError();
 }
 

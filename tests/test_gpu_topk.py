@@ -78,6 +78,33 @@ def test_rows_longer_than_the_lds_cache():
     np.testing.assert_array_equal(got, o_topk(logits, ks, ke, K))
 
 
+def test_small_k_every_alignment():
+    """K = 1, 2, 3 over short rows starting at every offset mod 4 (the kernel
+    reads each row's unaligned head one by one, the body as 16-byte loads)."""
+    rng = np.random.default_rng(9)
+    S, S_kv = 96, 37
+    logits = rng.standard_normal((S, S_kv)).astype(np.float32)
+    logits[::7] = np.round(logits[::7])                 # some rows with ties
+    ks = (np.arange(S) % 8).astype(np.int32)
+    ke = np.minimum(S_kv, ks + 2 + (np.arange(S) // 8) % 9).astype(np.int32)
+    for K in (1, 2, 3):
+        print(f"[topk] small K={K} S={S} S_kv={S_kv}", flush=True)
+        got = _gpu_topk(logits, ks, ke, K)
+        np.testing.assert_array_equal(got, o_topk(logits, ks, ke, K))
+
+
+def test_rows_between_the_two_cache_sizes():
+    """S_kv just past 8192: rows of 8193..9000 keys use the larger LDS cache."""
+    rng = np.random.default_rng(10)
+    S, S_kv, K = 6, 9000, 2048
+    logits = rng.standard_normal((S, S_kv)).astype(np.float32)
+    ks = np.array([0, 1, 2, 3, 0, 500], dtype=np.int32)
+    ke = np.array([9000, 8194, 9000, 8999, 8192, 9000], dtype=np.int32)
+    print(f"[topk] medium rows S_kv={S_kv} K={K}", flush=True)
+    got = _gpu_topk(logits, ks, ke, K)
+    np.testing.assert_array_equal(got, o_topk(logits, ks, ke, K))
+
+
 def test_indices_feed_the_attention():
     """topk -> sparse_mla_fwd equals the oracle's forward on the oracle's
     selection (packed causal sequences, rows shorter and longer than K)."""
