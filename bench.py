@@ -141,6 +141,40 @@ def topk_measure(steps: int):
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def nonfinite_measure(run, steps: int):
+    """The finite check of the backward's outputs: NaN / Inf counted over dq
+    and dkv of the step just run (one counter, two launches per check), mean
+    time per check and its bytes against HBM (each buffer read once)."""
+    import torch
+
+    import bwd_sparse_mla_amd as smla
+    cnt = torch.zeros(1, dtype=torch.int64, device=run.dq.device)
+
+    def check():
+        smla.count_nonfinite(run.dq, cnt)
+        smla.count_nonfinite(run.dkv, cnt)
+
+    for _ in range(3):
+        check()
+    torch.cuda.synchronize()
+    cnt.zero_()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        check()
+    e1.record()
+    torch.cuda.synchronize()
+    if int(cnt.item()) != 0:
+        raise RuntimeError("nonfinite entries in dq / dkv")
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = run.dq.numel() * run.dq.element_size() + run.dkv.numel() * run.dkv.element_size()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"what": "NaN/Inf count over dq and dkv", "ms": round(ms, 5), "bytes_per_check": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def cpu_baseline(w, target_s: float):
     """The fp64 oracle as it stands, on a seeded sample of tokens of the same
     workload (their forward + backward, dkv scattered into the full kv)."""
@@ -274,6 +308,9 @@ def main():
                 rec["bytes_per_launch"] / (kernels[dom]["avg_ms"] * 1e-3) / 1e9, 1)
         print(f"[bench] kernels {kernels}", file=sys.stderr, flush=True)
 
+    print("[bench] finite check of dq / dkv ...", file=sys.stderr, flush=True)
+    finite = nonfinite_measure(run, max(10, args.steps))
+
     topk = None
     if not args.no_topk:
         print("[bench] index production (top-k) ...", file=sys.stderr, flush=True)
@@ -307,6 +344,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "index_topk": topk,
+        "nonfinite_check": finite,
     }
     print(json.dumps(line), flush=True)
 

@@ -10,6 +10,8 @@ SMLA_OK = 0
 SMLA_DKV_ACCUMULATE = 1
 SMLA_DKV_ATOMIC = 2
 SMLA_PLAN_READY = 4
+SMLA_DTYPE_BF16 = 0
+SMLA_DTYPE_F32 = 1
 
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_ALIGN",
                 4: "SMLA_ERR_WORKSPACE", 5: "SMLA_ERR_FLAGS", 6: "SMLA_ERR_HIP",
@@ -31,6 +33,8 @@ SIGNATURES = {
                                 _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "smla_bwd_workspace_size": (_SZ, [_I64, _I64, _I32, _I32, ctypes.c_uint32]),
     "smla_validate_indices": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _P]),
+    "smla_nonfinite_count": (ctypes.c_int, [_P, _I32, _I64, _P, _P]),
+    "smla_nonfinite_replace": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _P]),
     "smla_topk_indices": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _P]),
     "smla_timing_start": (ctypes.c_int, [ctypes.c_int]),
     "smla_timing_stop": (ctypes.c_int, []),

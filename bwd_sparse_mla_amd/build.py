@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsmla.so")
-SOURCES = ["smla_plan.hip", "smla_fwd.hip", "smla_bwd.hip", "smla_topk.hip", "smla_capi.hip"]
+SOURCES = ["smla_plan.hip", "smla_fwd.hip", "smla_bwd.hip", "smla_topk.hip", "smla_diag.hip", "smla_capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -363,6 +363,41 @@ int smla_topk_indices(const float* logits, int64_t s_q, int64_t s_kv, int64_t ld
   return hip_status(timed("topk", s, [&] { return launch_topk(ta, s); }), "topk");
 }
 
+static int nonfinite_call(void* x, const void* ref, int32_t dtype, int64_t n, unsigned long long* count,
+                          bool replace, void* stream) {
+  g_last_error.clear();
+  if (dtype != SMLA_DTYPE_BF16 && dtype != SMLA_DTYPE_F32)
+    return fail(SMLA_ERR_SHAPE, "dtype must be SMLA_DTYPE_BF16 or SMLA_DTYPE_F32");
+  if (n < 0) return fail(SMLA_ERR_SHAPE, "n must be >= 0");
+  if (!count) return fail(SMLA_ERR_NULL, "count is null");
+  if (n > 0 && !x) return fail(SMLA_ERR_NULL, "x is null");
+  if ((reinterpret_cast<uintptr_t>(count) & 7u) != 0)
+    return fail(SMLA_ERR_ALIGN, "count must be 8-byte aligned");
+  if (!aligned16(x) || !aligned16(ref)) return fail(SMLA_ERR_ALIGN, "x and ref must be 16-byte aligned");
+  const int es = dtype == SMLA_DTYPE_BF16 ? 2 : 4;
+  if (replace && ref && ref != x) {
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(x), rb = reinterpret_cast<uintptr_t>(ref);
+    const uintptr_t bytes = (uintptr_t)n * es;
+    if (xb < rb + bytes && rb < xb + bytes) return fail(SMLA_ERR_SHAPE, "ref overlaps x");
+  }
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(timed(replace ? "nonfinite_replace" : "nonfinite_count", s,
+                          [&] { return launch_nonfinite(x, ref, n, es, replace, count, s); }),
+                    "nonfinite");
+}
+
+int smla_nonfinite_count(const void* x, int32_t dtype, int64_t n, unsigned long long* count,
+                         void* stream) {
+  return nonfinite_call(const_cast<void*>(x), nullptr, dtype, n, count, false, stream);
+}
+
+int smla_nonfinite_replace(void* x, const void* ref, int32_t dtype, int64_t n,
+                           unsigned long long* count, void* stream) {
+  return nonfinite_call(x, ref, dtype, n, count, true, stream);
+}
+
 int smla_validate_indices(const int32_t* indices, int64_t s_q, int32_t topk, int64_t s_kv,
                           unsigned long long* n_bad, void* stream) {
   g_last_error.clear();

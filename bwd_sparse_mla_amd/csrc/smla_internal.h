@@ -121,6 +121,11 @@ hipError_t launch_dkv_finalize(const BwdArgs& a, int heads, hipStream_t stream);
 // equal share of all sub-chunks in block order (stream-K style); a workgroup
 // w that covers sub-chunks of block b leaves its partial in slot w + b.
 constexpr int DKV_WGS = 256;
+// Nonfinite diagnostics over n elements of es (2: bf16, 4: fp32) bytes at
+// x: count the NaN / Inf entries, or replace them from ref (null: zero);
+// the count is added into *count.
+hipError_t launch_nonfinite(void* x, const void* ref, int64_t n, int es, bool replace,
+                            unsigned long long* count, hipStream_t stream);
 hipError_t launch_validate(const int32_t* idx, int64_t n, int64_t s_kv,
                            unsigned long long* n_bad, hipStream_t stream);
 

@@ -207,6 +207,92 @@ def topk_indices(logits: torch.Tensor, ks: torch.Tensor, ke: torch.Tensor, topk:
     return out
 
 
+_DIAG_DTYPES = {torch.bfloat16: _lib.SMLA_DTYPE_BF16, torch.float32: _lib.SMLA_DTYPE_F32}
+
+
+def _diag_operand(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype not in _DIAG_DTYPES:
+        raise TypeError(f"{name} must be bf16 or fp32, got {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    return t
+
+
+def _counter(counter: torch.Tensor | None, device) -> torch.Tensor:
+    if counter is None:
+        return torch.zeros(1, dtype=torch.int64, device=device)
+    if counter.dtype != torch.int64 or counter.numel() < 1 or not counter.is_cuda:
+        raise ValueError("counter must be an int64 GPU tensor")
+    return counter
+
+
+def count_nonfinite(t: torch.Tensor, counter: torch.Tensor | None = None) -> int | None:
+    """Number of NaN / Inf entries of a contiguous bf16 or fp32 GPU tensor.
+    With `counter` (an int64 GPU tensor), the count is added into counter[0]
+    without synchronizing and None is returned; without it, the call waits
+    for the count and returns it."""
+    lib = _lib.load()
+    t = _diag_operand(t, "t")
+    c = _counter(counter, t.device)
+    _lib.check(lib.smla_nonfinite_count(_ptr(t), _DIAG_DTYPES[t.dtype], t.numel(), _ptr(c),
+                                        _stream(t.device)))
+    return None if counter is not None else int(c.item())
+
+
+def replace_nonfinite_(t: torch.Tensor, ref: torch.Tensor | None = None,
+                       counter: torch.Tensor | None = None) -> int | None:
+    """In place: every NaN / Inf entry of `t` takes the value of the same
+    entry of `ref` (zero when ref is None); other entries are untouched.
+    Returns the number replaced (or adds it into `counter`, as in
+    count_nonfinite)."""
+    lib = _lib.load()
+    t = _diag_operand(t, "t")
+    if ref is not None:
+        ref = _diag_operand(ref, "ref")
+        if ref.dtype != t.dtype or ref.shape != t.shape:
+            raise ValueError("ref must match t in dtype and shape")
+    c = _counter(counter, t.device)
+    _lib.check(lib.smla_nonfinite_replace(_ptr(t), _ptr(ref), _DIAG_DTYPES[t.dtype], t.numel(),
+                                          _ptr(c), _stream(t.device)))
+    return None if counter is not None else int(c.item())
+
+
+class NonfiniteGradientError(RuntimeError):
+    """sparse_mla_bwd_checked found NaN / Inf in dq or dkv."""
+
+
+def sparse_mla_bwd_checked(q, kv, out, dout, indices, lse, sm_scale, reference=None,
+                           on_nonfinite: str = "raise"):
+    """The backward with the finite check of the pages' fallback workflow:
+    run sparse_mla_bwd, count NaN / Inf in dq and dkv on the device (one read
+    back for both), and if there are any, either take the values of a
+    caller-supplied `reference(q, kv, out, dout, indices, lse, sm_scale) ->
+    (dq_ref, dkv_ref)` at those entries only, or (no reference) raise
+    NonfiniteGradientError (on_nonfinite="raise") or write zeros there
+    (on_nonfinite="zero", a diagnostic confinement, not a fix).
+    Returns (dq, dkv, {"dq": n, "dkv": n, "replaced": n})."""
+    if on_nonfinite not in ("raise", "zero"):
+        raise ValueError("on_nonfinite must be 'raise' or 'zero'")
+    dq, dkv = sparse_mla_bwd(q, kv, out, dout, indices, lse, sm_scale)
+    cnt = torch.zeros(2, dtype=torch.int64, device=dq.device)
+    count_nonfinite(dq, cnt[0:1])
+    count_nonfinite(dkv, cnt[1:2])
+    n_dq, n_dkv = (int(v) for v in cnt.tolist())
+    info = {"dq": n_dq, "dkv": n_dkv, "replaced": 0}
+    if n_dq + n_dkv == 0:
+        return dq, dkv, info
+    if reference is not None:
+        dq_ref, dkv_ref = reference(q, kv, out, dout, indices, lse, sm_scale)
+        dq_ref = dq_ref.to(dq.dtype).reshape(dq.shape).contiguous()
+        dkv_ref = dkv_ref.to(dkv.dtype).reshape(dkv.shape).contiguous()
+    elif on_nonfinite == "raise":
+        raise NonfiniteGradientError(f"nonfinite entries: dq {n_dq}, dkv {n_dkv}")
+    else:
+        dq_ref = dkv_ref = None
+    info["replaced"] = replace_nonfinite_(dq, dq_ref) + replace_nonfinite_(dkv, dkv_ref)
+    return dq, dkv, info
+
+
 class SparseMLA(torch.autograd.Function):
     """out = SparseMLA.apply(q, kv, indices, sm_scale): differentiable in q and kv."""
 

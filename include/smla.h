@@ -160,6 +160,31 @@ int smla_topk_indices(const float* logits, int64_t s_q, int64_t s_kv, int64_t ld
                       const int32_t* ks, const int32_t* ke, int32_t topk, int32_t* indices,
                       void* stream);
 
+/* Nonfinite diagnostics: the device-side steps of the finite-check workflow
+ * of slime issue #2201, "GLM-5.2 SparseMLA TileLang backward returns NaN
+ * gradients from finite inputs", Workarounds tested (check the backward's dq /
+ * dkv for NaN / Inf; when some are found, take a reference's values at those
+ * entries only; writing zeros there instead was the diagnostic confinement
+ * patch).  An entry is nonfinite when all its exponent bits are ones.
+ *
+ * dtype: SMLA_DTYPE_BF16 (2-byte elements) or SMLA_DTYPE_F32 (4-byte).
+ * x, ref: n elements, device memory, 16-byte aligned.  count: a device
+ * pointer to one uint64, 8-byte aligned; the number of nonfinite entries
+ * found (count) or replaced (replace) is ADDED to *count, so one zeroed
+ * counter can gather several buffers before a single read back.
+ * smla_nonfinite_replace writes ref[i] into x[i] wherever x[i] is nonfinite
+ * (ref NULL: +0) and leaves every other entry untouched; ref must not
+ * overlap x except as the same buffer.  The library computes no reference:
+ * the caller supplies one.
+ * Errors: SMLA_ERR_NULL, SMLA_ERR_SHAPE (n < 0, unknown dtype),
+ * SMLA_ERR_ALIGN. */
+#define SMLA_DTYPE_BF16 0
+#define SMLA_DTYPE_F32 1
+int smla_nonfinite_count(const void* x, int32_t dtype, int64_t n, unsigned long long* count,
+                         void* stream);
+int smla_nonfinite_replace(void* x, const void* ref, int32_t dtype, int64_t n,
+                           unsigned long long* count, void* stream);
+
 /* Counts index entries that are neither -1 nor in [0, s_kv) and stores the
  * count in *n_bad (a device pointer to one uint64, overwritten). */
 int smla_validate_indices(const int32_t* indices, int64_t s_q, int32_t topk, int64_t s_kv,

@@ -130,3 +130,18 @@ def test_plan_and_fwd_ex_argument_errors(lib):
     assert lib.smla_fwd_ex(*args, 8, P(FAKE), fws, P(0)) == 5                  # unknown flag
     assert lib.smla_fwd_ex(*args, 4, P(FAKE), 64, P(0)) == 4                   # workspace
     assert call_bwd(lib, flags=16) == 5
+
+
+def test_nonfinite_argument_errors(lib):
+    P = ctypes.c_void_p
+    cnt = P(FAKE)
+    assert lib.smla_nonfinite_count(P(FAKE), 2, 8, cnt, P(0)) == 2              # unknown dtype
+    assert lib.smla_nonfinite_count(P(FAKE), 0, -1, cnt, P(0)) == 2             # negative size
+    assert lib.smla_nonfinite_count(P(FAKE), 0, 8, P(0), P(0)) == 1             # null counter
+    assert lib.smla_nonfinite_count(P(0), 1, 8, cnt, P(0)) == 1                 # null buffer
+    assert lib.smla_nonfinite_count(P(FAKE + 8), 1, 8, cnt, P(0)) == 3          # 16-byte alignment
+    assert lib.smla_nonfinite_count(P(FAKE), 1, 8, P(FAKE + 4), P(0)) == 3      # counter alignment
+    assert lib.smla_nonfinite_replace(P(FAKE), P(FAKE + 8), 0, 8, cnt, P(0)) == 3
+    # a reference that overlaps the buffer (other than the buffer itself) is refused
+    assert lib.smla_nonfinite_replace(P(FAKE), P(FAKE + 16), 1, 64, cnt, P(0)) == 2
+    assert b"overlaps" in lib.smla_last_error()

@@ -343,3 +343,27 @@ def custom(S, H, K, S_kv=None, seed=0, sigma=1.0, pad_frac=0.3, empty_frac=0.1,
         idx[m] = bad[m].astype(np.int32)
     return Workload(f"custom_s{S}_h{H}_k{K}_skv{S_kv}_seed{seed}", q, kv, dout, idx,
                     SM_SCALE, [S], seed)
+
+
+def planted_nonfinite(n: int, dtype: str, frac: float = 0.01, seed: int = 0):
+    """Input for the nonfinite diagnostics: n finite normal values (bf16 or
+    fp32 bits) with a seeded fraction replaced by NaN / Inf bit patterns of
+    every kind (quiet and signalling NaN of both signs, +-Inf), and a finite
+    reference of the same shape.  Returns (bits, ref_bits)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(n).astype(np.float32)
+    r = rng.standard_normal(n).astype(np.float32)
+    if dtype == "bf16":
+        bits, ref = f32_to_bf16_bits(x), f32_to_bf16_bits(r)
+        specials = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7F81, 0xFFFF, 0x7FFF], dtype=np.uint16)
+    elif dtype == "f32":
+        bits, ref = x.view(np.uint32).copy(), r.view(np.uint32).copy()
+        specials = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00000, 0x7F800001,
+                             0xFFFFFFFF, 0x7FFFFFFF], dtype=np.uint32)
+    else:
+        raise ValueError("dtype must be 'bf16' or 'f32'")
+    k = int(round(frac * n))
+    if k:
+        pos = rng.choice(n, size=k, replace=False)
+        bits[pos] = specials[rng.integers(0, len(specials), k)]
+    return bits, ref
