@@ -2,7 +2,10 @@
 
 One step = the index plan (built once: forward and backward take the same
 indices), the forward and the backward (dq pass, dkv pass) over the whole
-workload, inputs resident in HBM.  The default workload
+workload, inputs resident in HBM.  The backward runs in its stored-P form
+(the dq pass stores P and scale * dS, the dkv pass reads them: one recompute
+of the scores per backward); --dkv-scores recompute selects the form whose
+dkv pass recomputes them.  The default workload
 is the packed ragged batch: S=4096 tokens as sequences {512, 1024, 1536,
 1024}, H=8 heads, topk=2048 full causal rows (2,361,344 valid pairs).
 
@@ -37,6 +40,7 @@ FLOPS_PER_PAIR_HEAD = {
     "bwd_dq": 2 * (576 + 512 + 576),         # recomputed scores, dP, dQ
     "bwd_dkv": 2 * (576 + 512 + 576 + 512),  # recomputed scores, dP, dK, dV
 }
+FLOPS_STORED_DKV = 2 * (576 + 512)          # dK, dV only (stored-P backward)
 USEFUL_PER_PAIR_HEAD = 7680                  # fwd 2176 + bwd 5504 (one recompute)
 
 
@@ -53,6 +57,9 @@ def parse():
     ap.add_argument("--dkv-mode", default="deterministic", choices=["deterministic", "atomic"],
                     help="dkv reduction: the bitwise-reproducible per-row reduction (default) or "
                          "fp32 atomic adds")
+    ap.add_argument("--dkv-scores", default="stored", choices=["stored", "recompute"],
+                    help="dkv pass: read P and scale * dS stored by the dq pass (default: one "
+                         "recompute of the scores per backward) or recompute the scores and dP")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel HIP events")
     ap.add_argument("--no-topk", action="store_true",
@@ -238,7 +245,8 @@ def main():
         torch.bfloat16).to(dev)
     q, kv, dout = to_bf16(w.q), to_bf16(w.kv), to_bf16(w.dout)
     idx = torch.from_numpy(np.ascontiguousarray(w.idx)).to(dev)
-    run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, dev, dkv_atomic=args.dkv_mode == "atomic")
+    run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, dev, dkv_atomic=args.dkv_mode == "atomic",
+                               dkv_stored_p=args.dkv_scores == "stored")
     run._check(q, kv, idx, dout)
 
     def step():
@@ -295,7 +303,10 @@ def main():
                 kernels[name] = {"launches": n, "avg_ms": tot / n}
         dom = max((k for k in kernels if k in FLOPS_PER_PAIR_HEAD),
                   key=lambda k: kernels[k]["avg_ms"])
-        flops = FLOPS_PER_PAIR_HEAD[dom] * w.H * nv
+        per_pair = FLOPS_PER_PAIR_HEAD[dom]
+        if dom == "bwd_dkv" and args.dkv_scores == "stored":
+            per_pair = FLOPS_STORED_DKV   # P and dS come from the dq pass
+        flops = per_pair * w.H * nv
         ach = flops / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
         rec = recorded_traffic(dom, w.name)
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
@@ -336,7 +347,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "S": w.S, "S_kv": w.S_kv, "H": w.H, "topk": w.K,
                    "seqlens": w.seqlens, "valid_pairs": nv, "useful_gflop": useful / 1e9,
-                   "parallelism": "none (one GPU)", "dkv_mode": args.dkv_mode},
+                   "parallelism": "none (one GPU)", "dkv_mode": args.dkv_mode,
+                   "dkv_scores": args.dkv_scores},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
         "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kernels.items()},
         "kernel_timing": ("per-launch HIP events on the library's stream, in a second pass of "

@@ -193,17 +193,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const unsigned mk = *reinterpret_cast<const unsigned*>(mkb + nt * 16 + 4 * g16);
-      float d[4];
+      float d[4], pr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool v = (mk >> (8 * i + tl)) & 1u;
-        const float p = v ? fast_exp2(s[nt][i] * a.scale_log2 - ls2) : 0.f;
-        d[i] = p * (dp[nt][i] - del);
+        pr[i] = v ? fast_exp2(s[nt][i] * a.scale_log2 - ls2) : 0.f;
+        d[i] = pr[i] * (dp[nt][i] - del);
       }
       uint2 pk;
       pk.x = pack_bf2(d[0], d[1]);
       pk.y = pack_bf2(d[2], d[3]);
       *reinterpret_cast<uint2*>(&sdS[(16 * wave + r16) * SDS + nt * 16 + 4 * g16]) = pk;
+      if (a.pds) {
+        // Stored-P mode: P and scale * dS of the lane's row for its four
+        // entries, for the dkv pass ([group, entry, {P, dS}, 64 rows] bf16).
+        uint16_t* dst = a.pds + ((grp * a.qcap + tile * DQ_TILE + nt * 16 + 4 * g16) * 2) * GROUP_ROWS +
+                        16 * wave + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dst[i * 2 * GROUP_ROWS] = f2bf(pr[i]);
+          dst[i * 2 * GROUP_ROWS + GROUP_ROWS] = f2bf(d[i] * a.scale);
+        }
+      }
     }
     __syncthreads();
     short8_t dsa[4];
@@ -519,10 +530,162 @@ __device__ __forceinline__ void dkv_segment(const BwdArgs& a, int64_t blk, int u
   if (tid == 0) a.ptouch[slot] = touched;
 }
 
+// Stored-P form of a segment (SMLA_DKV_STORED_P): the dq pass has left P and
+// scale * dS of every (union entry, query row) in the workspace, so a step
+// only stages the sub-chunk's 64 x 32 P^T / dS^T tiles from there (thread t
+// takes kv row t / 8 of the block and 8 query rows of P or dS: the union
+// entry of a selected row is the chunk's first entry plus the selected rows
+// before it; other rows are zero) and runs the dK / dV contraction -- no
+// scores, no dP, no lse / delta / mask copies.  Per step: wait for the
+// copies, stage P^T / dS^T, issue the next sub-chunk's copies (Q, dout into
+// the other buffers; its P / dS piece into registers), sync, contract.
+template <int H>
+__device__ __forceinline__ void dkv_segment_pds(const BwdArgs& a, int64_t blk, int u0, int u1, int64_t slot,
+                                                DkvLds& lds) {
+  constexpr int SP = DKV_SP;
+  auto& sQ = lds.sQ;
+  auto& sD = lds.sD;
+  auto& sPT = lds.sPT;
+  auto& sDST = lds.sDST;
+  const int tid = threadIdx.x, lane_id = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = a.nchunk[blk];
+  const int64_t kb0 = blk * TILE_KV;
+  const int64_t qrows = a.s_q * H;
+  const int drh = wv & 1, dcq = wv >> 1;
+  float4_t acc[2][9];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  unsigned long long touched = 0ull;
+
+  // Chunk c of the block: group, first union entry in the block, row mask.
+  const int64_t cb = blk * a.G;
+  struct Chunk {
+    int g, e0;
+    unsigned long long m;
+  };
+  auto chunk = [&](int c) __attribute__((always_inline)) {
+    Chunk ch;   // wave-uniform values (scalar registers)
+    ch.g = __builtin_amdgcn_readfirstlane(a.clist[cb + c].x);
+    ch.e0 = __builtin_amdgcn_readfirstlane(a.cbase[cb + c]);
+    const unsigned long long m = a.cmask[cb + c];
+    // (readfirstlane returns int: widen through unsigned, not by sign extension)
+    ch.m = (unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)m) |
+           ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)(m >> 32)) << 32);
+    return ch;
+  };
+  Chunk c_cur = chunk(u0 >> 1);                       // chunk of the current sub-chunk
+  Chunk c_nxt = chunk(min((u0 >> 1) + 1, nch - 1));   // the chunk after it
+
+  const int pr_row = tid >> 3, pr_part = tid & 7;
+  auto pds_load = [&](int g, int e0, unsigned long long m, int half) __attribute__((always_inline)) {
+    short8_t v = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
+    if ((m >> pr_row) & 1ull) {
+      const int e = min(e0 + __popcll(m & ((1ull << pr_row) - 1ull)), (int)a.qcap - 1);
+      v = ld16_global(a.pds + ((int64_t)g * a.qcap + e) * (2 * GROUP_ROWS) +
+                      (pr_part >> 2) * GROUP_ROWS + DKV_SUB * half + 8 * (pr_part & 3));
+    }
+    return v;
+  };
+  auto copies = [&](int g, int u, char* nq, char* nd, int lane) __attribute__((always_inline)) {
+    const int64_t row0 = (int64_t)g * GROUP_ROWS + DKV_SUB * (u & 1);
+    const int nvalid = (int)max((int64_t)0, min((int64_t)DKV_SUB, qrows - row0));
+    gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW>(nq, a.q + row0 * D_K, nvalid, wv, lane);
+    gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW>(nd, a.dout + row0 * D_V, nvalid, wv, lane);
+  };
+
+  copies(c_cur.g, u0, sQ[0], sD[0], lane_id);
+  short8_t piece = pds_load(c_cur.g, c_cur.e0, c_cur.m, u0 & 1);
+  for (int u = u0; u < u1; ++u) {
+    const int b = (u - u0) & 1;
+    const char* sq = sQ[b];
+    const char* sd = sD[b];
+    wait_vmcnt0();
+    __syncthreads();
+    *reinterpret_cast<short8_t*>((pr_part < 4 ? sPT : sDST) + pr_row * SP + 8 * (pr_part & 3)) = piece;
+    touched |= c_cur.m;
+    if (u + 1 < u1) {   // the next sub-chunk: its P / dS piece and its Q / dout copies
+      int lane = lane_id;
+      asm volatile("" : "+v"(lane));   // offsets recomputed per sub-chunk, not kept live
+      const bool adv = (u & 1) != 0;
+      const int gn = adv ? c_nxt.g : c_cur.g;
+      const int en = adv ? c_nxt.e0 : c_cur.e0;
+      const unsigned long long mn = adv ? c_nxt.m : c_cur.m;
+      copies(gn, u + 1, sQ[b ^ 1], sD[b ^ 1], lane);
+      piece = pds_load(gn, en, mn, (u + 1) & 1);
+    }
+    __syncthreads();
+
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int g16 = lane >> 4, r16 = lane & 15;
+    // dK / dV for kv rows 32 drh .. +31 and the wave's 9 column blocks, as in
+    // the recomputing form.
+    short8_t ad[2], ap[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      ad[rb] = ld16_lds(&sDST[(32 * drh + 16 * rb + r16) * SP + 8 * g16]);
+      ap[rb] = ld16_lds(&sPT[(32 * drh + 16 * rb + r16) * SP + 8 * g16]);
+    }
+    const int col0 = 128 * dcq;
+    short8_t bq = ld_bt_rs_lo<DKV_SUB>(sq, 0, col0, lane);
+    short8_t bo = ld_bt_rs_lo<DKV_SUB>(sd, 0, col0, lane);
+#pragma unroll
+    for (int n = 0; n < 9; ++n) {
+      short8_t bqn = bq, bon = bo;
+      if (n + 1 < 8) {
+        bqn = ld_bt_rs_lo<DKV_SUB>(sq, 0, col0 + 16 * (n + 1), lane);
+        bon = ld_bt_rs_lo<DKV_SUB>(sd, 0, col0 + 16 * (n + 1), lane);
+      } else if (n + 1 == 8) {
+        bqn = ld_bt_rs_hi<DKV_SUB>(sq, 0, D_V + 16 * dcq, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) acc[rb][n] = mfma_bf16(ad[rb], bq, acc[rb][n]);
+      if (n < 8) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) acc[rb][n] = mfma_bf16(ap[rb], bo, acc[rb][n]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      bq = bqn;
+      bo = bon;
+    }
+    if (u & 1) {   // the next sub-chunk starts chunk u/2 + 1: load the one after it
+      c_cur = c_nxt;
+      if ((u >> 1) + 2 < nch) c_nxt = chunk((u >> 1) + 2);
+    }
+  }
+
+  const int g16 = lane_id >> 4, r16 = lane_id & 15;
+  if (a.acc32) {
+    float* dst = a.acc32 + (kb0 + 32 * drh + 4 * g16) * D_K + r16;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 9; ++n)
+          unsafeAtomicAdd(&dst[(16 * rb + i) * D_K + (n < 8 ? 128 * dcq + 16 * n : D_V + 16 * dcq)],
+                          acc[rb][n][i]);
+  } else {
+    float* dst = a.part + (slot * TILE_KV + 32 * drh + 4 * g16) * D_K + r16;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 9; ++n)
+          dst[(16 * rb + i) * D_K + (n < 8 ? 128 * dcq + 16 * n : D_V + 16 * dcq)] = acc[rb][n][i];
+  }
+  if (tid == 0) a.ptouch[slot] = touched;
+}
+
 // The dkv pass: workgroup w takes sub-chunks [w per, (w+1) per) of all
 // blocks' sub-chunks in block order (per = ceil(total / DKV_WGS)), as one
 // segment per block it meets, starting from block wstart[w].
-template <int H>
+template <int H, bool PDS>
 __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
   __shared__ DkvLds lds;
   const int total = a.spre[a.NB];
@@ -534,7 +697,10 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int sb = a.spre[blk], se = a.spre[blk + 1];
     if (se <= lo) continue;   // a block with no records
     const int end = min(hi, se);
-    dkv_segment<H>(a, blk, lo - sb, end - sb, (int64_t)blockIdx.x + blk, lds);
+    if constexpr (PDS)
+      dkv_segment_pds<H>(a, blk, lo - sb, end - sb, (int64_t)blockIdx.x + blk, lds);
+    else
+      dkv_segment<H>(a, blk, lo - sb, end - sb, (int64_t)blockIdx.x + blk, lds);
     lo = end;
     __syncthreads();   // the next segment refills the LDS buffers
   }
@@ -554,7 +720,13 @@ __global__ __launch_bounds__(256) void dkv_schedule_kernel(BwdArgs a) {
     const int nz = e.y > 0 ? 1 : 0;
     int total;
     const int pos = base + block_exclusive_scan256(nz, scratch, &total);
-    if (nz) a.clist[blk * a.G + pos] = make_int2((int)g, e.x);
+    if (nz) {
+      a.clist[blk * a.G + pos] = make_int2((int)g, e.x);
+      if (a.cbase) {   // stored-P mode: the chunk's first union entry and row mask
+        a.cbase[blk * a.G + pos] = a.kbase[blk * a.G + g];
+        a.cmask[blk * a.G + pos] = a.korm[blk * a.G + g];
+      }
+    }
     base += total;
   }
   if (tid == 0) a.nchunk[blk] = base;
@@ -751,11 +923,16 @@ hipError_t launch_dkv_schedule(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream) {
   if (a.NB == 0) return hipSuccess;
   const dim3 grid((unsigned)DKV_WGS), block(DKV_NW * 64);
+  const bool pds = a.pds != nullptr;
   switch (heads) {
-    case 8: bwd_dkv_kernel<8><<<grid, block, 0, stream>>>(a); break;
-    case 16: bwd_dkv_kernel<16><<<grid, block, 0, stream>>>(a); break;
-    case 32: bwd_dkv_kernel<32><<<grid, block, 0, stream>>>(a); break;
-    case 64: bwd_dkv_kernel<64><<<grid, block, 0, stream>>>(a); break;
+    case 8: pds ? bwd_dkv_kernel<8, true><<<grid, block, 0, stream>>>(a)
+                : bwd_dkv_kernel<8, false><<<grid, block, 0, stream>>>(a); break;
+    case 16: pds ? bwd_dkv_kernel<16, true><<<grid, block, 0, stream>>>(a)
+                 : bwd_dkv_kernel<16, false><<<grid, block, 0, stream>>>(a); break;
+    case 32: pds ? bwd_dkv_kernel<32, true><<<grid, block, 0, stream>>>(a)
+                 : bwd_dkv_kernel<32, false><<<grid, block, 0, stream>>>(a); break;
+    case 64: pds ? bwd_dkv_kernel<64, true><<<grid, block, 0, stream>>>(a)
+                 : bwd_dkv_kernel<64, false><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

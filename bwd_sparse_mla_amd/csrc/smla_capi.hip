@@ -91,7 +91,8 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
 
 }  // namespace
 
-Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward, bool atomic) {
+Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward, bool atomic,
+               bool stored_p) {
   Plan p;
   p.s_q = s_q;
   p.s_kv = s_kv;
@@ -120,11 +121,20 @@ Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward, bo
     p.off_spre = o;    o = align256(o + (size_t)(p.NB + 1) * 4);
     p.off_wstart = o;  o = align256(o + (size_t)DKV_WGS * 4);
     p.off_part = o;    o = align256(o + (size_t)(DKV_WGS + p.NB) * TILE_KV * 576 * 4);
-    // Atomic dkv mode: the fp32 accumulator goes last, so the rest of the
-    // layout (and a plan smla_plan built) is the same in both modes.
+    p.off_kbase = o;   o = align256(o + (size_t)p.NB * p.G * 4);
+    p.off_korm = o;    o = align256(o + (size_t)p.NB * p.G * 8);
+    p.off_cbase = o;   o = align256(o + (size_t)p.NB * p.G * 4);
+    p.off_cmask = o;   o = align256(o + (size_t)p.NB * p.G * 8);
+    // Mode-specific buffers go last, so the rest of the layout (and a plan
+    // smla_plan built) is the same in every mode: the atomic mode's fp32
+    // accumulator, then the stored-P mode's P / dS buffer.
     if (atomic) {
       p.off_acc32 = o;
       o = align256(o + (size_t)p.NB * TILE_KV * 576 * 4);
+    }
+    if (stored_p) {
+      p.off_pds = o;
+      o = align256(o + (size_t)p.G * p.qcap * 2 * GROUP_ROWS * 2);
     }
   }
   p.bytes = o;
@@ -155,7 +165,8 @@ size_t smla_fwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t
 size_t smla_bwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
                                uint32_t flags) {
   if (check_shape(s_q, s_kv, heads, topk) != SMLA_OK) return 0;
-  return make_plan(s_q, s_kv, heads, topk, true, (flags & SMLA_DKV_ATOMIC) != 0).bytes;
+  return make_plan(s_q, s_kv, heads, topk, true, (flags & SMLA_DKV_ATOMIC) != 0,
+                   (flags & SMLA_DKV_STORED_P) != 0).bytes;
 }
 
 // Fills the planner's arguments for a workspace laid out by make_plan.
@@ -177,6 +188,8 @@ static PlanArgs plan_args(const Plan& p, const int32_t* indices, int64_t s_q, in
   pa.qmask = reinterpret_cast<uint8_t*>(ws + p.off_qmask);
   pa.ktab = backward ? reinterpret_cast<int2*>(ws + p.off_ktab) : nullptr;
   pa.krmask = backward ? reinterpret_cast<unsigned long long*>(ws + p.off_krmask) : nullptr;
+  pa.kbase = backward ? reinterpret_cast<int*>(ws + p.off_kbase) : nullptr;
+  pa.korm = backward ? reinterpret_cast<unsigned long long*>(ws + p.off_korm) : nullptr;
   return pa;
 }
 
@@ -270,7 +283,7 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   if (!kv || (s_q > 0 && (!q || !out || !dout || !indices || !lse || !dq)))
     return fail(SMLA_ERR_NULL, "null tensor pointer");
   if (!dkv && !dkv_f32) return fail(SMLA_ERR_NULL, "dkv and dkv_f32 are both null");
-  if (flags & ~(SMLA_DKV_ACCUMULATE | SMLA_DKV_ATOMIC | SMLA_PLAN_READY))
+  if (flags & ~(SMLA_DKV_ACCUMULATE | SMLA_DKV_ATOMIC | SMLA_PLAN_READY | SMLA_DKV_STORED_P))
     return fail(SMLA_ERR_FLAGS, "unknown flag bits");
   if ((flags & SMLA_DKV_ACCUMULATE) && !dkv_f32)
     return fail(SMLA_ERR_FLAGS, "SMLA_DKV_ACCUMULATE needs dkv_f32");
@@ -280,7 +293,8 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   if ((dkv && !aligned16(dkv)) || (dkv_f32 && !aligned16(dkv_f32)))
     return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   const bool atomic = (flags & SMLA_DKV_ATOMIC) != 0;
-  const Plan p = make_plan(s_q, s_kv, heads, topk, true, atomic);
+  const bool stored_p = (flags & SMLA_DKV_STORED_P) != 0;
+  const Plan p = make_plan(s_q, s_kv, heads, topk, true, atomic, stored_p);
   if (!workspace || workspace_bytes < p.bytes)
     return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_bwd_workspace_size(flags)");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -323,6 +337,11 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   ba.part = reinterpret_cast<float*>(ws + p.off_part);
   ba.ptouch = reinterpret_cast<unsigned long long*>(ws + p.off_ptouch);
   ba.acc32 = atomic ? reinterpret_cast<float*>(ws + p.off_acc32) : nullptr;
+  ba.kbase = pa.kbase;
+  ba.korm = pa.korm;
+  ba.cbase = stored_p ? reinterpret_cast<int*>(ws + p.off_cbase) : nullptr;
+  ba.cmask = stored_p ? reinterpret_cast<unsigned long long*>(ws + p.off_cmask) : nullptr;
+  ba.pds = stored_p ? reinterpret_cast<uint16_t*>(ws + p.off_pds) : nullptr;
   ba.dq = static_cast<uint16_t*>(dq);
   ba.dkv = static_cast<uint16_t*>(dkv);
   ba.dkv_f32 = dkv_f32;

@@ -30,11 +30,14 @@ struct Plan {
   size_t off_ktab = 0, off_krmask = 0, off_delta = 0;
   size_t off_clist = 0, off_nchunk = 0, off_part = 0, off_ptouch = 0;
   size_t off_gorder = 0, off_spre = 0, off_wstart = 0;
+  size_t off_kbase = 0, off_korm = 0, off_cbase = 0, off_cmask = 0;
   size_t off_acc32 = 0;   // atomic dkv mode only: [NB * 64, 576] fp32 accumulator
+  size_t off_pds = 0;     // stored-P mode only: [G, qcap, 2, 64] bf16 P and scale * dS
   size_t bytes = 0;
 };
 
-Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward, bool atomic = false);
+Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward, bool atomic = false,
+               bool stored_p = false);
 
 struct PlanArgs {
   const int32_t* idx;
@@ -48,6 +51,8 @@ struct PlanArgs {
   uint8_t* qmask;     // [G, qcap] mask of the group's tokens that select it
   int2* ktab;         // [NB, G] (record start within the group, T) or (0, 0); may be null
   unsigned long long* krmask;  // [G, rcap] 64-bit row masks, T per (block, group) pair
+  int* kbase;                  // [NB, G] first main union entry of the group in the block (with records)
+  unsigned long long* korm;    // [NB, G] OR of the group's row masks for the block (with records)
 };
 
 struct FwdArgs {
@@ -85,6 +90,12 @@ struct BwdArgs {
   int* wstart;        // [DKV_WGS] first kv block of each dkv workgroup's range
   float* delta;       // [s_q * H] rowsum(dout * out), written by the dq pass
   int2* clist;        // [NB, G] per block: (group, record start), compacted
+  const int* kbase;   // [NB, G] from the planner (stored-P mode)
+  const unsigned long long* korm;   // [NB, G] from the planner (stored-P mode)
+  int* cbase;         // [NB, G] parallel to clist: the chunk's first union entry (stored-P mode)
+  unsigned long long* cmask;   // [NB, G] parallel to clist: the block rows the chunk selects
+  uint16_t* pds;      // stored-P mode: [G, qcap, 2, 64] bf16 P and scale * dS per union entry and
+                      // group row, written by the dq pass and read by the dkv pass; else null
   int* nchunk;        // [NB] entries of clist per block
   float* part;        // [DKV_WGS + NB, 64, 576] fp32 partial dkv per (workgroup w, block b): slot w + b
   unsigned long long* ptouch;  // [DKV_WGS + NB] rows each partial touched

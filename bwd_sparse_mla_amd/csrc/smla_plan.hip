@@ -105,6 +105,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   }
   // Windows start on a 64-row block boundary so kv blocks never straddle two.
   for (int w0 = (hi >= 0 ? (lo & ~63) : 1); w0 <= hi; w0 += WIN_BITS) {
+    const int qbase0 = qbase;   // union entries before this window
     for (int i = tid; i < T * WIN_WORDS; i += 256) (&bm[0][0])[i] = 0u;
     __syncthreads();
     // 16 index loads in flight per thread before their bitmap updates.
@@ -162,22 +163,27 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
       // kv-block records: thread tid owns block (w0 >> 6) + tid.  A block any
       // token of the group selects gets T records, one 64-bit row mask per
       // token of the group (zero for tokens that select none of its rows).
-      unsigned long long mk[T];
-      int any = 0;
+      unsigned long long mk[T], orm = 0ull;
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         mk[t] = (unsigned long long)bm[t][2 * tid] |
                 ((unsigned long long)bm[t][2 * tid + 1] << 32);
-        any |= (mk[t] != 0ull);
+        orm |= mk[t];
       }
-      int rtotal;
+      const int any = orm != 0ull;
+      int rtotal, etotal;
       const int rpos = rbase + block_exclusive_scan256(any ? T : 0, scratch, &rtotal);
+      // The block's union entries follow those of the window's earlier
+      // blocks (the union is in row order): its first entry index.
+      const int epos = qbase0 + block_exclusive_scan256(__popcll(orm), scratch, &etotal);
       const int64_t b = (int64_t)(w0 >> 6) + tid;   // a set bit is a row < s_kv, so any => b < NB
       if (b < a.NB) a.ktab[b * a.G + g] = any ? make_int2(rpos, T) : make_int2(0, 0);
       if (any) {
         const int64_t r = g * a.rcap + rpos;
 #pragma unroll
         for (int t = 0; t < T; ++t) a.krmask[r + t] = mk[t];
+        a.kbase[b * a.G + g] = epos;
+        a.korm[b * a.G + g] = orm;
       }
       rbase += rtotal;
     }

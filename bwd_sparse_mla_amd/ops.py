@@ -130,14 +130,16 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_
 def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
                    indices: torch.Tensor, lse: torch.Tensor, sm_scale: float, *,
                    dkv_f32: torch.Tensor | None = None, accumulate: bool = False,
-                   atomic: bool = False,
+                   atomic: bool = False, stored_p: bool = False,
                    want_bf16_dkv: bool = True):
     """Backward: returns (dq like q, dkv like kv in bf16 or None).
 
     dkv_f32, if given, is an fp32 [S_kv, 576] tensor that receives the fp32
     dkv (overwritten, or added to with accumulate=True).  The default mode is
     the deterministic per-row reduction; atomic=True scatters dkv with fp32
-    atomic adds (not bitwise reproducible)."""
+    atomic adds (not bitwise reproducible).  stored_p=True has the dq pass
+    store P and scale * dS for the dkv pass (one recompute of the scores
+    instead of two; a larger workspace)."""
     lib = _lib.load()
     q3 = _prep(_flat_q(q), torch.bfloat16, "q")
     kv2 = _prep(_flat_kv(kv), torch.bfloat16, "kv")
@@ -154,7 +156,7 @@ def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, out: torch.Tensor, dout: t
     K = ix.shape[1]
     S_kv = kv2.shape[0]
     dev = q3.device
-    flags = _lib.SMLA_DKV_ATOMIC if atomic else 0
+    flags = (_lib.SMLA_DKV_ATOMIC if atomic else 0) | (_lib.SMLA_DKV_STORED_P if stored_p else 0)
     if accumulate:
         if dkv_f32 is None:
             raise ValueError("accumulate=True needs dkv_f32")
@@ -317,10 +319,11 @@ class SparseMLARunner:
     shapes given here."""
 
     def __init__(self, s_q: int, s_kv: int, heads: int, topk: int, device="cuda",
-                 dkv_atomic: bool = False):
+                 dkv_atomic: bool = False, dkv_stored_p: bool = False):
         self.lib = _lib.load()
         self.shape = (s_q, s_kv, heads, topk)
-        self._bflags = _lib.SMLA_DKV_ATOMIC if dkv_atomic else 0
+        self._bflags = ((_lib.SMLA_DKV_ATOMIC if dkv_atomic else 0) |
+                        (_lib.SMLA_DKV_STORED_P if dkv_stored_p else 0))
         dev = torch.device(device)
         self.out = torch.empty(s_q, heads, D_V, dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty(s_q, heads, dtype=torch.float32, device=dev)

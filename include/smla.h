@@ -89,6 +89,16 @@ enum smla_status {
 #define SMLA_PLAN_READY 4u      /* smla_fwd_ex / smla_bwd: the workspace already
                                    holds the index plan smla_plan built for the
                                    same indices and sizes; skip planning */
+#define SMLA_DKV_STORED_P 8u    /* smla_bwd: the dq pass stores P and
+                                   sm_scale * dS (bf16, per union entry and
+                                   query row) in the workspace and the dkv pass
+                                   reads them instead of recomputing the scores
+                                   and dP; same results within rounding, one
+                                   recompute of the scores per backward; the
+                                   workspace must be
+                                   smla_bwd_workspace_size(..., SMLA_DKV_STORED_P)
+                                   bytes (256 bytes more per union slot bound:
+                                   s_q * topk * 256 at most) */
 
 /* Index plan: which slots are valid (an index is a row iff it is not -1 and
  * lies in [0, s_kv): miles PR #2079 digest, "fix GLM-5 sparse-MLA kernel -1

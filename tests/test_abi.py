@@ -89,7 +89,7 @@ def test_bwd_argument_errors(lib):
     assert call_bwd(lib, heads=7) == 2
     assert call_bwd(lib, dq=0) == 1
     assert call_bwd(lib, dkv=0, dkv32=0) == 1
-    assert call_bwd(lib, flags=8) == 5
+    assert call_bwd(lib, flags=32) == 5
     assert call_bwd(lib, flags=1, dkv32=0) == 5
     assert call_bwd(lib, dkv32=FAKE + 4) == 3
     assert call_bwd(lib, ws_bytes=64) == 4
@@ -99,6 +99,11 @@ def test_bwd_argument_errors(lib):
     atom = lib.smla_bwd_workspace_size(16, 16, 8, 4, 2)
     assert atom >= det + 64 * 576 * 4
     assert call_bwd(lib, flags=2, ws_bytes=det) == 4
+    # the stored-P backward keeps P and dS of every union slot: 256 bytes per
+    # (token, slot) bound on top of the plan
+    stored = lib.smla_bwd_workspace_size(16, 16, 8, 4, 8)
+    assert stored >= det + 16 * 4 * 256
+    assert call_bwd(lib, flags=8, ws_bytes=det) == 4
 
 
 def test_validate_argument_errors(lib):

@@ -32,12 +32,13 @@ pytestmark = pytest.mark.gpu
 MAX_SELECTORS = 768   # tokens the oracle recomputes for the sampled dkv rows
 
 
-def _run(w, atomic=False):
+def _run(w, atomic=False, stored=False):
     import torch
 
     import bwd_sparse_mla_amd as smla
     q, kv, dout, idx = gpu_inputs(w)
-    run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, q.device, dkv_atomic=atomic)
+    run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, q.device, dkv_atomic=atomic,
+                               dkv_stored_p=stored)
     run._check(q, kv, idx, dout)
     run.plan(idx)
     run.fwd(q, kv, idx, w.sm_scale, planned=True)
@@ -77,18 +78,22 @@ def _bf16_rows(t, rows):
     return t.index_select(0, torch.as_tensor(rows, device=t.device)).float().cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("name,atomic", [("packed_ragged", False), ("padding_stress", False),
-                                         ("recency", False), ("long_context", False),
-                                         ("long_context", True)])
-def test_full_size_sampled_parity(name, atomic):
+@pytest.mark.parametrize("name,atomic,stored", [
+    ("packed_ragged", False, False), ("padding_stress", False, False), ("recency", False, False),
+    ("long_context", False, False), ("long_context", True, False),
+    ("packed_ragged", False, True), ("padding_stress", False, True), ("recency", False, True),
+    ("long_context", True, True)])
+def test_full_size_sampled_parity(name, atomic, stored):
     """atomic: the same checks with dkv scattered by fp32 atomic adds (the
-    long-context workload runs in both dkv modes)."""
+    long-context workload runs in both dkv modes); stored: the dkv pass reads
+    P and dS stored by the dq pass instead of recomputing them."""
     import torch
 
     w = synth.WORKLOADS[name]()
     print(f"[fullsize] {w.name} S={w.S} H={w.H} K={w.K} S_kv={w.S_kv} valid={w.n_valid} "
-          f"dkv {'atomic' if atomic else 'deterministic'}", flush=True)
-    run = _run(w, atomic)
+          f"dkv {'atomic' if atomic else 'deterministic'} "
+          f"{'stored P' if stored else 'recomputed P'}", flush=True)
+    run = _run(w, atomic, stored)
     for label, t in (("out", run.out), ("lse", run.lse), ("dq", run.dq), ("dkv", run.dkv)):
         bad = int((~torch.isfinite(t.float())).sum())
         assert bad == 0, f"{bad} nonfinite values in {label}"
