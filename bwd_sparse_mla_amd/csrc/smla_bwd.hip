@@ -24,6 +24,8 @@
 // a record or a union entry (miles PR #2079 digest, "fix GLM-5 sparse-MLA
 // kernel -1 index OOB and NaN gradients", 实现拆解 item 3 -- there a clamped
 // -1 added exact zeros into row 0; here it adds nothing anywhere).
+#include <type_traits>
+
 #include "smla_device.h"
 #include "smla_internal.h"
 
@@ -527,63 +529,80 @@ __device__ __forceinline__ void dkv_segment(const BwdArgs& a, int64_t blk, int u
         for (int n = 0; n < 9; ++n)
           dst[(16 * rb + i) * D_K + (n < 8 ? 128 * dcq + 16 * n : D_V + 16 * dcq)] = acc[rb][n][i];
   }
-  if (tid == 0) a.ptouch[slot] = touched;
+  if (tid == 0) a.ptouch[2 * slot] = touched;
 }
 
-// Stored-P form of a segment (SMLA_DKV_STORED_P): the dq pass has left P and
-// scale * dS of every (union entry, query row) in the workspace, so a step
-// only stages the sub-chunk's 64 x 32 P^T / dS^T tiles from there (thread t
-// takes kv row t / 8 of the block and 8 query rows of P or dS: the union
-// entry of a selected row is the chunk's first entry plus the selected rows
-// before it; other rows are zero) and runs the dK / dV contraction -- no
-// scores, no dP, no lse / delta / mask copies.  Per step: wait for the
-// copies, stage P^T / dS^T, issue the next sub-chunk's copies (Q, dout into
-// the other buffers; its P / dS piece into registers), sync, contract.
+// Stored-P form (SMLA_DKV_STORED_P): the dq pass has left P and scale * dS
+// of every (union entry, query row) in the workspace, so the dkv pass does
+// not recompute scores or dP, and its unit is a pair of kv blocks (128 rows):
+// one copy of a sub-chunk's Q / dout then serves twice the rows.  A chunk is
+// a query group with records in either block.  Per step: wait for the copies,
+// stage the sub-chunk's 128 x 32 P^T / dS^T tiles from the workspace (thread
+// t takes kv row t / 8 of each block and 8 query rows of P or dS; the union
+// entry of a selected row is the chunk's first entry in that block plus the
+// selected rows before it; other rows are zero), issue the next sub-chunk's
+// copies (Q, dout into the other buffers; its P / dS pieces into
+// registers), sync, and run the dK / dV contraction: wave w takes kv rows
+// 64 (w & 1) .. +63 (four 16-row blocks) and the column blocks of w >> 1.
+struct DkvPairLds {
+  __attribute__((aligned(16))) char sQ[2][KV32_TILE_BYTES];
+  __attribute__((aligned(16))) char sD[2][DO32_TILE_BYTES];
+  __attribute__((aligned(16))) unsigned short sPT[2 * TILE_KV * DKV_SP];
+  __attribute__((aligned(16))) unsigned short sDST[2 * TILE_KV * DKV_SP];
+};
+
 template <int H>
-__device__ __forceinline__ void dkv_segment_pds(const BwdArgs& a, int64_t blk, int u0, int u1, int64_t slot,
-                                                DkvLds& lds) {
+__device__ __forceinline__ void dkv_segment_pair(const BwdArgs& a, int64_t unit, int u0, int u1,
+                                                 int64_t slot, DkvPairLds& lds) {
   constexpr int SP = DKV_SP;
+  constexpr int UR = 2 * TILE_KV;   // kv rows per unit
   auto& sQ = lds.sQ;
   auto& sD = lds.sD;
   auto& sPT = lds.sPT;
   auto& sDST = lds.sDST;
   const int tid = threadIdx.x, lane_id = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nch = a.nchunk[blk];
-  const int64_t kb0 = blk * TILE_KV;
+  const int nch = a.nchunk[unit];
+  const int64_t kb0 = unit * UR;
   const int64_t qrows = a.s_q * H;
   const int drh = wv & 1, dcq = wv >> 1;
-  float4_t acc[2][9];
+  float4_t acc[4][9];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  unsigned long long touched = 0ull;
+  unsigned long long touched0 = 0ull, touched1 = 0ull;
 
-  // Chunk c of the block: group, first union entry in the block, row mask.
-  const int64_t cb = blk * a.G;
+  // Chunk c of the unit: group, and per block its first union entry and the
+  // rows the group selects there (wave-uniform: scalar registers).
+  const int64_t cu = unit * a.G;
   struct Chunk {
-    int g, e0;
-    unsigned long long m;
+    int g, e0, e1;
+    unsigned long long m0, m1;
+  };
+  auto uni64 = [](unsigned long long m) __attribute__((always_inline)) {
+    // readfirstlane returns int: widen through unsigned, not by sign extension
+    return (unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)m) |
+           ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)(m >> 32)) << 32);
   };
   auto chunk = [&](int c) __attribute__((always_inline)) {
-    Chunk ch;   // wave-uniform values (scalar registers)
-    ch.g = __builtin_amdgcn_readfirstlane(a.clist[cb + c].x);
-    ch.e0 = __builtin_amdgcn_readfirstlane(a.cbase[cb + c]);
-    const unsigned long long m = a.cmask[cb + c];
-    // (readfirstlane returns int: widen through unsigned, not by sign extension)
-    ch.m = (unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)m) |
-           ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)(m >> 32)) << 32);
+    Chunk ch;
+    ch.g = __builtin_amdgcn_readfirstlane(a.clist[cu + c].x);
+    ch.e0 = __builtin_amdgcn_readfirstlane(a.cbase[2 * (cu + c)]);
+    ch.e1 = __builtin_amdgcn_readfirstlane(a.cbase[2 * (cu + c) + 1]);
+    ch.m0 = uni64(a.cmask[2 * (cu + c)]);
+    ch.m1 = uni64(a.cmask[2 * (cu + c) + 1]);
     return ch;
   };
   Chunk c_cur = chunk(u0 >> 1);                       // chunk of the current sub-chunk
   Chunk c_nxt = chunk(min((u0 >> 1) + 1, nch - 1));   // the chunk after it
 
   const int pr_row = tid >> 3, pr_part = tid & 7;
+  const unsigned long long below = (1ull << pr_row) - 1ull;
   auto pds_load = [&](int g, int e0, unsigned long long m, int half) __attribute__((always_inline)) {
     short8_t v = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
     if ((m >> pr_row) & 1ull) {
-      const int e = min(e0 + __popcll(m & ((1ull << pr_row) - 1ull)), (int)a.qcap - 1);
+      const int e = min(e0 + __popcll(m & below), (int)a.qcap - 1);
       v = ld16_global(a.pds + ((int64_t)g * a.qcap + e) * (2 * GROUP_ROWS) +
                       (pr_part >> 2) * GROUP_ROWS + DKV_SUB * half + 8 * (pr_part & 3));
     }
@@ -597,37 +616,40 @@ __device__ __forceinline__ void dkv_segment_pds(const BwdArgs& a, int64_t blk, i
   };
 
   copies(c_cur.g, u0, sQ[0], sD[0], lane_id);
-  short8_t piece = pds_load(c_cur.g, c_cur.e0, c_cur.m, u0 & 1);
+  short8_t piece0 = pds_load(c_cur.g, c_cur.e0, c_cur.m0, u0 & 1);
+  short8_t piece1 = pds_load(c_cur.g, c_cur.e1, c_cur.m1, u0 & 1);
   for (int u = u0; u < u1; ++u) {
     const int b = (u - u0) & 1;
     const char* sq = sQ[b];
     const char* sd = sD[b];
     wait_vmcnt0();
     __syncthreads();
-    *reinterpret_cast<short8_t*>((pr_part < 4 ? sPT : sDST) + pr_row * SP + 8 * (pr_part & 3)) = piece;
-    touched |= c_cur.m;
-    if (u + 1 < u1) {   // the next sub-chunk: its P / dS piece and its Q / dout copies
+    {
+      unsigned short* st = (pr_part < 4 ? sPT : sDST) + pr_row * SP + 8 * (pr_part & 3);
+      *reinterpret_cast<short8_t*>(st) = piece0;
+      *reinterpret_cast<short8_t*>(st + TILE_KV * SP) = piece1;
+    }
+    touched0 |= c_cur.m0;
+    touched1 |= c_cur.m1;
+    if (u + 1 < u1) {   // the next sub-chunk: its Q / dout copies and its P / dS pieces
       int lane = lane_id;
       asm volatile("" : "+v"(lane));   // offsets recomputed per sub-chunk, not kept live
       const bool adv = (u & 1) != 0;
       const int gn = adv ? c_nxt.g : c_cur.g;
-      const int en = adv ? c_nxt.e0 : c_cur.e0;
-      const unsigned long long mn = adv ? c_nxt.m : c_cur.m;
       copies(gn, u + 1, sQ[b ^ 1], sD[b ^ 1], lane);
-      piece = pds_load(gn, en, mn, (u + 1) & 1);
+      piece0 = pds_load(gn, adv ? c_nxt.e0 : c_cur.e0, adv ? c_nxt.m0 : c_cur.m0, (u + 1) & 1);
+      piece1 = pds_load(gn, adv ? c_nxt.e1 : c_cur.e1, adv ? c_nxt.m1 : c_cur.m1, (u + 1) & 1);
     }
     __syncthreads();
 
     int lane = lane_id;
     asm volatile("" : "+v"(lane));
     const int g16 = lane >> 4, r16 = lane & 15;
-    // dK / dV for kv rows 32 drh .. +31 and the wave's 9 column blocks, as in
-    // the recomputing form.
-    short8_t ad[2], ap[2];
+    short8_t ad[4], ap[4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      ad[rb] = ld16_lds(&sDST[(32 * drh + 16 * rb + r16) * SP + 8 * g16]);
-      ap[rb] = ld16_lds(&sPT[(32 * drh + 16 * rb + r16) * SP + 8 * g16]);
+    for (int rb = 0; rb < 4; ++rb) {
+      ad[rb] = ld16_lds(&sDST[(64 * drh + 16 * rb + r16) * SP + 8 * g16]);
+      ap[rb] = ld16_lds(&sPT[(64 * drh + 16 * rb + r16) * SP + 8 * g16]);
     }
     const int col0 = 128 * dcq;
     short8_t bq = ld_bt_rs_lo<DKV_SUB>(sq, 0, col0, lane);
@@ -643,10 +665,10 @@ __device__ __forceinline__ void dkv_segment_pds(const BwdArgs& a, int64_t blk, i
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) acc[rb][n] = mfma_bf16(ad[rb], bq, acc[rb][n]);
+      for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(ad[rb], bq, acc[rb][n]);
       if (n < 8) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) acc[rb][n] = mfma_bf16(ap[rb], bo, acc[rb][n]);
+        for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(ap[rb], bo, acc[rb][n]);
       }
       __builtin_amdgcn_sched_barrier(0);
       bq = bqn;
@@ -658,28 +680,35 @@ __device__ __forceinline__ void dkv_segment_pds(const BwdArgs& a, int64_t blk, i
     }
   }
 
+  // Partial of the unit (rows 64 drh + 16 rb + 4 g + i); the atomic mode adds
+  // it into the accumulator instead, rows of blocks past the last skipped.
   const int g16 = lane_id >> 4, r16 = lane_id & 15;
   if (a.acc32) {
-    float* dst = a.acc32 + (kb0 + 32 * drh + 4 * g16) * D_K + r16;
+    if (2 * unit + drh < a.NB) {
+      float* dst = a.acc32 + (kb0 + 64 * drh + 4 * g16) * D_K + r16;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int n = 0; n < 9; ++n)
-          unsafeAtomicAdd(&dst[(16 * rb + i) * D_K + (n < 8 ? 128 * dcq + 16 * n : D_V + 16 * dcq)],
-                          acc[rb][n][i]);
+          for (int n = 0; n < 9; ++n)
+            unsafeAtomicAdd(&dst[(16 * rb + i) * D_K + (n < 8 ? 128 * dcq + 16 * n : D_V + 16 * dcq)],
+                            acc[rb][n][i]);
+    }
   } else {
-    float* dst = a.part + (slot * TILE_KV + 32 * drh + 4 * g16) * D_K + r16;
+    float* dst = a.part + (slot * UR + 64 * drh + 4 * g16) * D_K + r16;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int n = 0; n < 9; ++n)
           dst[(16 * rb + i) * D_K + (n < 8 ? 128 * dcq + 16 * n : D_V + 16 * dcq)] = acc[rb][n][i];
   }
-  if (tid == 0) a.ptouch[slot] = touched;
+  if (tid == 0) {
+    a.ptouch[2 * slot] = touched0;
+    a.ptouch[2 * slot + 1] = touched1;
+  }
 }
 
 // The dkv pass: workgroup w takes sub-chunks [w per, (w+1) per) of all
@@ -687,8 +716,8 @@ __device__ __forceinline__ void dkv_segment_pds(const BwdArgs& a, int64_t blk, i
 // segment per block it meets, starting from block wstart[w].
 template <int H, bool PDS>
 __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
-  __shared__ DkvLds lds;
-  const int total = a.spre[a.NB];
+  __shared__ std::conditional_t<PDS, DkvPairLds, DkvLds> lds;
+  const int total = a.spre[a.NU];
   const int per = max(1, (total + DKV_WGS - 1) / DKV_WGS);
   int lo = min(total, (int)blockIdx.x * per);
   const int hi = min(total, lo + per);
@@ -698,7 +727,7 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
     if (se <= lo) continue;   // a block with no records
     const int end = min(hi, se);
     if constexpr (PDS)
-      dkv_segment_pds<H>(a, blk, lo - sb, end - sb, (int64_t)blockIdx.x + blk, lds);
+      dkv_segment_pair<H>(a, blk, lo - sb, end - sb, (int64_t)blockIdx.x + blk, lds);
     else
       dkv_segment<H>(a, blk, lo - sb, end - sb, (int64_t)blockIdx.x + blk, lds);
     lo = end;
@@ -706,58 +735,70 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
   }
 }
 
-// Compacts each kv block's row of the [block, group] record table into the
-// block's chunk list (groups with records for the block, ascending).
+// Compacts each dkv unit's column of the [block, group] record table into
+// the unit's chunk list (groups with records for the unit, ascending).  In
+// the stored-P form a unit is a pair of blocks: a group with records in
+// either block is a chunk, with, per block, its first union entry there and
+// the rows it selects (zero where it has none).
 __global__ __launch_bounds__(256) void dkv_schedule_kernel(BwdArgs a) {
   __shared__ int scratch[8];
-  const int64_t blk = blockIdx.x;
+  const int64_t unit = blockIdx.x;
   const int tid = threadIdx.x;
   int base = 0;
   for (int64_t gb = 0; gb < a.G; gb += 256) {
     const int64_t g = gb + tid;
-    int2 e = make_int2(0, 0);
-    if (g < a.G) e = a.ktab[blk * a.G + g];
-    const int nz = e.y > 0 ? 1 : 0;
+    int2 e = make_int2(0, 0), e1 = make_int2(0, 0);
+    if (a.ub == 2) {
+      if (g < a.G) e = a.ktab[(2 * unit) * a.G + g];
+      if (g < a.G && 2 * unit + 1 < a.NB) e1 = a.ktab[(2 * unit + 1) * a.G + g];
+    } else if (g < a.G) {
+      e = a.ktab[unit * a.G + g];
+    }
+    const int nz = (e.y > 0 || e1.y > 0) ? 1 : 0;
     int total;
     const int pos = base + block_exclusive_scan256(nz, scratch, &total);
     if (nz) {
-      a.clist[blk * a.G + pos] = make_int2((int)g, e.x);
-      if (a.cbase) {   // stored-P mode: the chunk's first union entry and row mask
-        a.cbase[blk * a.G + pos] = a.kbase[blk * a.G + g];
-        a.cmask[blk * a.G + pos] = a.korm[blk * a.G + g];
+      a.clist[unit * a.G + pos] = make_int2((int)g, e.x);
+      if (a.ub == 2) {   // stored-P form: per block, the first union entry and the rows
+        const int64_t c = unit * a.G + pos;
+        const int64_t k0 = (2 * unit) * a.G + g, k1 = (2 * unit + 1) * a.G + g;
+        a.cbase[2 * c] = e.y > 0 ? a.kbase[k0] : 0;
+        a.cmask[2 * c] = e.y > 0 ? a.korm[k0] : 0ull;
+        a.cbase[2 * c + 1] = e1.y > 0 ? a.kbase[k1] : 0;
+        a.cmask[2 * c + 1] = e1.y > 0 ? a.korm[k1] : 0ull;
       }
     }
     base += total;
   }
-  if (tid == 0) a.nchunk[blk] = base;
+  if (tid == 0) a.nchunk[unit] = base;
 }
 
-// Sub-chunk prefix over the blocks (spre[b] = sub-chunks of blocks before b,
-// spre[NB] = total) and the first block of each dkv workgroup's range.  Two
+// Sub-chunk prefix over the dkv units (spre[b] = sub-chunks of units before b,
+// spre[NU] = total) and the first block of each dkv workgroup's range.  Two
 // passes of the same scan: the second finds, for every block, the
 // workgroups whose range starts inside it.
 __global__ __launch_bounds__(256) void dkv_prefix_kernel(BwdArgs a) {
   __shared__ int scratch[8];
   __shared__ int s_total;
   int base = 0;
-  for (int64_t b0 = 0; b0 < a.NB; b0 += 256) {
+  for (int64_t b0 = 0; b0 < a.NU; b0 += 256) {
     const int64_t b = b0 + threadIdx.x;
-    const int v = b < a.NB ? 2 * a.nchunk[b] : 0;
+    const int v = b < a.NU ? 2 * a.nchunk[b] : 0;
     int tot;
     const int pos = base + block_exclusive_scan256(v, scratch, &tot);
-    if (b < a.NB) a.spre[b] = pos;
+    if (b < a.NU) a.spre[b] = pos;
     base += tot;
   }
   if (threadIdx.x == 0) {
-    a.spre[a.NB] = base;
+    a.spre[a.NU] = base;
     s_total = base;
   }
   __syncthreads();
   const int per = max(1, (s_total + DKV_WGS - 1) / DKV_WGS);
   base = 0;
-  for (int64_t b0 = 0; b0 < a.NB; b0 += 256) {
+  for (int64_t b0 = 0; b0 < a.NU; b0 += 256) {
     const int64_t b = b0 + threadIdx.x;
-    const int v = b < a.NB ? 2 * a.nchunk[b] : 0;
+    const int v = b < a.NU ? 2 * a.nchunk[b] : 0;
     int tot;
     const int pos = base + block_exclusive_scan256(v, scratch, &tot);
     if (v > 0)
@@ -793,15 +834,18 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
   const int64_t blk = blockIdx.x / FIN_PARTS;
   const int part = blockIdx.x % FIN_PARTS;
   const int64_t r0 = blk * TILE_KV + FIN_ROWS * part;  // first row of this workgroup
-  // The block's partials: slots w + blk of the workgroups w whose ranges
+  // The block's unit (the block itself, or its pair in the stored-P form)
+  // and the unit's partials: slots w + unit of the workgroups w whose ranges
   // cover its sub-chunks, added in w order.
-  const int total = a.spre[a.NB];
+  const int64_t unit = blk / a.ub;
+  const int hb = (int)(blk - unit * a.ub);   // the block's half of the unit
+  const int total = a.spre[a.NU];
   const int per = max(1, (total + DKV_WGS - 1) / DKV_WGS);
-  const int sb = a.spre[blk], se = a.spre[blk + 1];
+  const int sb = a.spre[unit], se = a.spre[unit + 1];
   const int w0 = sb / per;
   const int nsplit = se > sb ? (se - 1) / per - w0 + 1 : 0;
   unsigned long long touched = 0ull;
-  for (int sp = 0; sp < nsplit; ++sp) touched |= a.ptouch[w0 + sp + blk];
+  for (int sp = 0; sp < nsplit; ++sp) touched |= a.ptouch[2 * (w0 + sp + unit) + hb];
   touched = (touched >> (FIN_ROWS * part)) & ((1ull << FIN_ROWS) - 1ull);
 
   const bool extras = *a.xtotal > 0;
@@ -846,11 +890,12 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
   }
 
   // Atomic mode: one source, the accumulator's rows of the block.
+  const int64_t unit_rows = (int64_t)TILE_KV * a.ub;
   const float* src = a.acc32 ? a.acc32 + (blk * TILE_KV + FIN_ROWS * part) * D_K
-                             : a.part + ((w0 + blk) * TILE_KV + FIN_ROWS * part) * D_K;
+                             : a.part + ((w0 + unit) * unit_rows + TILE_KV * hb + FIN_ROWS * part) * D_K;
   const int nsrc = a.acc32 ? (nsplit > 0 ? 1 : 0) : nsplit;
   constexpr int N4 = FIN_ROWS * D_K / 4;  // float4 elements of the rows
-  constexpr int64_t SPLIT = (int64_t)TILE_KV * D_K;
+  const int64_t SPLIT = unit_rows * D_K;
   for (int e = tid; e < N4; e += 256) {
     // Partials summed left to right in workgroup order; loads go out four
     // at a time (indices clamped into range, extra ones unused).  A block no
@@ -913,7 +958,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream) {
 
 hipError_t launch_dkv_schedule(const BwdArgs& a, hipStream_t stream) {
   if (a.NB == 0) return hipSuccess;
-  dkv_schedule_kernel<<<dim3((unsigned)a.NB), dim3(256), 0, stream>>>(a);
+  dkv_schedule_kernel<<<dim3((unsigned)a.NU), dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dkv_prefix_kernel<<<dim3(1), dim3(256), 0, stream>>>(a);

@@ -117,17 +117,23 @@ Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward, bo
     p.off_delta = o;   o = align256(o + (size_t)s_q * heads * 4);
     p.off_clist = o;   o = align256(o + (size_t)p.NB * p.G * 8);
     p.off_nchunk = o;  o = align256(o + (size_t)p.NB * 4);
-    p.off_ptouch = o;  o = align256(o + (size_t)(DKV_WGS + p.NB) * 8);
+    p.off_ptouch = o;  o = align256(o + (size_t)(DKV_WGS + p.NB) * 2 * 8);
     p.off_spre = o;    o = align256(o + (size_t)(p.NB + 1) * 4);
     p.off_wstart = o;  o = align256(o + (size_t)DKV_WGS * 4);
-    p.off_part = o;    o = align256(o + (size_t)(DKV_WGS + p.NB) * TILE_KV * 576 * 4);
     p.off_kbase = o;   o = align256(o + (size_t)p.NB * p.G * 4);
     p.off_korm = o;    o = align256(o + (size_t)p.NB * p.G * 8);
-    p.off_cbase = o;   o = align256(o + (size_t)p.NB * p.G * 4);
-    p.off_cmask = o;   o = align256(o + (size_t)p.NB * p.G * 8);
-    // Mode-specific buffers go last, so the rest of the layout (and a plan
-    // smla_plan built) is the same in every mode: the atomic mode's fp32
-    // accumulator, then the stored-P mode's P / dS buffer.
+    p.off_cbase = o;   o = align256(o + (size_t)(p.NB + 1) * p.G * 4);
+    p.off_cmask = o;   o = align256(o + (size_t)(p.NB + 1) * p.G * 8);
+    // Mode-specific sizes go last, so the rest of the layout (and a plan
+    // smla_plan built) is the same in every mode: the fp32 partials (64-row
+    // units, or 128-row units in the stored-P form), the atomic mode's fp32
+    // accumulator, then the stored-P form's P / dS buffer.
+    {
+      const int64_t ub = stored_p ? 2 : 1;
+      const int64_t nu = (p.NB + ub - 1) / ub;
+      p.off_part = o;
+      o = align256(o + (size_t)(DKV_WGS + nu) * TILE_KV * ub * 576 * 4);
+    }
     if (atomic) {
       p.off_acc32 = o;
       o = align256(o + (size_t)p.NB * TILE_KV * 576 * 4);
@@ -319,6 +325,8 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   ba.scale_log2 = sm_scale * 1.4426950408889634f;
   ba.G = p.G;
   ba.NB = p.NB;
+  ba.ub = stored_p ? 2 : 1;
+  ba.NU = (p.NB + ba.ub - 1) / ba.ub;
   ba.qcap = p.qcap;
   ba.rcap = p.rcap;
   ba.qcount = pa.qcount;

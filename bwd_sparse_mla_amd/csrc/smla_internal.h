@@ -78,6 +78,8 @@ struct BwdArgs {
   int64_t s_q, s_kv;
   float scale, scale_log2;
   int64_t G, NB, qcap, rcap;
+  int64_t NU;         // dkv units: kv blocks (NB) or, in the stored-P form, pairs of blocks
+  int ub;             // kv blocks per dkv unit: 1, or 2 in the stored-P form
   const int* qcount;
   const int* xcount;
   const int* xtotal;
@@ -86,19 +88,20 @@ struct BwdArgs {
   const int2* ktab;
   const unsigned long long* krmask;
   const int* gorder;  // [G] groups by decreasing union size (dq pass)
-  int* spre;          // [NB + 1] dkv sub-chunks before each block (exclusive prefix; [NB] = total)
-  int* wstart;        // [DKV_WGS] first kv block of each dkv workgroup's range
+  int* spre;          // [NU + 1] dkv sub-chunks before each unit (exclusive prefix; [NU] = total)
+  int* wstart;        // [DKV_WGS] first dkv unit of each dkv workgroup's range
   float* delta;       // [s_q * H] rowsum(dout * out), written by the dq pass
-  int2* clist;        // [NB, G] per block: (group, record start), compacted
+  int2* clist;        // [NU, G] per unit: (group, record start), compacted
   const int* kbase;   // [NB, G] from the planner (stored-P mode)
   const unsigned long long* korm;   // [NB, G] from the planner (stored-P mode)
-  int* cbase;         // [NB, G] parallel to clist: the chunk's first union entry (stored-P mode)
-  unsigned long long* cmask;   // [NB, G] parallel to clist: the block rows the chunk selects
+  int* cbase;         // [NU, G, 2] parallel to clist: per block of the unit, the chunk's first
+                      // union entry there (stored-P form)
+  unsigned long long* cmask;   // [NU, G, 2] parallel to clist: per block, the rows the chunk selects
   uint16_t* pds;      // stored-P mode: [G, qcap, 2, 64] bf16 P and scale * dS per union entry and
                       // group row, written by the dq pass and read by the dkv pass; else null
-  int* nchunk;        // [NB] entries of clist per block
-  float* part;        // [DKV_WGS + NB, 64, 576] fp32 partial dkv per (workgroup w, block b): slot w + b
-  unsigned long long* ptouch;  // [DKV_WGS + NB] rows each partial touched
+  int* nchunk;        // [NU] entries of clist per unit
+  float* part;        // [DKV_WGS + NU, 64 ub, 576] fp32 partial dkv per (workgroup w, unit u): slot w + u
+  unsigned long long* ptouch;  // [DKV_WGS + NU, 2] rows each partial touched (per 64-row block)
   float* acc32;       // atomic mode: [NB * 64, 576] fp32 dkv accumulated with atomics; else null
   uint16_t* dq;
   uint16_t* dkv;      // may be null
