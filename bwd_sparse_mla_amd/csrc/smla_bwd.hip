@@ -33,6 +33,47 @@ namespace smla {
 
 namespace {
 
+// Compacts each dkv unit's column of the [block, group] record table into
+// the unit's chunk list (groups with records for the unit, ascending).  In
+// the stored-P form a unit is a pair of blocks: a group with records in
+// either block is a chunk, with, per block, its first union entry there and
+// the rows it selects (zero where it has none).
+__device__ __forceinline__ void dkv_schedule_unit(const BwdArgs& a, int64_t unit) {
+  __shared__ int scratch[8];
+  const int tid = threadIdx.x;
+  int base = 0;
+  for (int64_t gb = 0; gb < a.G; gb += 256) {
+    const int64_t g = gb + tid;
+    int2 e = make_int2(0, 0), e1 = make_int2(0, 0);
+    if (a.ub == 2) {
+      if (g < a.G) e = a.ktab[(2 * unit) * a.G + g];
+      if (g < a.G && 2 * unit + 1 < a.NB) e1 = a.ktab[(2 * unit + 1) * a.G + g];
+    } else if (g < a.G) {
+      e = a.ktab[unit * a.G + g];
+    }
+    const int nz = (e.y > 0 || e1.y > 0) ? 1 : 0;
+    int total;
+    const int pos = base + block_exclusive_scan256(nz, scratch, &total);
+    if (nz) {
+      a.clist[unit * a.G + pos] = make_int2((int)g, e.x);
+      if (a.ub == 2) {   // stored-P form: per block, the first union entry and the rows
+        const int64_t c = unit * a.G + pos;
+        const int64_t k0 = (2 * unit) * a.G + g, k1 = (2 * unit + 1) * a.G + g;
+        a.cbase[2 * c] = e.y > 0 ? a.kbase[k0] : 0;
+        a.cmask[2 * c] = e.y > 0 ? a.korm[k0] : 0ull;
+        a.cbase[2 * c + 1] = e1.y > 0 ? a.kbase[k1] : 0;
+        a.cmask[2 * c + 1] = e1.y > 0 ? a.korm[k1] : 0ull;
+      }
+    }
+    base += total;
+  }
+  if (tid == 0) a.nchunk[unit] = base;
+}
+
+__global__ __launch_bounds__(256) void dkv_schedule_kernel(BwdArgs a) {
+  dkv_schedule_unit(a, blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // dq pass
 // ---------------------------------------------------------------------------
@@ -54,11 +95,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) int sRow[2][64];   // kv row indices of a tile's entries
   __shared__ float sDelta[GROUP_ROWS];
   __shared__ float sLse2[GROUP_ROWS];
+  // stored-P form: the tile's P and scale * dS as [entry, {P, dS}, 64 rows]
+  // bf16, the layout of the workspace, for one contiguous 8 KB copy out
+  __shared__ __attribute__((aligned(16))) unsigned short sPDS[DQ_TILE * 2 * GROUP_ROWS];
 
+  // The first NU workgroups build the dkv pass's chunk lists (they depend on
+  // the plan only, so they run beside the dq work instead of in a launch of
+  // their own).
+  if ((int64_t)blockIdx.x < a.NU) {
+    dkv_schedule_unit(a, blockIdx.x);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, r16 = lane & 15;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int64_t grp = a.gorder[blockIdx.x];
+  const int64_t grp = a.gorder[blockIdx.x - a.NU];
   const int64_t t0 = grp * T;
   const int n_ent = a.qcount[grp];
   const int32_t* erow = a.qrow + grp * a.qcap;
@@ -166,31 +217,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
       s[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
       dp[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
     }
-    // K fragments (and this wave's dout fragment) one k-step ahead of their
-    // MFMAs; the scheduling barriers keep the reads from sinking onto their
-    // uses.
-    short8_t kc[2], kn[2], dc, dn;
+    // K fragments (and this wave's dout fragments) KPF k-steps ahead of
+    // their MFMAs (a ring of KPF + 1 register sets); the scheduling barriers
+    // keep the reads from sinking onto their uses.
+    constexpr int KPF = 3;
+    short8_t kb[KPF + 1][2], db[KPF + 1];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) kc[nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 0, lane);
-    dc = ld_b_rs<GROUP_ROWS>(sDO, 16 * wave, 0, lane);   // A fragments of dout
+    for (int d = 0; d < KPF; ++d) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) kb[d][nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * d, lane);
+      db[d] = ld_b_rs<GROUP_ROWS>(sDO, 16 * wave, 32 * d, lane);   // A fragments of dout
+    }
     static_for<18>([&](auto KS) __attribute__((always_inline)) {
       constexpr int ks = decltype(KS)::value;
-      if constexpr (ks + 1 < 18) {
+      constexpr int cur = ks % (KPF + 1), nxt = (ks + KPF) % (KPF + 1);
+      if constexpr (ks + KPF < 18) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) kn[nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * (ks + 1), lane);
-        if constexpr (ks + 1 < 16) dn = ld_b_rs<GROUP_ROWS>(sDO, 16 * wave, 32 * (ks + 1), lane);
+        for (int nt = 0; nt < 2; ++nt) kb[nxt][nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * (ks + KPF), lane);
+        if constexpr (ks + KPF < 16) db[nxt] = ld_b_rs<GROUP_ROWS>(sDO, 16 * wave, 32 * (ks + KPF), lane);
       }
       if constexpr (ks % 2 == 0) kv_gather_copy<DQ_TILE, ks / 2>(gnext, wv, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        s[nt] = mfma_bf16(kc[nt], qf[ks], s[nt]);
-        if constexpr (ks < 16) dp[nt] = mfma_bf16(kc[nt], dc, dp[nt]);
+        s[nt] = mfma_bf16(kb[cur][nt], qf[ks], s[nt]);
+        if constexpr (ks < 16) dp[nt] = mfma_bf16(kb[cur][nt], db[cur], dp[nt]);
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) kc[nt] = kn[nt];
-      dc = dn;
     });
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -207,28 +260,43 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
       pk.y = pack_bf2(d[2], d[3]);
       *reinterpret_cast<uint2*>(&sdS[(16 * wave + r16) * SDS + nt * 16 + 4 * g16]) = pk;
       if (a.pds) {
-        // Stored-P mode: P and scale * dS of the lane's row for its four
-        // entries, for the dkv pass ([group, entry, {P, dS}, 64 rows] bf16).
-        uint16_t* dst = a.pds + ((grp * a.qcap + tile * DQ_TILE + nt * 16 + 4 * g16) * 2) * GROUP_ROWS +
-                        16 * wave + r16;
+        // Stored-P form: P and scale * dS of the lane's row for its four
+        // entries, staged in LDS in the workspace's layout.
+        unsigned short* st = sPDS + (nt * 16 + 4 * g16) * 2 * GROUP_ROWS + 16 * wave + r16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          dst[i * 2 * GROUP_ROWS] = f2bf(pr[i]);
-          dst[i * 2 * GROUP_ROWS + GROUP_ROWS] = f2bf(d[i] * a.scale);
+          st[i * 2 * GROUP_ROWS] = f2bf(pr[i]);
+          st[i * 2 * GROUP_ROWS + GROUP_ROWS] = f2bf(d[i] * a.scale);
         }
       }
     }
     __syncthreads();
+    if (a.pds) {   // the tile's 32 entries x 256 bytes, contiguous in the workspace
+      uint4_t* dst = reinterpret_cast<uint4_t*>(a.pds + (grp * a.qcap + tile * DQ_TILE) * 2 * GROUP_ROWS);
+      const uint4_t* src = reinterpret_cast<const uint4_t*>(sPDS);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) dst[tid + 256 * k] = src[tid + 256 * k];
+    }
     short8_t dsa[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) dsa[rb] = ld16_lds(&sdS[(16 * rb + r16) * SDS + 8 * g16]);
     // Column blocks n < 8: 128 w + 16 n; block 8: tail columns 512 + 16 w.
+    // The transposed K fragments run two column blocks ahead of their MFMAs.
+    auto kt_frag = [&](int n) __attribute__((always_inline)) {
+      return n < 8 ? ld_bt_rs_lo<DQ_TILE>(kt, 0, 128 * wave + 16 * n, lane)
+                   : ld_bt_rs_hi<DQ_TILE>(kt, 0, D_V + 16 * wave, lane);
+    };
+    constexpr int BPF = 2;
+    short8_t bb[BPF + 1];
+#pragma unroll
+    for (int d = 0; d < BPF; ++d) bb[d] = kt_frag(d);
 #pragma unroll
     for (int n = 0; n < 9; ++n) {
-      const short8_t b = n < 8 ? ld_bt_rs_lo<DQ_TILE>(kt, 0, 128 * wave + 16 * n, lane)
-                               : ld_bt_rs_hi<DQ_TILE>(kt, 0, D_V + 16 * wave, lane);
+      if (n + BPF < 9) bb[(n + BPF) % (BPF + 1)] = kt_frag(n + BPF);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(dsa[rb], b, acc[rb][n]);
+      for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(dsa[rb], bb[n % (BPF + 1)], acc[rb][n]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -735,44 +803,6 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
   }
 }
 
-// Compacts each dkv unit's column of the [block, group] record table into
-// the unit's chunk list (groups with records for the unit, ascending).  In
-// the stored-P form a unit is a pair of blocks: a group with records in
-// either block is a chunk, with, per block, its first union entry there and
-// the rows it selects (zero where it has none).
-__global__ __launch_bounds__(256) void dkv_schedule_kernel(BwdArgs a) {
-  __shared__ int scratch[8];
-  const int64_t unit = blockIdx.x;
-  const int tid = threadIdx.x;
-  int base = 0;
-  for (int64_t gb = 0; gb < a.G; gb += 256) {
-    const int64_t g = gb + tid;
-    int2 e = make_int2(0, 0), e1 = make_int2(0, 0);
-    if (a.ub == 2) {
-      if (g < a.G) e = a.ktab[(2 * unit) * a.G + g];
-      if (g < a.G && 2 * unit + 1 < a.NB) e1 = a.ktab[(2 * unit + 1) * a.G + g];
-    } else if (g < a.G) {
-      e = a.ktab[unit * a.G + g];
-    }
-    const int nz = (e.y > 0 || e1.y > 0) ? 1 : 0;
-    int total;
-    const int pos = base + block_exclusive_scan256(nz, scratch, &total);
-    if (nz) {
-      a.clist[unit * a.G + pos] = make_int2((int)g, e.x);
-      if (a.ub == 2) {   // stored-P form: per block, the first union entry and the rows
-        const int64_t c = unit * a.G + pos;
-        const int64_t k0 = (2 * unit) * a.G + g, k1 = (2 * unit + 1) * a.G + g;
-        a.cbase[2 * c] = e.y > 0 ? a.kbase[k0] : 0;
-        a.cmask[2 * c] = e.y > 0 ? a.korm[k0] : 0ull;
-        a.cbase[2 * c + 1] = e1.y > 0 ? a.kbase[k1] : 0;
-        a.cmask[2 * c + 1] = e1.y > 0 ? a.korm[k1] : 0ull;
-      }
-    }
-    base += total;
-  }
-  if (tid == 0) a.nchunk[unit] = base;
-}
-
 // Sub-chunk prefix over the dkv units (spre[b] = sub-chunks of units before b,
 // spre[NU] = total) and the first block of each dkv workgroup's range.  Two
 // passes of the same scan: the second finds, for every block, the
@@ -945,7 +975,7 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream) {
   if (a.G == 0) return hipSuccess;
-  dim3 grid((unsigned)a.G), block(256);
+  dim3 grid((unsigned)(a.NU + a.G)), block(256);   // NU schedule workgroups, then the groups
   switch (heads) {
     case 8: bwd_dq_kernel<8><<<grid, block, 0, stream>>>(a); break;
     case 16: bwd_dq_kernel<16><<<grid, block, 0, stream>>>(a); break;
@@ -956,11 +986,13 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_dkv_schedule(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_dkv_schedule(const BwdArgs& a, bool lists_built, hipStream_t stream) {
   if (a.NB == 0) return hipSuccess;
-  dkv_schedule_kernel<<<dim3((unsigned)a.NU), dim3(256), 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!lists_built) {   // no dq launch built them (an empty query batch)
+    dkv_schedule_kernel<<<dim3((unsigned)a.NU), dim3(256), 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   dkv_prefix_kernel<<<dim3(1), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }

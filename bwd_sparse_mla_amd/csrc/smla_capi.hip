@@ -355,7 +355,7 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   ba.dkv_f32 = dkv_f32;
   ba.accumulate = (flags & SMLA_DKV_ACCUMULATE) ? 1 : 0;
   if (s_q > 0 && (st = hip_status(timed("bwd_dq", s, [&] { return launch_bwd_dq(ba, heads, s); }), "bwd_dq"))) return st;
-  if ((st = hip_status(timed("dkv_schedule", s, [&] { return launch_dkv_schedule(ba, s); }), "dkv_schedule"))) return st;
+  if ((st = hip_status(timed("dkv_schedule", s, [&] { return launch_dkv_schedule(ba, s_q > 0, s); }), "dkv_schedule"))) return st;
   if (atomic && (st = hip_status(timed("dkv_clear", s, [&] {
                    return launch_fill_u32(ba.acc32, (size_t)p.NB * TILE_KV * 576, 0u, s);
                  }), "dkv_clear")))

@@ -127,7 +127,9 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream);
 hipError_t launch_order_groups(const int* qcount, const int* xcount, int64_t G, int* order, int* xtotal,
                                hipStream_t stream);
 // dkv pass: schedule (chunk lists and work order), main kernel, finalize.
-hipError_t launch_dkv_schedule(const BwdArgs& a, hipStream_t stream);
+// The chunk lists are built by the first workgroups of the dq launch; with no
+// dq launch (s_q == 0) lists_built is false and a kernel of their own does it.
+hipError_t launch_dkv_schedule(const BwdArgs& a, bool lists_built, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdArgs& a, int heads, hipStream_t stream);
 hipError_t launch_dkv_finalize(const BwdArgs& a, int heads, hipStream_t stream);
 // dkv split schedule: chunks a split covers at least, and the split count.
