@@ -853,7 +853,7 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // some index row repeats an entry -- the extra slots' contributions, each
 // computed directly in (group, slot) order.  Output semantics (bf16, fp32,
 // accumulate, rows no slot selects) are applied here.  Bitwise reproducible.
-constexpr int FIN_ROWS = 4;
+constexpr int FIN_ROWS = 2;
 constexpr int FIN_PARTS = TILE_KV / FIN_ROWS;   // workgroups per block
 template <int H>
 __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
@@ -927,20 +927,19 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
   constexpr int N4 = FIN_ROWS * D_K / 4;  // float4 elements of the rows
   const int64_t SPLIT = unit_rows * D_K;
   for (int e = tid; e < N4; e += 256) {
-    // Partials summed left to right in workgroup order; loads go out four
+    // Partials summed left to right in workgroup order; loads go out eight
     // at a time (indices clamped into range, extra ones unused).  A block no
     // record touches has no partial: zeros.
     const float* pe = src + 4 * e;
     float4_t v = nsrc > 0 ? *reinterpret_cast<const float4_t*>(pe) : (float4_t){0.f, 0.f, 0.f, 0.f};
-    for (int sp = 1; sp < nsrc; sp += 4) {
-      const float4_t p0 = *reinterpret_cast<const float4_t*>(pe + sp * SPLIT);
-      const float4_t p1 = *reinterpret_cast<const float4_t*>(pe + min(sp + 1, nsrc - 1) * SPLIT);
-      const float4_t p2 = *reinterpret_cast<const float4_t*>(pe + min(sp + 2, nsrc - 1) * SPLIT);
-      const float4_t p3 = *reinterpret_cast<const float4_t*>(pe + min(sp + 3, nsrc - 1) * SPLIT);
-      v += p0;
-      if (sp + 1 < nsrc) v += p1;
-      if (sp + 2 < nsrc) v += p2;
-      if (sp + 3 < nsrc) v += p3;
+    for (int sp = 1; sp < nsrc; sp += 8) {
+      float4_t pp[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        pp[j] = *reinterpret_cast<const float4_t*>(pe + min(sp + j, nsrc - 1) * SPLIT);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (sp + j < nsrc) v += pp[j];
     }
     if (extras) v += *reinterpret_cast<const float4_t*>(sX + 4 * e);
     const int kvl = (4 * e) / D_K;
