@@ -627,17 +627,25 @@ __device__ __forceinline__ void dkv_segment(const BwdArgs& a, int64_t blk, int u
 // copies (Q, dout into the other buffers; its P / dS pieces into
 // registers), sync, and run the dK / dV contraction: wave w takes kv rows
 // 64 (w & 1) .. +63 (four 16-row blocks) and the column blocks of w >> 1.
+// P^T / dS^T tiles of the stored-P form: 128 kv rows x 32 query rows (bf16),
+// 64 bytes per row, with 16-byte chunk c of row r at 64-byte group
+// 4 (r / 4) + (c ^ (r / 4 mod 4)), slot r mod 4 (offsets in bf16 units).  A
+// fragment read (16 rows, one chunk) then keeps each quad of lanes inside one
+// aligned 64-byte bank group and 16 lanes on all 64 banks.
+__device__ __forceinline__ int pt_off(int r, int c) {
+  return 32 * (4 * (r >> 2) + (c ^ ((r >> 2) & 3))) + 8 * (r & 3);
+}
+
 struct DkvPairLds {
   __attribute__((aligned(16))) char sQ[2][KV32_TILE_BYTES];
   __attribute__((aligned(16))) char sD[2][DO32_TILE_BYTES];
-  __attribute__((aligned(16))) unsigned short sPT[2 * TILE_KV * DKV_SP];
-  __attribute__((aligned(16))) unsigned short sDST[2 * TILE_KV * DKV_SP];
+  __attribute__((aligned(16))) unsigned short sPT[2 * TILE_KV * DKV_SUB];
+  __attribute__((aligned(16))) unsigned short sDST[2 * TILE_KV * DKV_SUB];
 };
 
 template <int H>
 __device__ __forceinline__ void dkv_segment_pair(const BwdArgs& a, int64_t unit, int u0, int u1,
                                                  int64_t slot, DkvPairLds& lds) {
-  constexpr int SP = DKV_SP;
   constexpr int UR = 2 * TILE_KV;   // kv rows per unit
   auto& sQ = lds.sQ;
   auto& sD = lds.sD;
@@ -708,9 +716,9 @@ __device__ __forceinline__ void dkv_segment_pair(const BwdArgs& a, int64_t unit,
     wait_vmcnt0();
     __syncthreads();
     {
-      unsigned short* st = (pr_part < 4 ? sPT : sDST) + pr_row * SP + 8 * (pr_part & 3);
-      *reinterpret_cast<short8_t*>(st) = piece0;
-      *reinterpret_cast<short8_t*>(st + TILE_KV * SP) = piece1;
+      unsigned short* st = pr_part < 4 ? sPT : sDST;
+      *reinterpret_cast<short8_t*>(st + pt_off(pr_row, pr_part & 3)) = piece0;
+      *reinterpret_cast<short8_t*>(st + pt_off(TILE_KV + pr_row, pr_part & 3)) = piece1;
     }
     touched0 |= c_cur.m0;
     touched1 |= c_cur.m1;
@@ -731,8 +739,8 @@ __device__ __forceinline__ void dkv_segment_pair(const BwdArgs& a, int64_t unit,
     short8_t ad[4], ap[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      ad[rb] = ld16_lds(&sDST[(64 * drh + 16 * rb + r16) * SP + 8 * g16]);
-      ap[rb] = ld16_lds(&sPT[(64 * drh + 16 * rb + r16) * SP + 8 * g16]);
+      ad[rb] = ld16_lds(&sDST[pt_off(64 * drh + 16 * rb + r16, g16)]);
+      ap[rb] = ld16_lds(&sPT[pt_off(64 * drh + 16 * rb + r16, g16)]);
     }
     const int col0 = 128 * dcq;
     short8_t bq = ld_bt_rs_lo<DKV_SUB>(sq, 0, col0, lane);
