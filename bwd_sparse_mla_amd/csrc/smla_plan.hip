@@ -30,6 +30,7 @@ constexpr int WIN_BITS = 16384;            // kv rows per bitmap window
 constexpr int WIN_WORDS = WIN_BITS / 32;   // 512: two per thread
 constexpr int WIN_BLOCKS = WIN_BITS / 64;  // 256: one per thread
 constexpr int XFLAG_WORDS = 4096;          // T * topk <= 8 * 16384 slots
+constexpr int PLAN_LOADS = 16;             // index loads in flight per thread
 
 __device__ __forceinline__ int wave_min(int v) {
 #pragma unroll
@@ -72,12 +73,16 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   if (skv > WIN_BITS) {
     lo = 0x7fffffff;
     hi = -1;
-    for (int s = tid; s < nslots; s += 256) {
-      const int v = ix[s];
-      if (v >= 0 && v < skv) {
-        lo = min(lo, v);
-        hi = max(hi, v);
-      }
+    for (int s0 = tid; s0 < nslots; s0 += 256 * 16) {   // 16 loads in flight per thread
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = s0 + 256 * j < nslots ? ix[s0 + 256 * j] : -1;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (v[j] >= 0 && v[j] < skv) {
+          lo = min(lo, v[j]);
+          hi = max(hi, v[j]);
+        }
     }
     lo = wave_min(lo);
     hi = wave_max(hi);
@@ -108,16 +113,16 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     const int qbase0 = qbase;   // union entries before this window
     for (int i = tid; i < T * WIN_WORDS; i += 256) (&bm[0][0])[i] = 0u;
     __syncthreads();
-    // 16 index loads in flight per thread before their bitmap updates.
-    for (int s0 = tid; s0 < nslots; s0 += 256 * 16) {
-      int v[16];
+    // PLAN_LOADS index loads in flight per thread before their bitmap updates.
+    for (int s0 = tid; s0 < nslots; s0 += 256 * PLAN_LOADS) {
+      int v[PLAN_LOADS];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < PLAN_LOADS; ++j) {
         const int s = s0 + 256 * j;
         v[j] = s < nslots ? ix[s] : -1;
       }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < PLAN_LOADS; ++j) {
         const int s = s0 + 256 * j;
         if (v[j] >= w0 && v[j] < w0 + WIN_BITS && v[j] < skv) {
           const int t = s / K;
