@@ -88,12 +88,11 @@ template <int H>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
   constexpr int SDS = DQ_TILE + 8;  // dS row stride (bf16): 80 bytes, conflict-free reads
-  // Three tile buffers: tile t lives in buffer t % 3, and its copies are
-  // issued two tiles ahead (during tile t - 2).
-  __shared__ __attribute__((aligned(16))) char sK[3][KV32_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sK[2][KV32_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sDO[GROUP_ROWS * D_V * 2];   // swizzled 64-row tile
   __shared__ __attribute__((aligned(16))) unsigned short sdS[GROUP_ROWS * SDS];
-  __shared__ __attribute__((aligned(16))) unsigned char sMask[3][256];   // token masks (copied as words)
-  __shared__ __attribute__((aligned(16))) int sRow[3][64];   // kv row indices of a tile's entries
+  __shared__ __attribute__((aligned(16))) unsigned char sMask[2][256];   // token masks (copied as words)
+  __shared__ __attribute__((aligned(16))) int sRow[2][64];   // kv row indices of a tile's entries
   __shared__ float sDelta[GROUP_ROWS];
   __shared__ float sLse2[GROUP_ROWS];
   // stored-P form: the tile's P and scale * dS as [entry, {P, dS}, 64 rows]
@@ -117,30 +116,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   const uint8_t* emask = a.qmask + grp * a.qcap;
   const int ntiles = (n_ent + DQ_TILE - 1) / DQ_TILE;
 
-  // Row indices of tiles 0 and 1, in the same round trip.
+  // dout rows of the group (contiguous: token-major, then head) into a
+  // swizzled 64-row tile, 16 row copies per wave; rows past the sequence end
+  // read the zero row.
+  gather_seq_rows<GROUP_ROWS, DO_CHUNKS>(sDO, a.dout + t0 * H * D_V,
+                                         (int)min<int64_t>(GROUP_ROWS, (a.s_q - t0) * H), wv, lane);
+  // Row indices and masks of tile 0 and the row indices of tile 1, in the
+  // same round trip.
   if (ntiles > 0) {
-    copy_union_entries(sRow[0], nullptr, erow, emask, 0, n_ent, DQ_TILE, wv, 0, 0, lane);
-    copy_union_entries(sRow[1], nullptr, erow, emask, DQ_TILE, n_ent, DQ_TILE, wv, 2, 2, lane);
+    copy_union_entries(sRow[0], sMask[0], erow, emask, 0, n_ent, DQ_TILE, wv, 0, 1, lane);
+    if (ntiles > 1) copy_union_entries(sRow[1], nullptr, erow, emask, DQ_TILE, n_ent, DQ_TILE, wv, 2, 2, lane);
   }
-  // The wave's 16 rows of Q (18 fragments) and of dout (16), held in
-  // registers for the whole group as the B operands of S^T and dP^T; rows
-  // past the sequence end are zero.
-  short8_t qf[18], df[16];
+  short8_t qf[18];
   {
     const int rr = 16 * wave + r16;
     const int64_t tok = t0 + rr / H;
     if (tok < a.s_q) {
       const uint16_t* qrow = a.q + (tok * H + rr % H) * D_K + 8 * g16;
-      const uint16_t* drow = a.dout + (tok * H + rr % H) * D_V + 8 * g16;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) qf[ks] = ld16_global(qrow + 32 * ks);
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) df[ks] = ld16_global(drow + 32 * ks);
     } else {
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) qf[ks] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) df[ks] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
   // delta = rowsum(dout * out) for the group's 64 rows: 4 threads per row,
@@ -189,68 +186,62 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  // The copies that make tile t ready, issued during tile t - 2 (the first
-  // two in the prologue): the masks of tile t (wave 1), the row indices of
-  // tile t + 2 (wave 2), and the 9 kv copies of every wave (rows of entries
-  // past the union, and whole tiles past the last, read the zero row).  The
-  // count of vector-memory operations a wave issues per tile is fixed: 9,
-  // plus one for waves 1 and 2, plus the 2 stores of the stored-P copy-out,
-  // so a tile's wait leaves exactly the previous tile's operations in flight.
-  auto issue_meta = [&](int t) __attribute__((always_inline)) {
-    copy_union_entries(nullptr, sMask[t % 3], erow, emask, t * DQ_TILE, n_ent, DQ_TILE, wv, 1, 1, lane);
-    copy_union_entries(sRow[(t + 2) % 3], nullptr, erow, emask, (t + 2) * DQ_TILE, n_ent, DQ_TILE, wv, 2,
-                       2, lane);
+  // kv rows of tile 0 (count entries at rows_t in LDS) into a swizzled
+  // 32-row tile.
+  auto gather = [&](char* kbuf, const int* rows_t, int count) __attribute__((always_inline)) {
+    gather_kv_rows<DQ_TILE, ROW_CHUNKS>(kbuf, a.kv, a.s_kv, rows_t, count, wv, lane);
   };
-  auto prepare = [&](int t) __attribute__((always_inline)) {
-    return kv_gather_prepare<DQ_TILE>(sK[t % 3], a.kv, a.s_kv, sRow[t % 3],
-                                      max(0, min(DQ_TILE, n_ent - t * DQ_TILE)), wv, lane);
-  };
-  const bool meta_wave = wv == 1 || wv == 2;
 
-  auto step = [&](int tile) __attribute__((always_inline)) {
-    const char* kt = sK[tile % 3];
-    const unsigned char* mkb = sMask[tile % 3];
-    // Tile `tile`'s copies were issued two tiles ago: wait until only the
-    // previous tile's operations are in flight.
-    if (tile > 0 && a.pds) {
-      if (meta_wave) wait_vmcnt<12>(); else wait_vmcnt<11>();
-    } else {
-      if (meta_wave) wait_vmcnt<10>(); else wait_vmcnt<9>();
-    }
+  auto step = [&](int tile, const char* kt, const unsigned char* mkb, char* knext,
+                  unsigned char* mnext, const int* rnext, int* rcur) __attribute__((always_inline)) {
+    wait_vmcnt0();
     __syncthreads();
-    // Copies of tile + 2 into the buffers tile - 1 used (free: every wave has
-    // passed the barrier above): masks and row indices now, the kv copies
-    // spread over the score loop below.
-    issue_meta(tile + 2);
-    const KvGather<DQ_TILE> gnext = prepare(tile + 2);
+    // Prefetch into the other buffers (free: every wave has passed the
+    // barrier above, so the previous tile's reads are done): masks of tile+1
+    // and row indices of tile+2 now, the 9 kv copies of tile+1 spread over
+    // the score loop below (after the last tile they read the zero row into
+    // the spare buffer, which nothing reads).
+    const bool pre = tile + 1 < ntiles;
+    if (pre) {
+      copy_union_entries(nullptr, mnext, erow, emask, (tile + 1) * DQ_TILE, n_ent, DQ_TILE, wv, 1, 1,
+                         lane);
+      if (tile + 2 < ntiles)
+        copy_union_entries(rcur, nullptr, erow, emask, (tile + 2) * DQ_TILE, n_ent, DQ_TILE, wv, 2, 2,
+                           lane);
+    }
+    const KvGather<DQ_TILE> gnext = kv_gather_prepare<DQ_TILE>(
+        knext, a.kv, a.s_kv, rnext, pre ? min(DQ_TILE, n_ent - (tile + 1) * DQ_TILE) : 0, wv, lane);
     float4_t s[2], dp[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       s[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
       dp[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
     }
-    // K fragments KPF k-steps ahead of their MFMAs (a ring of KPF + 1
-    // register sets); the scheduling barriers keep the reads from sinking
-    // onto their uses.
+    // K fragments (and this wave's dout fragments) KPF k-steps ahead of
+    // their MFMAs (a ring of KPF + 1 register sets); the scheduling barriers
+    // keep the reads from sinking onto their uses.
     constexpr int KPF = 3;
-    short8_t kb[KPF + 1][2];
+    short8_t kb[KPF + 1][2], db[KPF + 1];
 #pragma unroll
-    for (int d = 0; d < KPF; ++d)
+    for (int d = 0; d < KPF; ++d) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) kb[d][nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * d, lane);
+      db[d] = ld_b_rs<GROUP_ROWS>(sDO, 16 * wave, 32 * d, lane);   // A fragments of dout
+    }
     static_for<18>([&](auto KS) __attribute__((always_inline)) {
       constexpr int ks = decltype(KS)::value;
       constexpr int cur = ks % (KPF + 1), nxt = (ks + KPF) % (KPF + 1);
       if constexpr (ks + KPF < 18) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) kb[nxt][nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * (ks + KPF), lane);
+        if constexpr (ks + KPF < 16) db[nxt] = ld_b_rs<GROUP_ROWS>(sDO, 16 * wave, 32 * (ks + KPF), lane);
       }
       if constexpr (ks % 2 == 0) kv_gather_copy<DQ_TILE, ks / 2>(gnext, wv, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         s[nt] = mfma_bf16(kb[cur][nt], qf[ks], s[nt]);
-        if constexpr (ks < 16) dp[nt] = mfma_bf16(kb[cur][nt], df[ks], dp[nt]);
+        if constexpr (ks < 16) dp[nt] = mfma_bf16(kb[cur][nt], db[cur], dp[nt]);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -309,17 +300,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  if (ntiles > 0) {   // the copies of tiles 0 and 1 (row indices landed before the barrier above)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      issue_meta(t);
-      const KvGather<DQ_TILE> g = prepare(t);
-      static_for<DQ_TILE / 4 + DQ_TILE / 32>([&](auto J) __attribute__((always_inline)) {
-        kv_gather_copy<DQ_TILE, decltype(J)::value>(g, wv, lane);
-      });
-    }
+  if (ntiles > 0) gather(sK[0], sRow[0], min(DQ_TILE, n_ent));   // indices landed before the barrier above
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int b = tile & 1;
+    step(tile, sK[b], sMask[b], sK[b ^ 1], sMask[b ^ 1], sRow[b ^ 1], sRow[b]);
   }
-  for (int tile = 0; tile < ntiles; ++tile) step(tile);
 
   // Epilogue: dq = scale * acc, staged through LDS in two halves of 32 rows
   // (sK[0] holds rows 0..31, sK[1] rows 32..63), then 16-byte stores (the

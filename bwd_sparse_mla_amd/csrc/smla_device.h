@@ -198,13 +198,6 @@ __device__ __forceinline__ void static_for(F&& f) { static_for_from<0, N>(f); }
 
 // s_waitcnt vmcnt(0) (other counters untouched).
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// s_waitcnt vmcnt(N), N < 16: at most the N most recent vector-memory
-// operations of the wave still in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
 
 // Reductions across the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
 // with the gfx950 row-swap instructions (VALU, no LDS round trip).
