@@ -141,24 +141,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     }
   }
   // delta = rowsum(dout * out) for the group's 64 rows: 4 threads per row,
-  // thread p of a row takes chunks p, p+4, ... (four threads read 64
-  // contiguous bytes per load); all 32 loads are issued before the sums.
+  // thread p of a row takes chunks p, p+4, ... of out (four threads read 64
+  // contiguous bytes per load; all 16 loads are issued at once) and the same
+  // chunks of dout from the LDS tile once its copies have landed.
   {
     const int row = tid >> 2, part = tid & 3;
     const int64_t tok = t0 + row / H;
-    float d = 0.f;
+    short8_t y[16];
+    float lse_row = 0.f;
     if (tok < a.s_q) {
       const int64_t o = (tok * H + row % H) * D_V + 8 * part;
-      short8_t x[16], y[16];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        x[c] = ld16_global(a.dout + o + 32 * c);
-        y[c] = ld16_global(a.out + o + 32 * c);
-      }
+      for (int c = 0; c < 16; ++c) y[c] = ld16_global(a.out + o + 32 * c);
+      lse_row = a.lse[tok * H + row % H];
+    } else {
 #pragma unroll
-      for (int c = 0; c < 16; ++c)
+      for (int c = 0; c < 16; ++c) y[c] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    wait_vmcnt0();
+    __syncthreads();   // the dout tile (and the tile-0 indices) are in LDS
+    float d = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) d += bf2f((unsigned short)x[c][j]) * bf2f((unsigned short)y[c][j]);
+    for (int c = 0; c < 16; ++c) {
+      const int gc = part + 4 * c;   // 16-byte chunk of the row
+      const short8_t x = ld16_lds(sDO + row * 1024 + 16 * (gc ^ swz_lo(row)));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) d += bf2f((unsigned short)x[j]) * bf2f((unsigned short)y[c][j]);
     }
     d += __shfl_xor(d, 1);
     d += __shfl_xor(d, 2);
@@ -167,12 +175,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
       float l2 = 0.f;
       if (tok < a.s_q) {
         a.delta[tok * H + row % H] = d;
-        l2 = a.lse[tok * H + row % H] * LOG2E;
+        l2 = lse_row * LOG2E;
       }
       sLse2[row] = l2;
     }
   }
-  wait_vmcnt0();
   __syncthreads();
   // Scores and dP are computed transposed (K Q^T, K dO^T): lane (g, r) of
   // wave w holds row 16w + r of the group and kv entries 16nt + 4g + i.
