@@ -104,3 +104,20 @@ def test_stored_p_with_the_plan_built_once():
     torch.cuda.synchronize()
     assert torch.equal(dq.view(torch.int16), dq_s.view(torch.int16))
     assert torch.equal(dkv.view(torch.int16), dkv_s.view(torch.int16))
+
+
+@pytest.mark.parametrize("atomic", [False, True])
+def test_stored_p_empty_query_batch(atomic):
+    """No query rows: no dq launch builds the chunk lists, the schedule kernel
+    runs on its own, and dkv is all zeros (kv blocks of an odd count)."""
+    import bwd_sparse_mla_amd as smla
+    w = synth.custom(S=4, H=8, K=4, S_kv=70, seed=15)
+    print(f"[stored-p] empty batch atomic={atomic}", flush=True)
+    q, kv, dout, idx = gpu_inputs(w)
+    out, lse = smla.sparse_mla_fwd(q[:0], kv, idx[:0], w.sm_scale)
+    d32 = torch.full((w.S_kv, 576), 7.0, dtype=torch.float32, device="cuda")
+    dq, dkv = smla.sparse_mla_bwd(q[:0], kv, out, dout[:0], idx[:0], lse, w.sm_scale, dkv_f32=d32,
+                                  stored_p=True, atomic=atomic)
+    torch.cuda.synchronize()
+    assert dq.shape == (0, 8, 576)
+    assert torch.count_nonzero(dkv).item() == 0 and torch.count_nonzero(d32).item() == 0
