@@ -59,7 +59,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
   __shared__ int s_digit, s_rank, s_count;
   __shared__ int s_wave[4][2];
 
-  const int64_t s = blockIdx.x;
+  const int64_t s = a.s_q - 1 - (int64_t)blockIdx.x;   // last rows first (on causal rows, the longest)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = a.topk;
   const int64_t lo = max<int64_t>(0, a.ks[s]);
