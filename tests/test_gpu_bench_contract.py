@@ -1,0 +1,40 @@
+"""The benchmark's output contract on a GPU: one JSON line with the metric,
+the whole-step throughput, the dominant kernel's roofline and the oracle's
+CPU rate, for both backward forms (run on the small workload, few steps)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("scores", ["stored", "recompute"])
+def test_bench_prints_one_json_line(scores):
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"[bench] contract, dkv scores {scores}", flush=True)
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny",
+                          "--steps", "3", "--warmup", "1", "--cpu-seconds", "0.5", "--no-topk",
+                          "--dkv-scores", scores],
+                         capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    lines = [ln for ln in res.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline", "nonfinite_check"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["value"] > 0 and d["ms_per_step"] > 0
+    assert d["config"]["dkv_scores"] == scores
+    r = d["roofline"]
+    assert r["bound"] == "mfma" and r["peak"] == 2516.6 and 0 < r["frac"] < 1
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1
+
