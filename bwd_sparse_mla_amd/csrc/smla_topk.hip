@@ -15,8 +15,9 @@
 // longer row finds the K-th largest key by an MSB-first radix select over
 // order-preserving 32-bit keys (8-bit digits; per-wave LDS histograms), then
 // writes, in position order, every key above it and the first keys equal to
-// it.  The row's logits are read from HBM once, with 16-byte loads several in
-// flight per thread, and their keys kept in LDS when the row fits the cache
+// it, each thread over its own contiguous run of positions.  The row's logits
+// are read from HBM once, with 16-byte loads several in flight per thread, and
+// their keys kept in LDS when the row fits the cache
 // (sized at launch from s_kv, so short-context launches run several
 // workgroups per CU).  The select stops early once the keys sharing the
 // selected digits are exactly the ones still needed.
@@ -41,26 +42,15 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ int lanes_below(unsigned long long m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
 template <int CACHE>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t keys[CACHE + 4];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[CACHE + 8 + (CACHE + 8) / 32];
   __shared__ int hist[4][256];
   __shared__ int scratch[8];
   __shared__ int s_digit, s_rank, s_count;
-  __shared__ int s_wave[4][2];
 
   const int64_t s = a.s_q - 1 - (int64_t)blockIdx.x;   // last rows first (on causal rows, the longest)
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int K = a.topk;
   const int64_t lo = max<int64_t>(0, a.ks[s]);
   const int64_t hi = min<int64_t>(a.s_kv, a.ke[s]);
@@ -74,13 +64,18 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
 
   const float* row = a.logits + s * a.ld + lo;
   const bool cached = n <= CACHE;
-  // Elements before the row's first 16-byte boundary are read one by one;
-  // key i is cached at keys[i + pad], so the body's keys are stored 16 bytes
-  // at a time.
+  // Elements before the row's first 16-byte boundary are read one by one.
+  // Key i is cached at c + c / 32 with c = i + pad (one spare word after every
+  // 32 keys): a thread that walks 32 consecutive keys then sits on its own
+  // bank, and coalesced walks stay conflict-free.
   const int head = min(n, (int)(((16u - ((uint32_t)reinterpret_cast<uintptr_t>(row) & 15u)) & 15u) >> 2));
   const int pad = (4 - head) & 3;
+  auto cix = [&](int i) __attribute__((always_inline)) {
+    const int c = i + pad;
+    return c + (c >> 5);
+  };
   auto key_at = [&](int i) __attribute__((always_inline)) {
-    return cached ? keys[i + pad] : order_key(row[i]);
+    return cached ? keys[cix(i)] : order_key(row[i]);
   };
 
   for (int b = tid; b < 4 * 256; b += TOPK_THREADS) (&hist[0][0])[b] = 0;
@@ -90,7 +85,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
   // tail one by one; each key is cached and counted by its top digit.
   auto first = [&](int i, float x) __attribute__((always_inline)) {
     const uint32_t k = order_key(x);
-    if (cached) keys[i + pad] = k;
+    if (cached) keys[cix(i)] = k;
     atomicAdd(&hist[wave][k >> 24], 1);
   };
   if (tid < head) first(tid, row[tid]);
@@ -109,7 +104,13 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
       if (i < nv4) {
         const uint4 k = make_uint4(order_key(v[j].x), order_key(v[j].y), order_key(v[j].z),
                                    order_key(v[j].w));
-        if (cached) *reinterpret_cast<uint4*>(&keys[head + pad + 4 * i]) = k;
+        if (cached) {   // four keys inside one 32-key run: consecutive words
+          uint32_t* kp = &keys[cix(head + 4 * i)];
+          kp[0] = k.x;
+          kp[1] = k.y;
+          kp[2] = k.z;
+          kp[3] = k.w;
+        }
         atomicAdd(&hist[wave][k.x >> 24], 1);
         atomicAdd(&hist[wave][k.y >> 24], 1);
         atomicAdd(&hist[wave][k.z >> 24], 1);
@@ -167,58 +168,41 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
   }
 
   // The selection: keys whose selected digits exceed the prefix, and the
-  // first `rank` keys (in position order) whose digits equal it.  Wave w
-  // writes positions [q0, q1), a quarter of the row, in 64-key chunks.
-  const int qlen = (n + 3) / 4;
-  const int q0 = min(n, wave * qlen), q1 = min(n, q0 + qlen);
+  // first `rank` keys (in position order) whose digits equal it.  Thread t
+  // takes positions [t C, (t+1) C): it counts both kinds, two block scans
+  // give its output slot and its share of the equal keys, and it writes its
+  // chosen positions in order.
+  const int C = (n + TOPK_THREADS - 1) / TOPK_THREADS;
+  const int b0 = min(n, tid * C), b1 = min(n, b0 + C);
   int gt = 0, eq = 0;
-  for (int base = q0; base < q1; base += TOPK_BATCH * 64) {
+  for (int i0 = b0; i0 < b1; i0 += TOPK_BATCH) {
     uint32_t k[TOPK_BATCH];
 #pragma unroll
-    for (int j = 0; j < TOPK_BATCH; ++j) {
-      const int i = base + 64 * j + lane;
-      k[j] = i < q1 ? key_at(i) & pmask : 0u;
-    }
+    for (int j = 0; j < TOPK_BATCH; ++j) k[j] = i0 + j < b1 ? key_at(i0 + j) & pmask : 0u;
 #pragma unroll
     for (int j = 0; j < TOPK_BATCH; ++j) {
-      const int i = base + 64 * j + lane;
-      gt += i < q1 && k[j] > prefix;
-      eq += i < q1 && k[j] == prefix;
+      gt += i0 + j < b1 && k[j] > prefix;
+      eq += i0 + j < b1 && k[j] == prefix;
     }
   }
-  gt = wave_sum(gt);
-  eq = wave_sum(eq);
-  if (lane == 0) {
-    s_wave[wave][0] = gt;
-    s_wave[wave][1] = eq;
-  }
-  __syncthreads();
-  int pos = 0, eq_before = 0;
-  for (int w = 0; w < wave; ++w) {
-    const int take = min(s_wave[w][1], max(0, rank - eq_before));
-    pos += s_wave[w][0] + take;
-    eq_before += s_wave[w][1];
-  }
-  int eq_left = min(eq, max(0, rank - eq_before));
-  for (int base = q0; base < q1; base += TOPK_BATCH * 64) {
+  int eq_total;
+  const int eq_before = block_exclusive_scan256(eq, scratch, &eq_total);
+  int left = min(eq, max(0, rank - eq_before));   // equal keys this thread takes
+  int sel_total;
+  int pos = block_exclusive_scan256(gt + left, scratch, &sel_total);
+  for (int i0 = b0; i0 < b1; i0 += TOPK_BATCH) {
     uint32_t k[TOPK_BATCH];
 #pragma unroll
-    for (int j = 0; j < TOPK_BATCH; ++j) {
-      const int i = base + 64 * j + lane;
-      k[j] = i < q1 ? key_at(i) & pmask : 0u;
-    }
+    for (int j = 0; j < TOPK_BATCH; ++j) k[j] = i0 + j < b1 ? key_at(i0 + j) & pmask : 0u;
 #pragma unroll
     for (int j = 0; j < TOPK_BATCH; ++j) {
-      const int i = base + 64 * j + lane;
-      const bool in = i < q1;
-      const bool g = in && k[j] > prefix, e = in && k[j] == prefix;
-      const unsigned long long me = __ballot(e);
-      const bool take = g || (e && lanes_below(me) < eq_left);
-      const unsigned long long mt = __ballot(take);
-      const int p = pos + lanes_below(mt);
-      if (take && p < K) out[p] = (int32_t)(lo + i);   // p < K always: the counts sum to K
-      pos += __popcll(mt);
-      eq_left -= min(eq_left, __popcll(me));
+      if (i0 + j >= b1) continue;
+      bool take = k[j] > prefix;
+      if (k[j] == prefix && left > 0) {
+        take = true;
+        --left;
+      }
+      if (take && pos < K) out[pos++] = (int32_t)(lo + i0 + j);   // pos < K always: the counts sum to K
     }
   }
 }
