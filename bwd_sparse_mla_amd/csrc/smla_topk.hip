@@ -13,7 +13,8 @@
 //
 // One workgroup per query row.  A row no longer than K is the whole range.  A
 // longer row finds the K-th largest key by an MSB-first radix select over
-// order-preserving 32-bit keys (8-bit digits; per-wave LDS histograms), then
+// order-preserving 32-bit keys (digits of 10, 10, 10 and 2 bits; one LDS
+// histogram of 1024 bins), then
 // writes, in position order, every key above it and the first keys equal to
 // it, each thread over its own contiguous run of positions.  The row's logits
 // are read from HBM once, with 16-byte loads several in flight per thread, and
@@ -33,6 +34,10 @@ constexpr int TOPK_SMALL_CACHE = 8192;    // keys cached per row when s_kv <= 81
 constexpr int TOPK_LARGE_CACHE = 32768;   // otherwise rows up to this long are cached
 constexpr int TOPK_LOADS = 8;             // 16-byte loads in flight per thread
 constexpr int TOPK_BATCH = 8;             // keys read ahead per thread in the LDS passes
+constexpr int TOPK_BINS = 1024;           // histogram bins: digits of up to 10 bits
+// The radix digits, most significant first: the first one (sign, exponent and
+// one mantissa bit) already spreads logits of one scale over many bins.
+constexpr int TOPK_PASSES = 4;
 
 // Unsigned keys that order like the floats (finite values); -0 and +0 get the
 // same key, as they compare equal.
@@ -45,12 +50,12 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 template <int CACHE>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t keys[CACHE + 8 + (CACHE + 8) / 32];
-  __shared__ int hist[4][256];
+  __shared__ int hist[TOPK_BINS];
   __shared__ int scratch[8];
   __shared__ int s_digit, s_rank, s_count;
 
   const int64_t s = a.s_q - 1 - (int64_t)blockIdx.x;   // last rows first (on causal rows, the longest)
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int K = a.topk;
   const int64_t lo = max<int64_t>(0, a.ks[s]);
   const int64_t hi = min<int64_t>(a.s_kv, a.ke[s]);
@@ -78,7 +83,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
     return cached ? keys[cix(i)] : order_key(row[i]);
   };
 
-  for (int b = tid; b < 4 * 256; b += TOPK_THREADS) (&hist[0][0])[b] = 0;
+  for (int b = tid; b < TOPK_BINS; b += TOPK_THREADS) hist[b] = 0;
   __syncthreads();
   // Pass 0 reads the logits: the elements before the first 16-byte boundary
   // one by one, the body as float4 (TOPK_LOADS per thread in flight), the
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
   auto first = [&](int i, float x) __attribute__((always_inline)) {
     const uint32_t k = order_key(x);
     if (cached) keys[cix(i)] = k;
-    atomicAdd(&hist[wave][k >> 24], 1);
+    atomicAdd(&hist[k >> 22], 1);
   };
   if (tid < head) first(tid, row[tid]);
   const int nv4 = (n - head) >> 2;
@@ -111,10 +116,10 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
           kp[2] = k.z;
           kp[3] = k.w;
         }
-        atomicAdd(&hist[wave][k.x >> 24], 1);
-        atomicAdd(&hist[wave][k.y >> 24], 1);
-        atomicAdd(&hist[wave][k.z >> 24], 1);
-        atomicAdd(&hist[wave][k.w >> 24], 1);
+        atomicAdd(&hist[k.x >> 22], 1);
+        atomicAdd(&hist[k.y >> 22], 1);
+        atomicAdd(&hist[k.z >> 22], 1);
+        atomicAdd(&hist[k.w >> 22], 1);
       }
     }
   }
@@ -127,10 +132,11 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
   uint32_t prefix = 0, pmask = 0;
   int rank = K;
 #pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  for (int pass = 0; pass < TOPK_PASSES; ++pass) {
+    const int shift = pass < 3 ? 22 - 10 * pass : 0;     // digits [31:22], [21:12], [11:2], [1:0]
+    const uint32_t dmask = pass < 3 ? 1023u : 3u;
     if (pass > 0) {
-      for (int b = tid; b < 4 * 256; b += TOPK_THREADS) (&hist[0][0])[b] = 0;
+      for (int b = tid; b < TOPK_BINS; b += TOPK_THREADS) hist[b] = 0;
       __syncthreads();
       for (int base = 0; base < n; base += TOPK_BATCH * TOPK_THREADS) {
         uint32_t k[TOPK_BATCH];
@@ -142,25 +148,34 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkArgs a) {
 #pragma unroll
         for (int j = 0; j < TOPK_BATCH; ++j) {
           const int i = base + j * TOPK_THREADS + tid;
-          if (i < n && (k[j] & pmask) == prefix) atomicAdd(&hist[wave][(k[j] >> shift) & 255u], 1);
+          if (i < n && (k[j] & pmask) == prefix) atomicAdd(&hist[(k[j] >> shift) & dmask], 1);
         }
       }
     }
     __syncthreads();
-    // Thread t holds digit 255 - t: a scan from the top gives the count of
-    // keys above each digit.
-    const int d = 255 - tid;
-    const int c = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
+    // Thread t holds digits 1023 - 4t - j (j = 0..3): a scan from the top
+    // gives the count of keys above each digit.
+    constexpr int PER = TOPK_BINS / TOPK_THREADS;
+    int c[PER], csum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      c[j] = hist[TOPK_BINS - 1 - PER * tid - j];
+      csum += c[j];
+    }
     int total;
-    const int above = block_exclusive_scan256(c, scratch, &total);
-    if (above < rank && rank <= above + c) {
-      s_digit = d;
-      s_rank = rank - above;
-      s_count = c;
+    int above = block_exclusive_scan256(csum, scratch, &total);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (above < rank && rank <= above + c[j]) {
+        s_digit = TOPK_BINS - 1 - PER * tid - j;
+        s_rank = rank - above;
+        s_count = c[j];
+      }
+      above += c[j];
     }
     __syncthreads();
     prefix |= (uint32_t)s_digit << shift;
-    pmask |= 255u << shift;
+    pmask |= dmask << shift;
     rank = s_rank;
     const bool done = s_count == rank;
     __syncthreads();
