@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="packed_ragged",
-                    choices=["tiny", "packed_ragged", "padding_stress", "recency", "long_context"])
+                    choices=["tiny", "packed_ragged", "padding_stress", "recency", "long_context",
+                             "heads128"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")

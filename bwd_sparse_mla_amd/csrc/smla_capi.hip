@@ -29,12 +29,26 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_shape(int64_t s_q, int64_t s_kv, int heads, int topk) {
   if (s_q < 0 || s_kv < 1 || s_kv > MAX_SKV)
     return fail(SMLA_ERR_SHAPE, "s_q must be >= 0 and s_kv in [1, 2^24)");
-  if (heads != 8 && heads != 16 && heads != 32 && heads != 64)
-    return fail(SMLA_ERR_SHAPE, "heads must be 8, 16, 32 or 64");
+  if (heads != 8 && heads != 16 && heads != 32 && heads != 64 && heads != 128)
+    return fail(SMLA_ERR_SHAPE, "heads must be 8, 16, 32, 64 or 128");
   if (topk < 1 || topk > MAX_TOPK) return fail(SMLA_ERR_SHAPE, "topk must be in [1, 16384]");
   if (s_q > (int64_t(1) << 31) / heads)
     return fail(SMLA_ERR_SHAPE, "s_q * heads must stay below 2^31");
   return SMLA_OK;
+}
+
+// The kernels' view of the query rows.  A query group is 64 rows; with 128
+// heads a token's rows are two groups, so the kernels run the 64-head form
+// over 2 s_q half-token rows (the same memory: row (2t + j, h) is (t, 64 j +
+// h)), and half-token row r reads the index row of token r / 2.
+struct KernelShape {
+  int64_t s_q;
+  int heads;
+  int idx_shift;
+};
+KernelShape kernel_shape(int64_t s_q, int heads) {
+  if (heads == 128) return {2 * s_q, 64, 1};
+  return {s_q, heads, 0};
 }
 
 // gfx950 check, cached per device ordinal.
@@ -165,21 +179,24 @@ int smla_device_supported(int device) {
 
 size_t smla_fwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk) {
   if (check_shape(s_q, s_kv, heads, topk) != SMLA_OK) return 0;
-  return make_plan(s_q, s_kv, heads, topk, false).bytes;
+  const KernelShape k = kernel_shape(s_q, heads);
+  return make_plan(k.s_q, s_kv, k.heads, topk, false).bytes;
 }
 
 size_t smla_bwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
                                uint32_t flags) {
   if (check_shape(s_q, s_kv, heads, topk) != SMLA_OK) return 0;
-  return make_plan(s_q, s_kv, heads, topk, true, (flags & SMLA_DKV_ATOMIC) != 0,
+  const KernelShape k = kernel_shape(s_q, heads);
+  return make_plan(k.s_q, s_kv, k.heads, topk, true, (flags & SMLA_DKV_ATOMIC) != 0,
                    (flags & SMLA_DKV_STORED_P) != 0).bytes;
 }
 
 // Fills the planner's arguments for a workspace laid out by make_plan.
 static PlanArgs plan_args(const Plan& p, const int32_t* indices, int64_t s_q, int64_t s_kv,
-                          int topk, char* ws, bool backward) {
+                          int topk, int idx_shift, char* ws, bool backward) {
   PlanArgs pa{};
   pa.idx = indices;
+  pa.idx_shift = idx_shift;
   pa.s_q = s_q;
   pa.s_kv = s_kv;
   pa.topk = topk;
@@ -219,6 +236,9 @@ int smla_plan(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads, 
   if (st) return st;
   if (s_q > 0 && !indices) return fail(SMLA_ERR_NULL, "indices is null");
   if (!aligned16(indices)) return fail(SMLA_ERR_ALIGN, "indices must be 16-byte aligned");
+  const KernelShape k = kernel_shape(s_q, heads);
+  s_q = k.s_q;
+  heads = k.heads;
   const Plan p = make_plan(s_q, s_kv, heads, topk, true);
   if (!workspace || workspace_bytes < p.bytes)
     return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_bwd_workspace_size()");
@@ -227,7 +247,7 @@ int smla_plan(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads, 
   if ((st = check_device())) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  return run_plan(p, plan_args(p, indices, s_q, s_kv, topk, ws, true), heads, true, s);
+  return run_plan(p, plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, ws, true), heads, true, s);
 }
 
 int smla_fwd_ex(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,
@@ -241,6 +261,9 @@ int smla_fwd_ex(const void* q, const void* kv, const int32_t* indices, int64_t s
     return fail(SMLA_ERR_NULL, "null tensor pointer");
   if (!aligned16(q) || !aligned16(kv) || !aligned16(indices) || !aligned16(out) || !aligned16(lse))
     return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const KernelShape k = kernel_shape(s_q, heads);
+  s_q = k.s_q;
+  heads = k.heads;
   // The forward fields of the workspace are a prefix of the backward layout,
   // so a plan built by smla_plan serves here too.
   const Plan p = make_plan(s_q, s_kv, heads, topk, false);
@@ -252,7 +275,7 @@ int smla_fwd_ex(const void* q, const void* kv, const int32_t* indices, int64_t s
   if (s_q == 0) return SMLA_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, ws, false);
+  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, ws, false);
   if (!(flags & SMLA_PLAN_READY) && (st = run_plan(p, pa, heads, false, s))) return st;
 
   FwdArgs fa{};
@@ -300,6 +323,9 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
     return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   const bool atomic = (flags & SMLA_DKV_ATOMIC) != 0;
   const bool stored_p = (flags & SMLA_DKV_STORED_P) != 0;
+  const KernelShape k = kernel_shape(s_q, heads);
+  s_q = k.s_q;
+  heads = k.heads;
   const Plan p = make_plan(s_q, s_kv, heads, topk, true, atomic, stored_p);
   if (!workspace || workspace_bytes < p.bytes)
     return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_bwd_workspace_size(flags)");
@@ -309,7 +335,7 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
-  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, ws, true);
+  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, ws, true);
   if (!(flags & SMLA_PLAN_READY) && (st = run_plan(p, pa, heads, true, s))) return st;
   int* gorder = reinterpret_cast<int*>(ws + p.off_gorder);
 

@@ -43,6 +43,7 @@ struct PlanArgs {
   const int32_t* idx;
   int64_t s_q, s_kv;
   int topk;
+  int idx_shift;      // query row t reads index row t >> idx_shift (1: two rows per token)
   int64_t G, NB, qcap, rcap;
   int* qcount;        // [G]   union entries (main + extra) per group
   int* xcount;        // [G]   extra entries (repeated slots) per group

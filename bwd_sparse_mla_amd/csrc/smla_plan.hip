@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   const int nt = (int)min<int64_t>(T, a.s_q - t0);
   const int K = a.topk;
   const int nslots = nt * K;
-  const int32_t* ix = a.idx + t0 * K;
+  const int32_t* ix = a.idx + (t0 >> a.idx_shift) * K;   // shift > 0 only with T = 1
   const int nxw = (nslots + 31) >> 5;
   const int skv = (int)a.s_kv;
 

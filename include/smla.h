@@ -31,7 +31,7 @@
  *  - A slot is valid iff 0 <= index < s_kv.  -1 is padding.  Any other value
  *    is a contract violation; the kernels treat it as padding (they never
  *    read or write outside the buffers) and smla_validate_indices counts it.
- *  - Supported: heads in {8, 16, 32, 64}; 1 <= topk <= 16384;
+ *  - Supported: heads in {8, 16, 32, 64, 128}; 1 <= topk <= 16384;
  *    1 <= s_kv < 2^24; s_q >= 0.  With s_q == 0 the pointers of the q-sized
  *    tensors (q, indices, out, dout, lse, dq) may be NULL; the forward then
  *    launches nothing and the backward only writes dkv (zeros).

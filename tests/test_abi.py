@@ -43,6 +43,12 @@ def test_version_and_workspace_queries(lib):
     bwd = lib.smla_bwd_workspace_size(4096, 4096, 8, 2048, 0)
     assert 0 < fwd < bwd
     assert lib.smla_fwd_workspace_size(4096, 4096, 12, 2048) == 0     # unsupported heads
+    assert lib.smla_fwd_workspace_size(4096, 4096, 256, 2048) == 0
+    # 128 heads run as 64-head groups over two half-token rows per token
+    assert lib.smla_fwd_workspace_size(300, 900, 128, 64) == lib.smla_fwd_workspace_size(600, 900, 64, 64) > 0
+    for flags in (0, 2, 8):
+        assert (lib.smla_bwd_workspace_size(300, 900, 128, 64, flags)
+                == lib.smla_bwd_workspace_size(600, 900, 64, 64, flags) > 0)
     assert lib.smla_fwd_workspace_size(4096, 4096, 8, 0) == 0         # topk < 1
     assert lib.smla_bwd_workspace_size(16, 1 << 24, 8, 8, 0) == 0     # s_kv too large
 

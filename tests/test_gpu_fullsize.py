@@ -82,7 +82,7 @@ def _bf16_rows(t, rows):
     ("packed_ragged", False, False), ("padding_stress", False, False), ("recency", False, False),
     ("long_context", False, False), ("long_context", True, False),
     ("packed_ragged", False, True), ("padding_stress", False, True), ("recency", False, True),
-    ("long_context", True, True)])
+    ("long_context", True, True), ("heads128", False, False), ("heads128", False, True)])
 def test_full_size_sampled_parity(name, atomic, stored):
     """atomic: the same checks with dkv scattered by fp32 atomic adds (the
     long-context workload runs in both dkv modes); stored: the dkv pass reads

@@ -74,11 +74,35 @@ def test_tiny_parity():
     check_full(synth.tiny())
 
 
-@pytest.mark.parametrize("H", [8, 16, 32, 64])
+@pytest.mark.parametrize("H", [8, 16, 32, 64, 128])
 def test_random_sparse_parity(H):
     # ragged tail: S not a multiple of the group size, S_kv not a multiple of 64
     w = synth.custom(S=37, H=H, K=300, S_kv=333, seed=H, pad_frac=0.4, empty_frac=0.1)
     check_full(w)
+
+
+def test_h128_is_the_64_head_path_over_half_token_rows():
+    # With 128 heads a token's rows are two 64-row query groups that share its
+    # index row: the result is, bit for bit, that of 64 heads over 2 S rows
+    # whose index rows come in equal pairs (forward, both backward forms).
+    import bwd_sparse_mla_amd as smla
+    w = synth.custom(S=29, H=128, K=200, S_kv=400, seed=31, pad_frac=0.3, empty_frac=0.1)
+    q, kv, dout, idx = gpu_inputs(w)
+    S2 = 2 * w.S
+    q2, dout2 = q.view(S2, 64, 576), dout.view(S2, 64, 512)
+    idx2 = idx.repeat_interleave(2, dim=0).contiguous()
+    out, lse = smla.sparse_mla_fwd(q, kv, idx, w.sm_scale)
+    out2, lse2 = smla.sparse_mla_fwd(q2, kv, idx2, w.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(S2, 64, 512).view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse.view(S2, 64).view(torch.int32), lse2.view(torch.int32))
+    for stored in (False, True):
+        dq, dkv = smla.sparse_mla_bwd(q, kv, out, dout, idx, lse, w.sm_scale, stored_p=stored)
+        dq2, dkv2 = smla.sparse_mla_bwd(q2, kv, out2, dout2, idx2, lse2, w.sm_scale,
+                                        stored_p=stored)
+        torch.cuda.synchronize()
+        assert torch.equal(dq.view(S2, 64, 576).view(torch.int16), dq2.view(torch.int16))
+        assert torch.equal(dkv.view(torch.int16), dkv2.view(torch.int16))
 
 
 @pytest.mark.parametrize("scatter", [True, False])

@@ -6,7 +6,7 @@ out / lse within the tolerance, rows no slot selects stay exact zeros (and
 keep a -0.0 sign bit when accumulating), the result is bitwise reproducible,
 and it composes with the atomic dkv mode and with the plan built once.
 Workloads cover padding anywhere, empty rows, repeated indices, several kv
-blocks per group, kv spans beyond one planner window and H = 8..64."""
+blocks per group, kv spans beyond one planner window and H = 8..128."""
 import numpy as np
 import pytest
 
@@ -24,6 +24,8 @@ CASES = {
     "multi_block_h8": lambda: synth.custom(S=96, H=8, K=512, S_kv=1500, seed=22, pad_frac=0.1),
     "h32": lambda: synth.custom(S=40, H=32, K=200, S_kv=900, seed=23, pad_frac=0.3),
     "h64": lambda: synth.custom(S=33, H=64, K=130, S_kv=700, seed=24, pad_frac=0.25, dup_frac=0.05),
+    "h128": lambda: synth.custom(S=21, H=128, K=150, S_kv=500, seed=26, pad_frac=0.2,
+                                 empty_frac=0.1),
     "windows": lambda: synth.custom(S=12, H=16, K=700, S_kv=40000, seed=9, pad_frac=0.2,
                                     empty_frac=0.0),
     "oob": lambda: synth.custom(S=50, H=8, K=64, S_kv=200, seed=25, oob_frac=0.05),

@@ -286,12 +286,25 @@ def long_context(seed: int = 4) -> Workload:
     return Workload("long_context_s32768_h16_k2048", q, kv, dout, idx, SM_SCALE, seqlens, seed)
 
 
+def heads128(seed: int = 5) -> Workload:
+    """S=2048 packed as sequences {512, 1536}, H=128 (one GPU's query heads
+    with no head split), topk=2048; row p lists all p+1 in-sequence causal
+    positions (shuffled) followed by trailing -1."""
+    rng = np.random.default_rng(seed)
+    seqlens = [512, 1536]
+    S, H, K = sum(seqlens), 128, 2048
+    q, kv, dout = _tensors(rng, S, H, S)
+    idx = causal_full_rows(rng, seqlens, K)
+    return Workload("packed_ragged_s2048_h128_k2048", q, kv, dout, idx, SM_SCALE, seqlens, seed)
+
+
 WORKLOADS = {
     "tiny": tiny,
     "packed_ragged": packed_ragged,
     "padding_stress": padding_stress,
     "recency": recency_hot_rows,
     "long_context": long_context,
+    "heads128": heads128,
 }
 
 
