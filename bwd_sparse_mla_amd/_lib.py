@@ -33,6 +33,13 @@ SIGNATURES = {
     "smla_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, ctypes.c_float,
                                 _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "smla_bwd_workspace_size": (_SZ, [_I64, _I64, _I32, _I32, ctypes.c_uint32]),
+    "smla_plan_g": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _I32, _P, _SZ, _P]),
+    "smla_fwd_g": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, ctypes.c_float,
+                                  _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
+    "smla_fwd_workspace_size_g": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
+    "smla_bwd_g": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32,
+                                  ctypes.c_float, _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
+    "smla_bwd_workspace_size_g": (_SZ, [_I64, _I64, _I32, _I32, _I32, ctypes.c_uint32]),
     "smla_validate_indices": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _P]),
     "smla_nonfinite_count": (ctypes.c_int, [_P, _I32, _I64, _P, _P]),
     "smla_nonfinite_replace": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _P]),

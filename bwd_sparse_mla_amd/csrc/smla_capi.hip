@@ -26,29 +26,40 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_shape(int64_t s_q, int64_t s_kv, int heads, int topk) {
-  if (s_q < 0 || s_kv < 1 || s_kv > MAX_SKV)
-    return fail(SMLA_ERR_SHAPE, "s_q must be >= 0 and s_kv in [1, 2^24)");
-  if (heads != 8 && heads != 16 && heads != 32 && heads != 64 && heads != 128)
-    return fail(SMLA_ERR_SHAPE, "heads must be 8, 16, 32, 64 or 128");
+int check_shape(int64_t s_q, int64_t s_kv, int heads, int topk, int kv_groups = 1) {
+  if (kv_groups < 1 || kv_groups > 64) return fail(SMLA_ERR_SHAPE, "kv_groups must be in [1, 64]");
+  if (s_q < 0 || s_kv < 1 || s_kv * kv_groups > MAX_SKV)
+    return fail(SMLA_ERR_SHAPE, "s_q must be >= 0, s_kv >= 1 and s_kv * kv_groups < 2^24");
+  if (heads < 1 || heads % kv_groups != 0)
+    return fail(SMLA_ERR_SHAPE, "heads must be a positive multiple of kv_groups");
+  const int hg = heads / kv_groups;
+  if (hg != 8 && hg != 16 && hg != 32 && hg != 64 && hg != 128)
+    return fail(SMLA_ERR_SHAPE, "heads per kv group must be 8, 16, 32, 64 or 128");
   if (topk < 1 || topk > MAX_TOPK) return fail(SMLA_ERR_SHAPE, "topk must be in [1, 16384]");
   if (s_q > (int64_t(1) << 31) / heads)
     return fail(SMLA_ERR_SHAPE, "s_q * heads must stay below 2^31");
   return SMLA_OK;
 }
 
-// The kernels' view of the query rows.  A query group is 64 rows; with 128
-// heads a token's rows are two groups, so the kernels run the 64-head form
-// over 2 s_q half-token rows (the same memory: row (2t + j, h) is (t, 64 j +
-// h)), and half-token row r reads the index row of token r / 2.
+// The kernels' view of the rows.  With G kv groups, q [s_q, heads, 576] is
+// [s_q G, heads / G, 576] (the pair (token, group) is one row of heads / G
+// heads, reading index row s G + g of indices [s_q, G, topk]), and kv
+// [s_kv, G, 576] is s_kv G flat rows (the planner maps a valid index j of
+// group g to row j G + g).  A query group is 64 rows; with 128 heads per kv
+// group a row's heads are two groups, so the kernels run the 64-head form
+// over twice the rows (the same memory: row (2r + j, h) is (r, 64 j + h)),
+// half-row 2r + j reading index row r.
 struct KernelShape {
-  int64_t s_q;
+  int64_t s_q;     // kernel rows of `heads` heads
+  int64_t s_kv;    // flat kv rows
   int heads;
   int idx_shift;
 };
-KernelShape kernel_shape(int64_t s_q, int heads) {
-  if (heads == 128) return {2 * s_q, 64, 1};
-  return {s_q, heads, 0};
+KernelShape kernel_shape(int64_t s_q, int64_t s_kv, int heads, int kv_groups) {
+  const int64_t r = s_q * kv_groups;
+  const int hg = heads / kv_groups;
+  if (hg == 128) return {2 * r, s_kv * kv_groups, 64, 1};
+  return {r, s_kv * kv_groups, hg, 0};
 }
 
 // gfx950 check, cached per device ordinal.
@@ -177,26 +188,38 @@ int smla_device_supported(int device) {
   return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
 }
 
+size_t smla_fwd_workspace_size_g(int64_t s_q, int64_t s_kv, int32_t heads, int32_t kv_groups,
+                                 int32_t topk) {
+  if (check_shape(s_q, s_kv, heads, topk, kv_groups) != SMLA_OK) return 0;
+  const KernelShape k = kernel_shape(s_q, s_kv, heads, kv_groups);
+  return make_plan(k.s_q, k.s_kv, k.heads, topk, false).bytes;
+}
+
 size_t smla_fwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk) {
-  if (check_shape(s_q, s_kv, heads, topk) != SMLA_OK) return 0;
-  const KernelShape k = kernel_shape(s_q, heads);
-  return make_plan(k.s_q, s_kv, k.heads, topk, false).bytes;
+  return smla_fwd_workspace_size_g(s_q, s_kv, heads, 1, topk);
+}
+
+size_t smla_bwd_workspace_size_g(int64_t s_q, int64_t s_kv, int32_t heads, int32_t kv_groups,
+                                 int32_t topk, uint32_t flags) {
+  if (check_shape(s_q, s_kv, heads, topk, kv_groups) != SMLA_OK) return 0;
+  const KernelShape k = kernel_shape(s_q, s_kv, heads, kv_groups);
+  return make_plan(k.s_q, k.s_kv, k.heads, topk, true, (flags & SMLA_DKV_ATOMIC) != 0,
+                   (flags & SMLA_DKV_STORED_P) != 0).bytes;
 }
 
 size_t smla_bwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
                                uint32_t flags) {
-  if (check_shape(s_q, s_kv, heads, topk) != SMLA_OK) return 0;
-  const KernelShape k = kernel_shape(s_q, heads);
-  return make_plan(k.s_q, s_kv, k.heads, topk, true, (flags & SMLA_DKV_ATOMIC) != 0,
-                   (flags & SMLA_DKV_STORED_P) != 0).bytes;
+  return smla_bwd_workspace_size_g(s_q, s_kv, heads, 1, topk, flags);
 }
 
 // Fills the planner's arguments for a workspace laid out by make_plan.
 static PlanArgs plan_args(const Plan& p, const int32_t* indices, int64_t s_q, int64_t s_kv,
-                          int topk, int idx_shift, char* ws, bool backward) {
+                          int topk, int idx_shift, int kv_groups, char* ws, bool backward) {
   PlanArgs pa{};
   pa.idx = indices;
   pa.idx_shift = idx_shift;
+  pa.kv_groups = kv_groups;
+  pa.s_kv_idx = s_kv / kv_groups;
   pa.s_q = s_q;
   pa.s_kv = s_kv;
   pa.topk = topk;
@@ -229,15 +252,17 @@ static int run_plan(const Plan& p, const PlanArgs& pa, int heads, bool backward,
   return hip_status(timed("order", s, [&] { return launch_order_groups(pa.qcount, pa.xcount, p.G, gorder, pa.xtotal, s); }), "order");
 }
 
-int smla_plan(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
-              void* workspace, size_t workspace_bytes, void* stream) {
+int smla_plan_g(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads,
+                int32_t kv_groups, int32_t topk, void* workspace, size_t workspace_bytes,
+                void* stream) {
   g_last_error.clear();
-  int st = check_shape(s_q, s_kv, heads, topk);
+  int st = check_shape(s_q, s_kv, heads, topk, kv_groups);
   if (st) return st;
   if (s_q > 0 && !indices) return fail(SMLA_ERR_NULL, "indices is null");
   if (!aligned16(indices)) return fail(SMLA_ERR_ALIGN, "indices must be 16-byte aligned");
-  const KernelShape k = kernel_shape(s_q, heads);
+  const KernelShape k = kernel_shape(s_q, s_kv, heads, kv_groups);
   s_q = k.s_q;
+  s_kv = k.s_kv;
   heads = k.heads;
   const Plan p = make_plan(s_q, s_kv, heads, topk, true);
   if (!workspace || workspace_bytes < p.bytes)
@@ -247,22 +272,29 @@ int smla_plan(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads, 
   if ((st = check_device())) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  return run_plan(p, plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, ws, true), heads, true, s);
+  return run_plan(p, plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups, ws, true), heads,
+                  true, s);
 }
 
-int smla_fwd_ex(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,
-                int32_t heads, int32_t topk, float sm_scale, void* out, float* lse, uint32_t flags,
-                void* workspace, size_t workspace_bytes, void* stream) {
+int smla_plan(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  return smla_plan_g(indices, s_q, s_kv, heads, 1, topk, workspace, workspace_bytes, stream);
+}
+
+int smla_fwd_g(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,
+               int32_t heads, int32_t kv_groups, int32_t topk, float sm_scale, void* out,
+               float* lse, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  int st = check_shape(s_q, s_kv, heads, topk);
+  int st = check_shape(s_q, s_kv, heads, topk, kv_groups);
   if (st) return st;
   if (flags & ~SMLA_PLAN_READY) return fail(SMLA_ERR_FLAGS, "unknown flag bits");
   if (!kv || (s_q > 0 && (!q || !indices || !out || !lse)))
     return fail(SMLA_ERR_NULL, "null tensor pointer");
   if (!aligned16(q) || !aligned16(kv) || !aligned16(indices) || !aligned16(out) || !aligned16(lse))
     return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  const KernelShape k = kernel_shape(s_q, heads);
+  const KernelShape k = kernel_shape(s_q, s_kv, heads, kv_groups);
   s_q = k.s_q;
+  s_kv = k.s_kv;
   heads = k.heads;
   // The forward fields of the workspace are a prefix of the backward layout,
   // so a plan built by smla_plan serves here too.
@@ -275,7 +307,7 @@ int smla_fwd_ex(const void* q, const void* kv, const int32_t* indices, int64_t s
   if (s_q == 0) return SMLA_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, ws, false);
+  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups, ws, false);
   if (!(flags & SMLA_PLAN_READY) && (st = run_plan(p, pa, heads, false, s))) return st;
 
   FwdArgs fa{};
@@ -295,19 +327,27 @@ int smla_fwd_ex(const void* q, const void* kv, const int32_t* indices, int64_t s
   return hip_status(timed("fwd", s, [&] { return launch_fwd(fa, heads, s); }), "fwd");
 }
 
+int smla_fwd_ex(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,
+                int32_t heads, int32_t topk, float sm_scale, void* out, float* lse, uint32_t flags,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  return smla_fwd_g(q, kv, indices, s_q, s_kv, heads, 1, topk, sm_scale, out, lse, flags,
+                    workspace, workspace_bytes, stream);
+}
+
 int smla_fwd(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,
              int32_t heads, int32_t topk, float sm_scale, void* out, float* lse,
              void* workspace, size_t workspace_bytes, void* stream) {
-  return smla_fwd_ex(q, kv, indices, s_q, s_kv, heads, topk, sm_scale, out, lse, 0u, workspace,
-                     workspace_bytes, stream);
+  return smla_fwd_g(q, kv, indices, s_q, s_kv, heads, 1, topk, sm_scale, out, lse, 0u, workspace,
+                    workspace_bytes, stream);
 }
 
-int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
-             const int32_t* indices, const float* lse, int64_t s_q, int64_t s_kv, int32_t heads,
-             int32_t topk, float sm_scale, void* dq, void* dkv, float* dkv_f32, uint32_t flags,
-             void* workspace, size_t workspace_bytes, void* stream) {
+int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
+               const int32_t* indices, const float* lse, int64_t s_q, int64_t s_kv, int32_t heads,
+               int32_t kv_groups, int32_t topk, float sm_scale, void* dq, void* dkv,
+               float* dkv_f32, uint32_t flags, void* workspace, size_t workspace_bytes,
+               void* stream) {
   g_last_error.clear();
-  int st = check_shape(s_q, s_kv, heads, topk);
+  int st = check_shape(s_q, s_kv, heads, topk, kv_groups);
   if (st) return st;
   if (!kv || (s_q > 0 && (!q || !out || !dout || !indices || !lse || !dq)))
     return fail(SMLA_ERR_NULL, "null tensor pointer");
@@ -323,8 +363,9 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
     return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   const bool atomic = (flags & SMLA_DKV_ATOMIC) != 0;
   const bool stored_p = (flags & SMLA_DKV_STORED_P) != 0;
-  const KernelShape k = kernel_shape(s_q, heads);
+  const KernelShape k = kernel_shape(s_q, s_kv, heads, kv_groups);
   s_q = k.s_q;
+  s_kv = k.s_kv;
   heads = k.heads;
   const Plan p = make_plan(s_q, s_kv, heads, topk, true, atomic, stored_p);
   if (!workspace || workspace_bytes < p.bytes)
@@ -335,7 +376,7 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
-  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, ws, true);
+  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups, ws, true);
   if (!(flags & SMLA_PLAN_READY) && (st = run_plan(p, pa, heads, true, s))) return st;
   int* gorder = reinterpret_cast<int*>(ws + p.off_gorder);
 
@@ -388,6 +429,14 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
     return st;
   if ((st = hip_status(timed("bwd_dkv", s, [&] { return launch_bwd_dkv(ba, heads, s); }), "bwd_dkv"))) return st;
   return hip_status(timed("dkv_finalize", s, [&] { return launch_dkv_finalize(ba, heads, s); }), "dkv_finalize");
+}
+
+int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
+             const int32_t* indices, const float* lse, int64_t s_q, int64_t s_kv, int32_t heads,
+             int32_t topk, float sm_scale, void* dq, void* dkv, float* dkv_f32, uint32_t flags,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  return smla_bwd_g(q, kv, out, dout, indices, lse, s_q, s_kv, heads, 1, topk, sm_scale, dq, dkv,
+                    dkv_f32, flags, workspace, workspace_bytes, stream);
 }
 
 int smla_topk_indices(const float* logits, int64_t s_q, int64_t s_kv, int64_t ld,

@@ -44,6 +44,11 @@ struct PlanArgs {
   int64_t s_q, s_kv;
   int topk;
   int idx_shift;      // query row t reads index row t >> idx_shift (1: two rows per token)
+  // kv groups: index row r belongs to kv group r % kv_groups, and its valid
+  // value j (0 <= j < s_kv_idx) names flat kv row j * kv_groups + r % kv_groups
+  // of the [s_kv_idx, kv_groups, 576] kv (s_kv = s_kv_idx * kv_groups rows)
+  int kv_groups;
+  int64_t s_kv_idx;
   int64_t G, NB, qcap, rcap;
   int* qcount;        // [G]   union entries (main + extra) per group
   int* xcount;        // [G]   extra entries (repeated slots) per group

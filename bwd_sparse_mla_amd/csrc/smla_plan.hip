@@ -43,7 +43,7 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
-template <int T>
+template <int T, bool KVG>
 __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   __shared__ unsigned bm[T][WIN_WORDS];      // per-token row bitmaps of one window
   __shared__ unsigned xflag[XFLAG_WORDS];    // slots that repeat an earlier slot's row
@@ -58,7 +58,17 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   const int nslots = nt * K;
   const int32_t* ix = a.idx + (t0 >> a.idx_shift) * K;   // shift > 0 only with T = 1
   const int nxw = (nslots + 31) >> 5;
-  const int skv = (int)a.s_kv;
+  const int skv = (int)a.s_kv;        // flat kv rows
+  const int sidx = (int)a.s_kv_idx;   // valid index values: [0, sidx)
+  const int kvg = a.kv_groups;
+  // Flat kv row of a valid value v in slot s of the group (KVG: the slot's
+  // index row picks the kv group).
+  auto flat_row = [&](int v, int s) __attribute__((always_inline)) {
+    if constexpr (KVG)
+      return v * kvg + (int)(((t0 + s / K) >> a.idx_shift) % kvg);
+    else
+      return v;
+  };
 
   if (tid == 0) {
     s_lo = 0x7fffffff;
@@ -79,7 +89,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
       for (int j = 0; j < 16; ++j) v[j] = s0 + 256 * j < nslots ? ix[s0 + 256 * j] : -1;
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if (v[j] >= 0 && v[j] < skv) {
+        if (v[j] >= 0 && v[j] < sidx) {
           lo = min(lo, v[j]);
           hi = max(hi, v[j]);
         }
@@ -93,6 +103,10 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     __syncthreads();
     lo = s_lo;
     hi = s_hi;
+    if (KVG && hi >= 0) {   // the flat rows of the values' span, every group's
+      lo *= kvg;
+      hi = hi * kvg + kvg - 1;
+    }
   }
 
   int32_t* qrow = a.qrow + g * a.qcap;
@@ -124,9 +138,10 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 #pragma unroll
       for (int j = 0; j < PLAN_LOADS; ++j) {
         const int s = s0 + 256 * j;
-        if (v[j] >= w0 && v[j] < w0 + WIN_BITS && v[j] < skv) {
+        const int m = v[j] >= 0 && v[j] < sidx ? flat_row(v[j], s) : -1;
+        if (m >= w0 && m < w0 + WIN_BITS) {
           const int t = s / K;
-          const int bit = v[j] - w0;
+          const int bit = m - w0;
           const unsigned m = 1u << (bit & 31);
           const unsigned old = atomicOr(&bm[t][bit >> 5], m);
           if (old & m) atomicOr(&xflag[s >> 5], 1u << (s & 31));
@@ -256,7 +271,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
       f &= f - 1;
       const int s = 32 * w + b;
       const int t = s / K;
-      qrow[pos] = ix[s];
+      qrow[pos] = flat_row(ix[s], s);
       qmask[pos] = (uint8_t)(1u << t);
       ++pos;
     }
@@ -317,11 +332,12 @@ hipError_t launch_order_groups(const int* qcount, const int* xcount, int64_t G, 
 hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream) {
   if (a.G == 0) return hipSuccess;
   dim3 grid((unsigned)a.G), block(256);
+  const bool kvg = a.kv_groups > 1;
   switch (heads) {
-    case 8: plan_kernel<8><<<grid, block, 0, stream>>>(a); break;
-    case 16: plan_kernel<4><<<grid, block, 0, stream>>>(a); break;
-    case 32: plan_kernel<2><<<grid, block, 0, stream>>>(a); break;
-    case 64: plan_kernel<1><<<grid, block, 0, stream>>>(a); break;
+    case 8: kvg ? plan_kernel<8, true><<<grid, block, 0, stream>>>(a) : plan_kernel<8, false><<<grid, block, 0, stream>>>(a); break;
+    case 16: kvg ? plan_kernel<4, true><<<grid, block, 0, stream>>>(a) : plan_kernel<4, false><<<grid, block, 0, stream>>>(a); break;
+    case 32: kvg ? plan_kernel<2, true><<<grid, block, 0, stream>>>(a) : plan_kernel<2, false><<<grid, block, 0, stream>>>(a); break;
+    case 64: kvg ? plan_kernel<1, true><<<grid, block, 0, stream>>>(a) : plan_kernel<1, false><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

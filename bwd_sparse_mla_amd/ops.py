@@ -41,32 +41,42 @@ def _flat_q(q: torch.Tensor) -> torch.Tensor:
     return q
 
 
-def _flat_kv(kv: torch.Tensor) -> torch.Tensor:
+def _grouped_kv(kv: torch.Tensor) -> tuple[torch.Tensor, int]:
+    """kv as [S_kv, G, 576] (G = 1 for [S_kv, 576]); returns (kv, G)."""
     if kv.dim() == 4:
         if kv.shape[0] != 1:
             raise ValueError("kv with a batch dimension must have batch 1")
         kv = kv[0]
-    if kv.dim() == 3:
-        if kv.shape[1] != 1:
-            raise ValueError("only one KV group is supported")
-        kv = kv[:, 0]
-    if kv.dim() != 2 or kv.shape[-1] != D_K:
-        raise ValueError(f"kv must be [S_kv, {D_K}], got {tuple(kv.shape)}")
-    return kv
+    if kv.dim() == 2:
+        kv = kv.unsqueeze(1)
+    if kv.dim() != 3 or kv.shape[-1] != D_K:
+        raise ValueError(f"kv must be [S_kv, {D_K}] or [S_kv, G, {D_K}], got {tuple(kv.shape)}")
+    return kv, kv.shape[1]
 
 
-def _flat_idx(idx: torch.Tensor) -> torch.Tensor:
+def _flat_kv(kv: torch.Tensor) -> torch.Tensor:
+    kv3, g = _grouped_kv(kv)
+    if g != 1:
+        raise ValueError("this call takes one KV group")
+    return kv3[:, 0]
+
+
+def _grouped_idx(idx: torch.Tensor, groups: int) -> torch.Tensor:
+    """indices as [S, G, K] ([S, K] when G = 1)."""
     if idx.dim() == 4:
         if idx.shape[0] != 1:
             raise ValueError("indices with a batch dimension must have batch 1")
         idx = idx[0]
-    if idx.dim() == 3:
-        if idx.shape[1] != 1:
-            raise ValueError("only one KV group is supported")
-        idx = idx[:, 0]
-    if idx.dim() != 2:
-        raise ValueError(f"indices must be [S, K], got {tuple(idx.shape)}")
+    if idx.dim() == 2 and groups == 1:
+        idx = idx.unsqueeze(1)
+    if idx.dim() != 3 or idx.shape[1] != groups:
+        raise ValueError(f"indices must be [S, {groups}, K] for {groups} KV group(s), "
+                         f"got {tuple(idx.shape)}")
     return idx
+
+
+def _flat_idx(idx: torch.Tensor) -> torch.Tensor:
+    return _grouped_idx(idx, 1)[:, 0]
 
 
 def _prep(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
@@ -85,15 +95,16 @@ def _workspace(nbytes: int, device) -> tuple[torch.Tensor, int]:
     return buf, (addr + 255) & ~255
 
 
-def fwd_workspace_bytes(s_q: int, s_kv: int, heads: int, topk: int) -> int:
-    n = _lib.load().smla_fwd_workspace_size(s_q, s_kv, heads, topk)
+def fwd_workspace_bytes(s_q: int, s_kv: int, heads: int, topk: int, kv_groups: int = 1) -> int:
+    n = _lib.load().smla_fwd_workspace_size_g(s_q, s_kv, heads, kv_groups, topk)
     if n == 0:
         raise ValueError("unsupported shape for smla_fwd")
     return n
 
 
-def bwd_workspace_bytes(s_q: int, s_kv: int, heads: int, topk: int, flags: int = 0) -> int:
-    n = _lib.load().smla_bwd_workspace_size(s_q, s_kv, heads, topk, flags)
+def bwd_workspace_bytes(s_q: int, s_kv: int, heads: int, topk: int, flags: int = 0,
+                        kv_groups: int = 1) -> int:
+    n = _lib.load().smla_bwd_workspace_size_g(s_q, s_kv, heads, kv_groups, topk, flags)
     if n == 0:
         raise ValueError("unsupported shape for smla_bwd")
     return n
@@ -101,29 +112,33 @@ def bwd_workspace_bytes(s_q: int, s_kv: int, heads: int, topk: int, flags: int =
 
 def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_scale: float,
                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """Forward: returns (out [..., H, 512] bf16, lse [..., H] fp32, natural log)."""
+    """Forward: returns (out [..., H, 512] bf16, lse [..., H] fp32, natural log).
+
+    kv is [S_kv, 576] or [S_kv, G, 576] with G KV groups; indices are [S, K]
+    or [S, G, K]; head h attends over kv group h // (H // G)."""
     lib = _lib.load()
     lead = q.shape[:-1]
     q3 = _prep(_flat_q(q), torch.bfloat16, "q")
-    kv2 = _prep(_flat_kv(kv), torch.bfloat16, "kv")
-    ix = _flat_idx(indices)
+    kv3, G = _grouped_kv(kv)
+    kv3 = _prep(kv3, torch.bfloat16, "kv")
+    ix = _grouped_idx(indices, G)
     if ix.dtype != torch.int32:
         ix = ix.to(torch.int32)
     ix = _prep(ix, torch.int32, "indices")
     S, H, _ = q3.shape
     if ix.shape[0] != S:
         raise ValueError("indices must have one row per query token")
-    K = ix.shape[1]
-    S_kv = kv2.shape[0]
+    K = ix.shape[2]
+    S_kv = kv3.shape[0]
     dev = q3.device
     if out is None:
         out = torch.empty(*lead[:-1], H, D_V, dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty(*lead[:-1], H, dtype=torch.float32, device=dev)
-    ws, ws_addr = _workspace(fwd_workspace_bytes(S, S_kv, H, K), dev)
-    _lib.check(lib.smla_fwd(_ptr(q3), _ptr(kv2), _ptr(ix), S, S_kv, H, K, float(sm_scale),
-                            _ptr(out), _ptr(lse), ctypes.c_void_p(ws_addr),
-                            ws.numel() - (ws_addr - ws.data_ptr()), _stream(dev)))
+    ws, ws_addr = _workspace(fwd_workspace_bytes(S, S_kv, H, K, G), dev)
+    _lib.check(lib.smla_fwd_g(_ptr(q3), _ptr(kv3), _ptr(ix), S, S_kv, H, G, K, float(sm_scale),
+                              _ptr(out), _ptr(lse), 0, ctypes.c_void_p(ws_addr),
+                              ws.numel() - (ws_addr - ws.data_ptr()), _stream(dev)))
     return out, lse
 
 
@@ -134,27 +149,30 @@ def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, out: torch.Tensor, dout: t
                    want_bf16_dkv: bool = True):
     """Backward: returns (dq like q, dkv like kv in bf16 or None).
 
-    dkv_f32, if given, is an fp32 [S_kv, 576] tensor that receives the fp32
-    dkv (overwritten, or added to with accumulate=True).  The default mode is
+    kv and indices take the shapes sparse_mla_fwd takes (with or without a KV
+    group dimension); dkv has kv's shape.  dkv_f32, if given, is a contiguous
+    fp32 tensor of kv's element count that receives the fp32 dkv
+    (overwritten, or added to with accumulate=True).  The default mode is
     the deterministic per-row reduction; atomic=True scatters dkv with fp32
     atomic adds (not bitwise reproducible).  stored_p=True has the dq pass
     store P and scale * dS for the dkv pass (one recompute of the scores
     instead of two; a larger workspace)."""
     lib = _lib.load()
     q3 = _prep(_flat_q(q), torch.bfloat16, "q")
-    kv2 = _prep(_flat_kv(kv), torch.bfloat16, "kv")
+    kv3, G = _grouped_kv(kv)
+    kv3 = _prep(kv3, torch.bfloat16, "kv")
     S, H, _ = q3.shape
     o3 = _prep(out.reshape(S, H, D_V), torch.bfloat16, "out")
     do3 = _prep(dout.reshape(S, H, D_V), torch.bfloat16, "dout")
     ls = _prep(lse.reshape(S, H), torch.float32, "lse")
-    ix = _flat_idx(indices)
+    ix = _grouped_idx(indices, G)
     if ix.dtype != torch.int32:
         ix = ix.to(torch.int32)
     ix = _prep(ix, torch.int32, "indices")
     if ix.shape[0] != S:
         raise ValueError("indices must have one row per query token")
-    K = ix.shape[1]
-    S_kv = kv2.shape[0]
+    K = ix.shape[2]
+    S_kv = kv3.shape[0]
     dev = q3.device
     flags = (_lib.SMLA_DKV_ATOMIC if atomic else 0) | (_lib.SMLA_DKV_STORED_P if stored_p else 0)
     if accumulate:
@@ -163,15 +181,15 @@ def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, out: torch.Tensor, dout: t
         flags |= _lib.SMLA_DKV_ACCUMULATE
     if dkv_f32 is not None:
         if dkv_f32.dtype != torch.float32 or not dkv_f32.is_contiguous() \
-                or dkv_f32.numel() != S_kv * D_K:
-            raise ValueError("dkv_f32 must be a contiguous fp32 tensor of S_kv*576 elements")
+                or dkv_f32.numel() != S_kv * G * D_K:
+            raise ValueError("dkv_f32 must be a contiguous fp32 tensor of S_kv*G*576 elements")
     dq = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     dkv = torch.empty(kv.shape, dtype=torch.bfloat16, device=dev) if want_bf16_dkv else None
-    ws, ws_addr = _workspace(bwd_workspace_bytes(S, S_kv, H, K, flags), dev)
-    _lib.check(lib.smla_bwd(_ptr(q3), _ptr(kv2), _ptr(o3), _ptr(do3), _ptr(ix), _ptr(ls),
-                            S, S_kv, H, K, float(sm_scale), _ptr(dq), _ptr(dkv), _ptr(dkv_f32),
-                            flags, ctypes.c_void_p(ws_addr),
-                            ws.numel() - (ws_addr - ws.data_ptr()), _stream(dev)))
+    ws, ws_addr = _workspace(bwd_workspace_bytes(S, S_kv, H, K, flags, G), dev)
+    _lib.check(lib.smla_bwd_g(_ptr(q3), _ptr(kv3), _ptr(o3), _ptr(do3), _ptr(ix), _ptr(ls),
+                              S, S_kv, H, G, K, float(sm_scale), _ptr(dq), _ptr(dkv),
+                              _ptr(dkv_f32), flags, ctypes.c_void_p(ws_addr),
+                              ws.numel() - (ws_addr - ws.data_ptr()), _stream(dev)))
     return dq, dkv
 
 
@@ -179,7 +197,7 @@ def validate_indices(indices: torch.Tensor, s_kv: int) -> int:
     """Number of index entries that are neither -1 nor in [0, s_kv).
     (Synchronizes the current stream to read the count.)"""
     lib = _lib.load()
-    ix = _flat_idx(indices)
+    ix = indices.reshape(-1, indices.shape[-1])   # [S, K], [S, G, K] or [1, S, G, K]
     if ix.dtype != torch.int32:
         ix = ix.to(torch.int32)
     ix = _prep(ix, torch.int32, "indices")
@@ -316,21 +334,26 @@ class SparseMLARunner:
     """Repeated forward + backward on fixed shapes with every buffer
     preallocated: each call enqueues the library's kernels and allocates
     nothing.  Inputs must already be contiguous bf16/int32 GPU tensors of the
-    shapes given here."""
+    shapes given here: with kv_groups = G > 1, kv [s_kv, G, 576] and indices
+    [s_q, G, topk] (dkv like kv)."""
 
     def __init__(self, s_q: int, s_kv: int, heads: int, topk: int, device="cuda",
-                 dkv_atomic: bool = False, dkv_stored_p: bool = False):
+                 dkv_atomic: bool = False, dkv_stored_p: bool = False, kv_groups: int = 1):
         self.lib = _lib.load()
         self.shape = (s_q, s_kv, heads, topk)
+        self.G = kv_groups
+        kv_shape = (s_kv, D_K) if kv_groups == 1 else (s_kv, kv_groups, D_K)
+        self._kv_shape = kv_shape
+        self._idx_shape = (s_q, topk) if kv_groups == 1 else (s_q, kv_groups, topk)
         self._bflags = ((_lib.SMLA_DKV_ATOMIC if dkv_atomic else 0) |
                         (_lib.SMLA_DKV_STORED_P if dkv_stored_p else 0))
         dev = torch.device(device)
         self.out = torch.empty(s_q, heads, D_V, dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty(s_q, heads, dtype=torch.float32, device=dev)
         self.dq = torch.empty(s_q, heads, D_K, dtype=torch.bfloat16, device=dev)
-        self.dkv = torch.empty(s_kv, D_K, dtype=torch.bfloat16, device=dev)
-        fb = fwd_workspace_bytes(s_q, s_kv, heads, topk)
-        bb = bwd_workspace_bytes(s_q, s_kv, heads, topk, self._bflags)
+        self.dkv = torch.empty(*kv_shape, dtype=torch.bfloat16, device=dev)
+        fb = fwd_workspace_bytes(s_q, s_kv, heads, topk, kv_groups)
+        bb = bwd_workspace_bytes(s_q, s_kv, heads, topk, self._bflags, kv_groups)
         self._fws, self._fws_addr = _workspace(fb, dev)
         self._bws, self._bws_addr = _workspace(bb, dev)
         self._fb, self._bb = fb, bb
@@ -339,8 +362,8 @@ class SparseMLARunner:
     def _check(self, q, kv, idx, dout=None):
         s_q, s_kv, h, k = self.shape
         assert q.shape == (s_q, h, D_K) and q.dtype == torch.bfloat16 and q.is_contiguous()
-        assert kv.shape == (s_kv, D_K) and kv.dtype == torch.bfloat16 and kv.is_contiguous()
-        assert idx.shape == (s_q, k) and idx.dtype == torch.int32 and idx.is_contiguous()
+        assert kv.shape == self._kv_shape and kv.dtype == torch.bfloat16 and kv.is_contiguous()
+        assert idx.shape == self._idx_shape and idx.dtype == torch.int32 and idx.is_contiguous()
         if dout is not None:
             assert dout.shape == (s_q, h, D_V) and dout.dtype == torch.bfloat16
             assert dout.is_contiguous()
@@ -349,27 +372,27 @@ class SparseMLARunner:
         """Build the index plan once (smla_plan) into the backward workspace;
         fwd / bwd with planned=True then reuse it (same indices)."""
         s_q, s_kv, h, k = self.shape
-        _lib.check(self.lib.smla_plan(_ptr(idx), s_q, s_kv, h, k,
-                                      ctypes.c_void_p(self._bws_addr), self._bb,
-                                      _stream(self.device)))
+        _lib.check(self.lib.smla_plan_g(_ptr(idx), s_q, s_kv, h, self.G, k,
+                                        ctypes.c_void_p(self._bws_addr), self._bb,
+                                        _stream(self.device)))
 
     def fwd(self, q, kv, idx, sm_scale, planned: bool = False):
         s_q, s_kv, h, k = self.shape
         ws, wb = (self._bws_addr, self._bb) if planned else (self._fws_addr, self._fb)
-        _lib.check(self.lib.smla_fwd_ex(_ptr(q), _ptr(kv), _ptr(idx), s_q, s_kv, h, k,
-                                        float(sm_scale), _ptr(self.out), _ptr(self.lse),
-                                        _lib.SMLA_PLAN_READY if planned else 0, ctypes.c_void_p(ws), wb,
-                                        _stream(self.device)))
+        _lib.check(self.lib.smla_fwd_g(_ptr(q), _ptr(kv), _ptr(idx), s_q, s_kv, h, self.G, k,
+                                       float(sm_scale), _ptr(self.out), _ptr(self.lse),
+                                       _lib.SMLA_PLAN_READY if planned else 0, ctypes.c_void_p(ws),
+                                       wb, _stream(self.device)))
         return self.out, self.lse
 
     def bwd(self, q, kv, dout, idx, sm_scale, planned: bool = False):
         s_q, s_kv, h, k = self.shape
-        _lib.check(self.lib.smla_bwd(_ptr(q), _ptr(kv), _ptr(self.out), _ptr(dout), _ptr(idx),
-                                     _ptr(self.lse), s_q, s_kv, h, k, float(sm_scale),
-                                     _ptr(self.dq), _ptr(self.dkv), ctypes.c_void_p(0),
-                                     self._bflags | (_lib.SMLA_PLAN_READY if planned else 0),
-                                     ctypes.c_void_p(self._bws_addr), self._bb,
-                                     _stream(self.device)))
+        _lib.check(self.lib.smla_bwd_g(_ptr(q), _ptr(kv), _ptr(self.out), _ptr(dout), _ptr(idx),
+                                       _ptr(self.lse), s_q, s_kv, h, self.G, k, float(sm_scale),
+                                       _ptr(self.dq), _ptr(self.dkv), ctypes.c_void_p(0),
+                                       self._bflags | (_lib.SMLA_PLAN_READY if planned else 0),
+                                       ctypes.c_void_p(self._bws_addr), self._bb,
+                                       _stream(self.device)))
         return self.dq, self.dkv
 
 

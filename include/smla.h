@@ -24,7 +24,8 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are device pointers owned by the caller, row-major
  *    and contiguous, 16-byte aligned.  bf16 tensors are passed as void*.
- *  - q [s_q, heads, 576] bf16; kv [s_kv, 576] bf16 (one KV group);
+ *  - q [s_q, heads, 576] bf16; kv [s_kv, 576] bf16 (one KV group; the *_g
+ *    calls below take several);
  *    indices [s_q, topk] int32; out and dout [s_q, heads, 512] bf16;
  *    lse [s_q, heads] fp32 (natural log); dq [s_q, heads, 576] bf16;
  *    dkv [s_kv, 576] bf16; dkv_f32 [s_kv, 576] fp32.
@@ -152,6 +153,38 @@ int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,
 
 size_t smla_bwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
                                uint32_t flags);
+
+/* KV groups.  The kernel excerpts of the miles PR #2079 digest ("fix GLM-5
+ * sparse-MLA kernel -1 index OOB and NaN gradients", key code snippets) index
+ * the indices and the kv by a kv-group coordinate derived from the query head
+ * block: the heads split into kv_groups equal blocks and block g attends over
+ * kv group g with its own index rows.  These calls take that layout:
+ *   q [s_q, heads, 576], out / dout [s_q, heads, 512], lse [s_q, heads],
+ *   dq [s_q, heads, 576] as before; kv [s_kv, kv_groups, 576] bf16;
+ *   indices [s_q, kv_groups, topk] int32 (row (s, g) lists rows of kv group
+ *   g; valid iff 0 <= index < s_kv, as before); dkv [s_kv, kv_groups, 576]
+ *   bf16 and dkv_f32 [s_kv, kv_groups, 576] fp32.
+ * Head h uses kv group h / (heads / kv_groups).  heads / kv_groups must be 8,
+ * 16, 32, 64 or 128; 1 <= kv_groups <= 64; s_kv * kv_groups < 2^24.  Flags,
+ * workspace rules and errors are those of the calls above (SMLA_PLAN_READY
+ * needs a plan from smla_plan_g with the same sizes).  kv_groups = 1 is
+ * exactly smla_plan / smla_fwd_ex / smla_bwd. */
+int smla_plan_g(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads,
+                int32_t kv_groups, int32_t topk, void* workspace, size_t workspace_bytes,
+                void* stream);
+int smla_fwd_g(const void* q, const void* kv, const int32_t* indices,
+               int64_t s_q, int64_t s_kv, int32_t heads, int32_t kv_groups, int32_t topk,
+               float sm_scale, void* out, float* lse, uint32_t flags, void* workspace,
+               size_t workspace_bytes, void* stream);
+size_t smla_fwd_workspace_size_g(int64_t s_q, int64_t s_kv, int32_t heads, int32_t kv_groups,
+                                 int32_t topk);
+int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
+               const int32_t* indices, const float* lse,
+               int64_t s_q, int64_t s_kv, int32_t heads, int32_t kv_groups, int32_t topk,
+               float sm_scale, void* dq, void* dkv, float* dkv_f32, uint32_t flags,
+               void* workspace, size_t workspace_bytes, void* stream);
+size_t smla_bwd_workspace_size_g(int64_t s_q, int64_t s_kv, int32_t heads, int32_t kv_groups,
+                                 int32_t topk, uint32_t flags);
 
 /* Index production, the step before the attention: for every query row s,
  * the top-k kv positions of its indexer logits inside its key range

@@ -53,6 +53,20 @@ def test_version_and_workspace_queries(lib):
     assert lib.smla_bwd_workspace_size(16, 1 << 24, 8, 8, 0) == 0     # s_kv too large
 
 
+def test_kv_group_workspace_queries(lib):
+    # (token, kv group) pairs are rows of heads / G heads over s_kv * G flat kv rows
+    assert lib.smla_fwd_workspace_size_g(300, 900, 16, 2, 64) == lib.smla_fwd_workspace_size(600, 1800, 8, 64) > 0
+    assert lib.smla_fwd_workspace_size_g(300, 900, 8, 1, 64) == lib.smla_fwd_workspace_size(300, 900, 8, 64)
+    for flags in (0, 2, 8):
+        assert (lib.smla_bwd_workspace_size_g(100, 500, 256, 2, 64, flags)
+                == lib.smla_bwd_workspace_size(200, 1000, 128, 64, flags) > 0)
+    assert lib.smla_fwd_workspace_size_g(16, 16, 24, 2, 8) == 0          # 12 heads per group
+    assert lib.smla_fwd_workspace_size_g(16, 16, 17, 2, 8) == 0          # heads not a multiple of G
+    assert lib.smla_fwd_workspace_size_g(16, 16, 16, 0, 8) == 0          # G < 1
+    assert lib.smla_fwd_workspace_size_g(16, 16, 8 * 65, 65, 8) == 0     # G > 64
+    assert lib.smla_bwd_workspace_size_g(16, 1 << 21, 64, 8, 8, 0) == 0  # s_kv * G >= 2^24
+
+
 FAKE = 0x100000  # 16-byte aligned, never dereferenced: the checks return first
 
 
@@ -141,6 +155,29 @@ def test_plan_and_fwd_ex_argument_errors(lib):
     assert lib.smla_fwd_ex(*args, 8, P(FAKE), fws, P(0)) == 5                  # unknown flag
     assert lib.smla_fwd_ex(*args, 4, P(FAKE), 64, P(0)) == 4                   # workspace
     assert call_bwd(lib, flags=16) == 5
+
+
+def test_kv_group_call_argument_errors(lib):
+    P = ctypes.c_void_p
+    fws = lib.smla_fwd_workspace_size_g(16, 16, 16, 2, 4)
+    bws = lib.smla_bwd_workspace_size_g(16, 16, 16, 2, 4, 0)
+    assert bws > fws > 0
+    assert lib.smla_plan_g(P(FAKE), 16, 16, 16, 3, 4, P(FAKE), bws, P(0)) == 2    # 16 % 3
+    assert lib.smla_plan_g(P(FAKE), 16, 16, 16, 2, 4, P(FAKE), fws, P(0)) == 4    # workspace
+    fargs = (P(FAKE), P(FAKE), P(FAKE), 16, 16)
+    tail = (0.1, P(FAKE), P(FAKE), 0, P(FAKE), fws, P(0))
+    assert lib.smla_fwd_g(*fargs, 16, 0, 4, *tail) == 2                          # G < 1
+    assert lib.smla_fwd_g(*fargs, 48, 2, 4, *tail) == 2                          # 24 per group
+    assert lib.smla_fwd_g(P(0), P(FAKE), P(FAKE), 16, 16, 16, 2, 4, *tail) == 1   # q
+    assert lib.smla_fwd_g(*fargs, 16, 2, 4, 0.1, P(FAKE), P(FAKE), 0, P(FAKE), fws - 1,
+                          P(0)) == 4
+    bargs = (P(FAKE),) * 6 + (16, 16)
+    btail = (0.1, P(FAKE), P(FAKE), P(0), 0, P(FAKE), bws, P(0))
+    assert lib.smla_bwd_g(*bargs, 16, 5, 4, *btail) == 2                          # 16 % 5
+    assert lib.smla_bwd_g(*bargs, 16, 2, 4, 0.1, P(FAKE), P(FAKE), P(0), 64, P(FAKE), bws,
+                          P(0)) == 5                                               # unknown flag
+    assert lib.smla_bwd_g(*bargs, 16, 2, 4, 0.1, P(FAKE), P(FAKE), P(0), 0, P(FAKE), bws - 1,
+                          P(0)) == 4
 
 
 def test_nonfinite_argument_errors(lib):

@@ -308,6 +308,49 @@ WORKLOADS = {
 }
 
 
+@dataclass
+class GroupedWorkload:
+    """Inputs with G kv groups: q [S, H, 576], kv [S_kv, G, 576], dout
+    [S, H, 512] (bf16 bits) and idx [S, G, K] int32; heads g H/G .. (g+1) H/G - 1
+    use kv group g and index rows idx[:, g]."""
+    q: np.ndarray
+    kv: np.ndarray
+    dout: np.ndarray
+    idx: np.ndarray
+    sm_scale: float
+
+    @property
+    def S(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def H(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def G(self) -> int:
+        return self.kv.shape[1]
+
+    @property
+    def S_kv(self) -> int:
+        return self.kv.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.idx.shape[2]
+
+
+def custom_grouped(S, H, G, K, S_kv, seed=0, **kw) -> GroupedWorkload:
+    """custom() per kv group (seeds seed * 64 + g), stacked: group g's heads,
+    kv rows and index rows are those of its own custom() draw."""
+    parts = [custom(S, H // G, K, S_kv, seed=seed * 64 + g, **kw) for g in range(G)]
+    return GroupedWorkload(q=np.concatenate([p.q for p in parts], axis=1),
+                           kv=np.stack([p.kv for p in parts], axis=1),
+                           dout=np.concatenate([p.dout for p in parts], axis=1),
+                           idx=np.stack([p.idx for p in parts], axis=1),
+                           sm_scale=parts[0].sm_scale)
+
+
 def causal_ranges(seqlens):
     """Key ranges [ks, ke) of packed causal sequences (input structure for the
     index-production step): token p of a sequence starting at row c sees kv
