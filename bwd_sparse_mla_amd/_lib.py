@@ -37,6 +37,8 @@ SIGNATURES = {
     "smla_fwd_g": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, ctypes.c_float,
                                   _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "smla_fwd_workspace_size_g": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
+    "smla_fwd_fp8": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, ctypes.c_float,
+                                    _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "smla_bwd_g": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32,
                                   ctypes.c_float, _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "smla_bwd_workspace_size_g": (_SZ, [_I64, _I64, _I32, _I32, _I32, ctypes.c_uint32]),

@@ -281,10 +281,15 @@ int smla_plan(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads, 
   return smla_plan_g(indices, s_q, s_kv, heads, 1, topk, workspace, workspace_bytes, stream);
 }
 
-int smla_fwd_g(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,
-               int32_t heads, int32_t kv_groups, int32_t topk, float sm_scale, void* out,
-               float* lse, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// The forward of smla_fwd_g (kv bf16 rows) and smla_fwd_fp8 (kv8 records).
+static int fwd_impl(const void* q, const void* kv, const uint8_t* kv8, const int32_t* indices,
+                    int64_t s_q, int64_t s_kv, int32_t heads, int32_t kv_groups, int32_t topk,
+                    float sm_scale, void* out, float* lse, uint32_t flags, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   g_last_error.clear();
+  if (!kv) kv = kv8;   // the checks below see the one kv given
   int st = check_shape(s_q, s_kv, heads, topk, kv_groups);
   if (st) return st;
   if (flags & ~SMLA_PLAN_READY) return fail(SMLA_ERR_FLAGS, "unknown flag bits");
@@ -312,7 +317,8 @@ int smla_fwd_g(const void* q, const void* kv, const int32_t* indices, int64_t s_
 
   FwdArgs fa{};
   fa.q = static_cast<const uint16_t*>(q);
-  fa.kv = static_cast<const uint16_t*>(kv);
+  fa.kv = kv8 ? nullptr : static_cast<const uint16_t*>(kv);
+  fa.kv8 = kv8;
   fa.s_q = s_q;
   fa.s_kv = s_kv;
   fa.scale_log2 = sm_scale * 1.4426950408889634f;
@@ -324,7 +330,34 @@ int smla_fwd_g(const void* q, const void* kv, const int32_t* indices, int64_t s_
   fa.order = reinterpret_cast<int*>(ws + p.off_gorder);
   fa.out = static_cast<uint16_t*>(out);
   fa.lse = lse;
+  if (kv8)
+    return hip_status(timed("fwd_fp8", s, [&] { return launch_fwd(fa, heads, s, true); }), "fwd_fp8");
   return hip_status(timed("fwd", s, [&] { return launch_fwd(fa, heads, s); }), "fwd");
+}
+
+extern "C" {
+
+int smla_fwd_g(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,
+               int32_t heads, int32_t kv_groups, int32_t topk, float sm_scale, void* out,
+               float* lse, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kv) {
+    g_last_error = "null tensor pointer";
+    return SMLA_ERR_NULL;
+  }
+  return fwd_impl(q, kv, nullptr, indices, s_q, s_kv, heads, kv_groups, topk, sm_scale, out, lse,
+                  flags, workspace, workspace_bytes, stream);
+}
+
+int smla_fwd_fp8(const void* q, const void* kv_fp8, const int32_t* indices, int64_t s_q,
+                 int64_t s_kv, int32_t heads, int32_t kv_groups, int32_t topk, float sm_scale,
+                 void* out, float* lse, uint32_t flags, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (!kv_fp8) {
+    g_last_error = "null tensor pointer";
+    return SMLA_ERR_NULL;
+  }
+  return fwd_impl(q, nullptr, static_cast<const uint8_t*>(kv_fp8), indices, s_q, s_kv, heads,
+                  kv_groups, topk, sm_scale, out, lse, flags, workspace, workspace_bytes, stream);
 }
 
 int smla_fwd_ex(const void* q, const void* kv, const int32_t* indices, int64_t s_q, int64_t s_kv,

@@ -24,6 +24,14 @@
 // sparse-MLA kernel -1 index OOB and NaN gradients", 实现拆解 item 2 and the
 // forward key code snippet); padding rows of a tile are copied from a zero
 // row, never from an address computed from -1.
+//
+// fp8 kv variant (FP8): kv rows are records of 512 e4m3 latent values, four
+// fp32 scales (one per 128 columns) and the 64 bf16 rope columns.  The PV
+// waves load their rows' latent bytes and scales into registers when they
+// would issue the copies, and after their PV MFMAs convert them (value =
+// e4m3 * scale, rounded to bf16) into the same swizzled bf16 tile; the score
+// waves copy the rope tails directly.  Everything downstream of the tile is
+// the bf16 kernel's.
 #include "smla_device.h"
 #include "smla_internal.h"
 
@@ -36,7 +44,20 @@ constexpr int FNB = 3;                // kv tile buffers
 constexpr int FNW = 8;                // waves per workgroup
 constexpr int SPS = FT + 8;           // P row stride (bf16): 80 bytes
 
-template <int H>
+// One PV wave's share of an fp8 tile: 8 rows, lane l holding latent bytes
+// 8l .. 8l+7 of each and the scale of its 128-column block.
+struct Fp8Rows {
+  uint2 v[FT / 4];
+  float sc[FT / 4];
+};
+
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, float sc) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);   // OCP e4m3 -> fp32 (exact)
+  return pack_bf2(f[0] * sc, f[1] * sc);
+}
+
+template <int H, bool FP8>
 __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
   __shared__ __attribute__((aligned(16))) char sK[FNB][KV32_TILE_BYTES];
@@ -89,16 +110,67 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   // the row indices of tile t + 1 by wave 5.
   auto issue = [&](int t) __attribute__((always_inline)) {
     const int b = t % FNB;
-    if (score_wave)
+    if constexpr (FP8) {
+      if (score_wave && wv < FT / 8) {   // rope tails of rows 8 wv .. 8 wv + 7
+        const int r = 8 * wv + (lane_id >> 3);
+        const int row = sRow[b][r];
+        const bool ok = r < min(FT, n_ent - t * FT) && (uint32_t)row < (uint32_t)a.s_kv;
+        const uint8_t* rec = ok ? a.kv8 + (uint64_t)(uint32_t)row * FP8_REC_BYTES
+                                : reinterpret_cast<const uint8_t*>(zero_row());
+        g2lds16_u(rec + FP8_ROPE_OFF + 16 * ((lane_id & 7) ^ swz_hi(r)),
+                  lds_offset(sK[b]) + (uint32_t)(FT * 1024 + 1024 * wv));
+      }
+    } else if (score_wave) {
       gather_kv_rows_nw<FT, ROW_CHUNKS, 4, false, true>(sK[b], a.kv, a.s_kv, sRow[b],
                                                         min(FT, n_ent - t * FT), wv, lane_id);
-    else
+    } else {
       gather_kv_rows_nw<FT, ROW_CHUNKS, 4, true, false>(sK[b], a.kv, a.s_kv, sRow[b],
                                                         min(FT, n_ent - t * FT), wv - 4, lane_id);
+    }
     copy_union_entries(nullptr, sMask[b], erow, emask, t * FT, n_ent, FT, wv, 5, 4, lane_id);
-    if (t + 1 < ntiles)
-      copy_union_entries(sRow[(t + 1) % FNB], nullptr, erow, emask, (t + 1) * FT, n_ent, FT, wv, 5,
-                         4, lane_id);
+    // Row indices of the tile the next copies need: t + 1, or t + 2 for fp8
+    // kv, whose PV-wave loads run a tile further ahead.  The buffer it lands
+    // in is read by no wave during this step.
+    const int ti = t + (FP8 ? 2 : 1);
+    if (ti < ntiles)
+      copy_union_entries(sRow[ti % FNB], nullptr, erow, emask, ti * FT, n_ent, FT, wv, 5, 4,
+                         lane_id);
+  };
+
+  // fp8: a PV wave's latent rows of tile t (rows 8c .. 8c+7, c = wv - 4):
+  // loads into registers, then (after the wave's MFMAs) the conversion into
+  // the tile.  Rows past the tile's count, and indices outside [0, s_kv),
+  // read the zero row (all-zero bytes: value 0, scale 0).
+  auto fp8_load = [&](int t) __attribute__((always_inline)) {
+    Fp8Rows f;
+    const int b = t % FNB, c = wv - 4;
+    const int count = min(FT, n_ent - t * FT);
+    const int vrow = sRow[b][8 * c + (lane_id & 7)];
+#pragma unroll
+    for (int i = 0; i < FT / 4; ++i) {
+      const int r = 8 * c + i;
+      const int row = __builtin_amdgcn_readlane(vrow, i);
+      const bool ok = r < count && (uint32_t)row < (uint32_t)a.s_kv;
+      const uint8_t* rec = ok ? a.kv8 + (uint64_t)(uint32_t)row * FP8_REC_BYTES
+                              : reinterpret_cast<const uint8_t*>(zero_row());
+      f.v[i] = *reinterpret_cast<const uint2*>(rec + 8 * lane_id);
+      f.sc[i] = *reinterpret_cast<const float*>(rec + FP8_SCALE_OFF + 4 * (lane_id >> 4));
+    }
+    return f;
+  };
+  auto fp8_store = [&](int t, const Fp8Rows& f) __attribute__((always_inline)) {
+    char* tile = sK[t % FNB];
+    const int c = wv - 4;
+#pragma unroll
+    for (int i = 0; i < FT / 4; ++i) {
+      const int r = 8 * c + i;
+      uint4_t w;
+      w[0] = fp8x2_to_bf16x2<false>(f.v[i].x, f.sc[i]);
+      w[1] = fp8x2_to_bf16x2<true>(f.v[i].x, f.sc[i]);
+      w[2] = fp8x2_to_bf16x2<false>(f.v[i].y, f.sc[i]);
+      w[3] = fp8x2_to_bf16x2<true>(f.v[i].y, f.sc[i]);
+      *reinterpret_cast<uint4_t*>(tile + 1024 * r + 16 * (lane_id ^ swz_lo(r))) = w;
+    }
   };
 
   // Scores and softmax of tile t (score waves).
@@ -212,11 +284,20 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
     }
   };
 
+  Fp8Rows f_cur;   // fp8: the latent rows of the next tile, loaded a step ago
   if (ntiles > 0) {
     copy_union_entries(sRow[0], nullptr, erow, emask, 0, n_ent, FT, wv, 5, 4, lane_id);
+    if (FP8 && ntiles > 1)
+      copy_union_entries(sRow[1], nullptr, erow, emask, FT, n_ent, FT, wv, 5, 4, lane_id);
     wait_vmcnt0();
     __syncthreads();
     issue(0);
+    if constexpr (FP8) {
+      if (!score_wave) {
+        fp8_store(0, fp8_load(0));
+        if (ntiles > 1) f_cur = fp8_load(1);
+      }
+    }
   }
   // Step j: the score waves take tile j, the PV waves tile j - 1; tile j + 1
   // is copied meanwhile into the buffer tile j - 2 used.  The two roles run
@@ -228,6 +309,20 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
       __syncthreads();
       if (j + 1 < ntiles) issue(j + 1);
       if (j < ntiles) score(j);
+    }
+  } else if constexpr (FP8) {
+    // Step j: load tile j + 2 (its indices landed at this step's barrier),
+    // PV of tile j - 1, then convert tile j + 1 (loaded a step ago) into its
+    // buffer before the next barrier.
+    for (int j = 0; j <= ntiles; ++j) {
+      wait_vmcnt0();
+      __syncthreads();
+      if (j + 1 < ntiles) issue(j + 1);
+      Fp8Rows f_next;
+      if (j + 2 < ntiles) f_next = fp8_load(j + 2);
+      if (j >= 1) pv(j - 1);
+      if (j + 1 < ntiles) fp8_store(j + 1, f_cur);
+      f_cur = f_next;
     }
   } else {
     for (int j = 0; j <= ntiles; ++j) {
@@ -277,17 +372,22 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream) {
-  if (a.G == 0) return hipSuccess;
+template <bool FP8>
+hipError_t launch_fwd_t(const FwdArgs& a, int heads, hipStream_t stream) {
   dim3 grid((unsigned)a.G), block(FNW * 64);
   switch (heads) {
-    case 8: fwd_kernel<8><<<grid, block, 0, stream>>>(a); break;
-    case 16: fwd_kernel<16><<<grid, block, 0, stream>>>(a); break;
-    case 32: fwd_kernel<32><<<grid, block, 0, stream>>>(a); break;
-    case 64: fwd_kernel<64><<<grid, block, 0, stream>>>(a); break;
+    case 8: fwd_kernel<8, FP8><<<grid, block, 0, stream>>>(a); break;
+    case 16: fwd_kernel<16, FP8><<<grid, block, 0, stream>>>(a); break;
+    case 32: fwd_kernel<32, FP8><<<grid, block, 0, stream>>>(a); break;
+    case 64: fwd_kernel<64, FP8><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream, bool fp8) {
+  if (a.G == 0) return hipSuccess;
+  return fp8 ? launch_fwd_t<true>(a, heads, stream) : launch_fwd_t<false>(a, heads, stream);
 }
 
 }  // namespace smla

@@ -61,9 +61,18 @@ struct PlanArgs {
   unsigned long long* korm;    // [NB, G] OR of the group's row masks for the block (with records)
 };
 
+// fp8 kv row record: e4m3 latent columns 0..511, then the fp32 scales of
+// columns 128b .. 128b+127 (b = 0..3), then the bf16 rope columns 512..575.
+constexpr int FP8_REC_BYTES = 656;
+constexpr int FP8_SCALE_OFF = 512;
+constexpr int FP8_ROPE_OFF = 528;
+
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* kv;
+  // fp8 kv (fp8 forward only; kv is then unused): FP8_REC_BYTES per row --
+  // 512 e4m3 latent values, 4 fp32 scales (one per 128 columns), 64 bf16 rope
+  const uint8_t* kv8;
   int64_t s_q, s_kv;
   float scale_log2;   // sm_scale * log2(e)
   int64_t G, qcap;
@@ -127,7 +136,7 @@ struct TopkArgs {
 hipError_t launch_fill_u32(void* ptr, size_t n_words, uint32_t value, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream);
-hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream, bool fp8 = false);
 hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream);
 // Work order of the query groups: decreasing union size (largest first).
 hipError_t launch_order_groups(const int* qcount, const int* xcount, int64_t G, int* order, int* xtotal,

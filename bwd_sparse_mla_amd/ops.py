@@ -142,6 +142,47 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_
     return out, lse
 
 
+FP8_REC_BYTES = 656
+
+
+def sparse_mla_fwd_fp8(q: torch.Tensor, kv_fp8: torch.Tensor, indices: torch.Tensor,
+                       sm_scale: float, out: torch.Tensor | None = None,
+                       lse: torch.Tensor | None = None):
+    """Forward over fp8 kv records: kv_fp8 is uint8 [S_kv, 656] (or
+    [S_kv, G, 656] with indices [S, G, K]), each row 512 e4m3 latent values,
+    four fp32 scales (one per 128 columns) and the 64 bf16 rope values.
+    Returns (out, lse) as sparse_mla_fwd does."""
+    lib = _lib.load()
+    lead = q.shape[:-1]
+    q3 = _prep(_flat_q(q), torch.bfloat16, "q")
+    k8 = kv_fp8[0] if kv_fp8.dim() == 4 else kv_fp8
+    if k8.dim() == 2:
+        k8 = k8.unsqueeze(1)
+    if k8.dim() != 3 or k8.shape[-1] != FP8_REC_BYTES:
+        raise ValueError(f"kv_fp8 must be [S_kv, {FP8_REC_BYTES}] or [S_kv, G, {FP8_REC_BYTES}]")
+    k8 = _prep(k8, torch.uint8, "kv_fp8")
+    G = k8.shape[1]
+    ix = _grouped_idx(indices, G)
+    if ix.dtype != torch.int32:
+        ix = ix.to(torch.int32)
+    ix = _prep(ix, torch.int32, "indices")
+    S, H, _ = q3.shape
+    if ix.shape[0] != S:
+        raise ValueError("indices must have one row per query token")
+    K = ix.shape[2]
+    S_kv = k8.shape[0]
+    dev = q3.device
+    if out is None:
+        out = torch.empty(*lead[:-1], H, D_V, dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty(*lead[:-1], H, dtype=torch.float32, device=dev)
+    ws, ws_addr = _workspace(fwd_workspace_bytes(S, S_kv, H, K, G), dev)
+    _lib.check(lib.smla_fwd_fp8(_ptr(q3), _ptr(k8), _ptr(ix), S, S_kv, H, G, K, float(sm_scale),
+                                _ptr(out), _ptr(lse), 0, ctypes.c_void_p(ws_addr),
+                                ws.numel() - (ws_addr - ws.data_ptr()), _stream(dev)))
+    return out, lse
+
+
 def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
                    indices: torch.Tensor, lse: torch.Tensor, sm_scale: float, *,
                    dkv_f32: torch.Tensor | None = None, accumulate: bool = False,
@@ -383,6 +424,17 @@ class SparseMLARunner:
                                        float(sm_scale), _ptr(self.out), _ptr(self.lse),
                                        _lib.SMLA_PLAN_READY if planned else 0, ctypes.c_void_p(ws),
                                        wb, _stream(self.device)))
+        return self.out, self.lse
+
+    def fwd_fp8(self, q, kv_fp8, idx, sm_scale, planned: bool = False):
+        """The forward over fp8 kv records (uint8 [s_kv, 656], or [s_kv, G,
+        656]) into the runner's out / lse."""
+        s_q, s_kv, h, k = self.shape
+        ws, wb = (self._bws_addr, self._bb) if planned else (self._fws_addr, self._fb)
+        _lib.check(self.lib.smla_fwd_fp8(_ptr(q), _ptr(kv_fp8), _ptr(idx), s_q, s_kv, h, self.G, k,
+                                         float(sm_scale), _ptr(self.out), _ptr(self.lse),
+                                         _lib.SMLA_PLAN_READY if planned else 0,
+                                         ctypes.c_void_p(ws), wb, _stream(self.device)))
         return self.out, self.lse
 
     def bwd(self, q, kv, dout, idx, sm_scale, planned: bool = False):

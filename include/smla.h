@@ -186,6 +186,22 @@ int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
 size_t smla_bwd_workspace_size_g(int64_t s_q, int64_t s_kv, int32_t heads, int32_t kv_groups,
                                  int32_t topk, uint32_t flags);
 
+/* Forward over an fp8 kv cache (a serving-side variant: the sources name fp8
+ * as a rollout format, Megatron-Bridge and miles digests; the record layout
+ * is this library's).  kv_fp8 holds one 656-byte record per kv row
+ * ([s_kv, kv_groups, 656] bytes, 16-byte aligned): bytes 0..511 the latent
+ * columns 0..511 as OCP e4m3 codes (4 exponent bits, bias 7, 3 mantissa
+ * bits), bytes 512..527 four little-endian fp32 scales (scale b multiplies
+ * columns 128b .. 128b+127), bytes 528..655 the rope columns 512..575 as
+ * bf16.  Each selected row is decoded as code * scale, rounded to bf16, and
+ * the forward then runs as smla_fwd_g does; every other argument, the
+ * workspace (smla_fwd_workspace_size_g) and the errors are those of
+ * smla_fwd_g.  Codes 0x7F / 0xFF (NaN) must not occur. */
+int smla_fwd_fp8(const void* q, const void* kv_fp8, const int32_t* indices,
+                 int64_t s_q, int64_t s_kv, int32_t heads, int32_t kv_groups, int32_t topk,
+                 float sm_scale, void* out, float* lse, uint32_t flags, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* Index production, the step before the attention: for every query row s,
  * the top-k kv positions of its indexer logits inside its key range
  * [ks[s], ke[s]) (clipped to [0, s_kv)), with k capped at the range length

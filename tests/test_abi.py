@@ -180,6 +180,17 @@ def test_kv_group_call_argument_errors(lib):
                           P(0)) == 4
 
 
+def test_fp8_forward_argument_errors(lib):
+    P = ctypes.c_void_p
+    fws = lib.smla_fwd_workspace_size_g(16, 16, 8, 1, 4)
+    tail = (0.1, P(FAKE), P(FAKE), 0, P(FAKE), fws, P(0))
+    assert lib.smla_fwd_fp8(P(FAKE), P(0), P(FAKE), 16, 16, 8, 1, 4, *tail) == 1       # kv_fp8
+    assert lib.smla_fwd_fp8(P(FAKE), P(FAKE), P(FAKE), 16, 16, 12, 1, 4, *tail) == 2   # heads
+    assert lib.smla_fwd_fp8(P(FAKE), P(FAKE + 8), P(FAKE), 16, 16, 8, 1, 4, *tail) == 3
+    assert lib.smla_fwd_fp8(P(FAKE), P(FAKE), P(FAKE), 16, 16, 8, 1, 4, 0.1, P(FAKE), P(FAKE),
+                            0, P(FAKE), fws - 1, P(0)) == 4
+
+
 def test_nonfinite_argument_errors(lib):
     P = ctypes.c_void_p
     cnt = P(FAKE)

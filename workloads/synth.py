@@ -351,6 +351,34 @@ def custom_grouped(S, H, G, K, S_kv, seed=0, **kw) -> GroupedWorkload:
                            sm_scale=parts[0].sm_scale)
 
 
+FP8_REC_BYTES = 656   # e4m3 latent [512], fp32 scales [4], bf16 rope [64]
+
+
+def quantize_kv_fp8(kv_bits: np.ndarray, pow2_scales: bool = True) -> np.ndarray:
+    """fp8 kv records [..., 656] (uint8) of bf16 kv rows [..., 576] (bits):
+    per row and 128-column block of the latent part, scale = amax / 448
+    (rounded up to a power of two with pow2_scales, so that every decoded
+    value is exact in bf16; 1 for an all-zero block) and codes = e4m3 (OCP,
+    round to nearest even) of value / scale; the rope columns keep their bf16
+    bits.  Input encoding for the fp8 forward's tests and bench."""
+    import torch
+    bits = np.ascontiguousarray(kv_bits, dtype=np.uint16)
+    lead = bits.shape[:-1]
+    flat = bits.reshape(-1, 576)
+    x = bf16_bits_to_f32(flat[:, :512]).reshape(-1, 4, 128)
+    amax = np.abs(x).max(axis=2)
+    scale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    if pow2_scales:
+        scale = np.exp2(np.ceil(np.log2(scale))).astype(np.float32)
+    y = np.clip(x / scale[:, :, None], -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(y.reshape(-1, 512)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    rec = np.zeros((flat.shape[0], FP8_REC_BYTES), dtype=np.uint8)
+    rec[:, :512] = codes
+    rec[:, 512:528] = scale.astype("<f4").view(np.uint8).reshape(-1, 16)
+    rec[:, 528:] = flat[:, 512:].astype("<u2").view(np.uint8).reshape(-1, 128)
+    return rec.reshape(*lead, FP8_REC_BYTES)
+
+
 def causal_ranges(seqlens):
     """Key ranges [ks, ke) of packed causal sequences (input structure for the
     index-production step): token p of a sequence starting at row c sees kv
