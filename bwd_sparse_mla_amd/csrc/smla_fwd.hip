@@ -26,12 +26,13 @@
 // row, never from an address computed from -1.
 //
 // fp8 kv variant (FP8): kv rows are records of 512 e4m3 latent values, four
-// fp32 scales (one per 128 columns) and the 64 bf16 rope columns.  The PV
-// waves load their rows' latent bytes and scales into registers when they
-// would issue the copies, and after their PV MFMAs convert them (value =
-// e4m3 * scale, rounded to bf16) into the same swizzled bf16 tile; the score
-// waves copy the rope tails directly.  Everything downstream of the tile is
-// the bf16 kernel's.
+// fp32 scales (one per 128 columns) and the 64 bf16 rope columns.  The
+// latent bytes and scales of a tile are copied directly into an LDS staging
+// buffer two tiles ahead (two buffers); a step before the tile is used, every
+// wave converts 4 of its rows (value = e4m3 * scale, rounded to bf16) from
+// the staging buffer into the same swizzled bf16 tile.  The score waves copy
+// the rope tails directly into the tile.  Everything downstream of the tile
+// is the bf16 kernel's.
 #include "smla_device.h"
 #include "smla_internal.h"
 
@@ -44,12 +45,11 @@ constexpr int FNB = 3;                // kv tile buffers
 constexpr int FNW = 8;                // waves per workgroup
 constexpr int SPS = FT + 8;           // P row stride (bf16): 80 bytes
 
-// One PV wave's share of an fp8 tile: 8 rows, lane l holding latent bytes
-// 8l .. 8l+7 of each and the scale of its 128-column block.
-struct Fp8Rows {
-  uint2 v[FT / 4];
-  float sc[FT / 4];
-};
+// fp8 staging buffer of one tile: latent bytes [FT][512], then 16 bytes of
+// scales per row for 64 rows (rows FT..63 are copies of the zero row, so the
+// scale copy is one full-wave instruction).
+constexpr int SF_LATENT = FT * FP8_SCALE_OFF;
+constexpr int SF_BYTES = SF_LATENT + 64 * 16;
 
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, float sc) {
@@ -61,6 +61,7 @@ template <int H, bool FP8>
 __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
   __shared__ __attribute__((aligned(16))) char sK[FNB][KV32_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char sF[2][FP8 ? SF_BYTES : 16];   // fp8 staging
   __shared__ __attribute__((aligned(16))) unsigned short sP[2][GROUP_ROWS * SPS];
   __shared__ __attribute__((aligned(16))) unsigned char sMask[FNB][256];  // token masks (word copies)
   __shared__ __attribute__((aligned(16))) int sRow[FNB][64];             // kv rows of a tile's entries
@@ -137,39 +138,57 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
                          lane_id);
   };
 
-  // fp8: a PV wave's latent rows of tile t (rows 8c .. 8c+7, c = wv - 4):
-  // loads into registers, then (after the wave's MFMAs) the conversion into
-  // the tile.  Rows past the tile's count, and indices outside [0, s_kv),
-  // read the zero row (all-zero bytes: value 0, scale 0).
-  auto fp8_load = [&](int t) __attribute__((always_inline)) {
-    Fp8Rows f;
-    const int b = t % FNB, c = wv - 4;
+  // fp8 staging copies of tile t into sF[t & 1]: wave w copies the latent
+  // bytes of rows 4w .. 4w+3 (two rows per copy: lanes 0-31 and 32-63, 16
+  // bytes each), wave 7 the 16 scale bytes of rows 0..63.  Rows past the
+  // tile's count, and indices outside [0, s_kv), read the zero row (all-zero
+  // bytes: value 0, scale 0).
+  auto fp8_stage = [&](int t) __attribute__((always_inline)) {
+    const int b = t % FNB;
     const int count = min(FT, n_ent - t * FT);
-    const int vrow = sRow[b][8 * c + (lane_id & 7)];
+    const uint32_t st = lds_offset(sF[t & 1]);
+    const int half = lane_id >> 5, m = lane_id & 31;
 #pragma unroll
-    for (int i = 0; i < FT / 4; ++i) {
-      const int r = 8 * c + i;
-      const int row = __builtin_amdgcn_readlane(vrow, i);
+    for (int p = 0; p < 2; ++p) {
+      const int r = 4 * wv + 2 * p + half;
+      const int row = sRow[b][r];
       const bool ok = r < count && (uint32_t)row < (uint32_t)a.s_kv;
       const uint8_t* rec = ok ? a.kv8 + (uint64_t)(uint32_t)row * FP8_REC_BYTES
                               : reinterpret_cast<const uint8_t*>(zero_row());
-      f.v[i] = *reinterpret_cast<const uint2*>(rec + 8 * lane_id);
-      f.sc[i] = *reinterpret_cast<const float*>(rec + FP8_SCALE_OFF + 4 * (lane_id >> 4));
+      g2lds16_u(rec + 16 * m, st + (uint32_t)(1024 * (2 * wv + p)));   // row r at 512 r
     }
-    return f;
+    if (wv == FNW - 1) {
+      const int r = lane_id;
+      const int row = sRow[b][r];
+      const bool ok = r < count && (uint32_t)row < (uint32_t)a.s_kv;
+      const uint8_t* rec = ok ? a.kv8 + (uint64_t)(uint32_t)row * FP8_REC_BYTES
+                              : reinterpret_cast<const uint8_t*>(zero_row());
+      g2lds16_u(rec + FP8_SCALE_OFF, st + (uint32_t)SF_LATENT);
+    }
   };
-  auto fp8_store = [&](int t, const Fp8Rows& f) __attribute__((always_inline)) {
+  // Conversion of tile t's staged rows 4w .. 4w+3 (wave w) into sK[t % 3]:
+  // in pair p, lane l takes bytes 16 (l mod 32) .. +15 of row 4w + 2p + l/32,
+  // which become bf16 chunks 2 (l mod 32) and 2 (l mod 32) + 1 of the row.
+  auto fp8_convert = [&](int t) __attribute__((always_inline)) {
+    const unsigned char* st = sF[t & 1];
     char* tile = sK[t % FNB];
-    const int c = wv - 4;
+    const int half = lane_id >> 5, m = lane_id & 31;
 #pragma unroll
-    for (int i = 0; i < FT / 4; ++i) {
-      const int r = 8 * c + i;
-      uint4_t w;
-      w[0] = fp8x2_to_bf16x2<false>(f.v[i].x, f.sc[i]);
-      w[1] = fp8x2_to_bf16x2<true>(f.v[i].x, f.sc[i]);
-      w[2] = fp8x2_to_bf16x2<false>(f.v[i].y, f.sc[i]);
-      w[3] = fp8x2_to_bf16x2<true>(f.v[i].y, f.sc[i]);
-      *reinterpret_cast<uint4_t*>(tile + 1024 * r + 16 * (lane_id ^ swz_lo(r))) = w;
+    for (int p = 0; p < 2; ++p) {
+      const int r = 4 * wv + 2 * p + half;
+      const uint4_t v = *reinterpret_cast<const uint4_t*>(st + FP8_SCALE_OFF * r + 16 * m);
+      const float sc = *reinterpret_cast<const float*>(st + SF_LATENT + 16 * r + 4 * (m >> 3));
+      uint4_t w0, w1;
+      w0[0] = fp8x2_to_bf16x2<false>(v[0], sc);
+      w0[1] = fp8x2_to_bf16x2<true>(v[0], sc);
+      w0[2] = fp8x2_to_bf16x2<false>(v[1], sc);
+      w0[3] = fp8x2_to_bf16x2<true>(v[1], sc);
+      w1[0] = fp8x2_to_bf16x2<false>(v[2], sc);
+      w1[1] = fp8x2_to_bf16x2<true>(v[2], sc);
+      w1[2] = fp8x2_to_bf16x2<false>(v[3], sc);
+      w1[3] = fp8x2_to_bf16x2<true>(v[3], sc);
+      *reinterpret_cast<uint4_t*>(tile + 1024 * r + 16 * ((2 * m) ^ swz_lo(r))) = w0;
+      *reinterpret_cast<uint4_t*>(tile + 1024 * r + 16 * ((2 * m + 1) ^ swz_lo(r))) = w1;
     }
   };
 
@@ -284,7 +303,6 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  Fp8Rows f_cur;   // fp8: the latent rows of the next tile, loaded a step ago
   if (ntiles > 0) {
     copy_union_entries(sRow[0], nullptr, erow, emask, 0, n_ent, FT, wv, 5, 4, lane_id);
     if (FP8 && ntiles > 1)
@@ -292,37 +310,38 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
     wait_vmcnt0();
     __syncthreads();
     issue(0);
-    if constexpr (FP8) {
-      if (!score_wave) {
-        fp8_store(0, fp8_load(0));
-        if (ntiles > 1) f_cur = fp8_load(1);
-      }
+    if constexpr (FP8) {   // tiles 0 and 1 staged, tile 0 converted
+      fp8_stage(0);
+      if (ntiles > 1) fp8_stage(1);
+      wait_vmcnt0();
+      __syncthreads();
+      fp8_convert(0);
     }
   }
   // Step j: the score waves take tile j, the PV waves tile j - 1; tile j + 1
   // is copied meanwhile into the buffer tile j - 2 used.  The two roles run
   // separate loops (so each keeps only its own state in registers) with the
-  // same count of workgroup barriers, one per step.
+  // same count of workgroup barriers, one per step.  fp8: tile j + 2 is
+  // staged (into the staging buffer tile j left; its indices landed at this
+  // step's barrier) and, after its role's work, every wave converts its rows
+  // of tile j + 1 (staged a step ago) into the buffer tile j - 2 used.
   if (score_wave) {
     for (int j = 0; j <= ntiles; ++j) {
       wait_vmcnt0();
       __syncthreads();
       if (j + 1 < ntiles) issue(j + 1);
+      if (FP8 && j + 2 < ntiles) fp8_stage(j + 2);
       if (j < ntiles) score(j);
+      if (FP8 && j + 1 < ntiles) fp8_convert(j + 1);
     }
   } else if constexpr (FP8) {
-    // Step j: load tile j + 2 (its indices landed at this step's barrier),
-    // PV of tile j - 1, then convert tile j + 1 (loaded a step ago) into its
-    // buffer before the next barrier.
     for (int j = 0; j <= ntiles; ++j) {
       wait_vmcnt0();
       __syncthreads();
       if (j + 1 < ntiles) issue(j + 1);
-      Fp8Rows f_next;
-      if (j + 2 < ntiles) f_next = fp8_load(j + 2);
+      if (j + 2 < ntiles) fp8_stage(j + 2);
       if (j >= 1) pv(j - 1);
-      if (j + 1 < ntiles) fp8_store(j + 1, f_cur);
-      f_cur = f_next;
+      if (j + 1 < ntiles) fp8_convert(j + 1);
     }
   } else {
     for (int j = 0; j <= ntiles; ++j) {

@@ -54,13 +54,6 @@ def _grouped_kv(kv: torch.Tensor) -> tuple[torch.Tensor, int]:
     return kv, kv.shape[1]
 
 
-def _flat_kv(kv: torch.Tensor) -> torch.Tensor:
-    kv3, g = _grouped_kv(kv)
-    if g != 1:
-        raise ValueError("this call takes one KV group")
-    return kv3[:, 0]
-
-
 def _grouped_idx(idx: torch.Tensor, groups: int) -> torch.Tensor:
     """indices as [S, G, K] ([S, K] when G = 1)."""
     if idx.dim() == 4:
@@ -73,10 +66,6 @@ def _grouped_idx(idx: torch.Tensor, groups: int) -> torch.Tensor:
         raise ValueError(f"indices must be [S, {groups}, K] for {groups} KV group(s), "
                          f"got {tuple(idx.shape)}")
     return idx
-
-
-def _flat_idx(idx: torch.Tensor) -> torch.Tensor:
-    return _grouped_idx(idx, 1)[:, 0]
 
 
 def _prep(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
