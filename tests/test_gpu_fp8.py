@@ -9,7 +9,10 @@ latent codes, per-128-column fp32 scales and bf16 rope):
     fp32 scales (amax / 448), padding, empty rows and out-of-range indices,
     and bit for bit against the bf16 forward over the oracle's decoded rows;
   * with several kv groups and 128 heads per group, against the grouped
-    oracle; the plan built once gives the one-shot result bit for bit.
+    oracle; the plan built once gives the one-shot result bit for bit;
+  * at the full size of the packed ragged batch in the bench's launch
+    configuration: bit for bit the bf16 forward over the decoded rows, and
+    sampled tokens against the oracle.
 """
 import numpy as np
 import pytest
@@ -120,4 +123,37 @@ def test_fp8_forward_with_kv_groups_and_the_plan_built_once():
     e_out = rel_err(bf16_to_np64(out), r_out)
     e_lse = rel_err(lse.cpu().numpy().astype(np.float64), r_lse)
     print(f"[fp8] kv groups rel errors out {e_out:.3e} lse {e_lse:.3e}", flush=True)
+    assert e_out <= TOL and e_lse <= TOL
+
+
+def test_fp8_forward_full_size_in_the_bench_configuration():
+    # the packed ragged batch (S = 4096, H = 8, topk = 2048) through the
+    # runner with the plan built once, as the bench times it: bit for bit the
+    # bf16 forward over the oracle's decoded rows, and sampled tokens against
+    # the oracle
+    import bwd_sparse_mla_amd as smla
+    from oracle import sparse_mla_fwd
+    w = synth.WORKLOADS["packed_ragged"]()
+    print(f"[fp8] full size {w.name}", flush=True)
+    rec = synth.quantize_kv_fp8(w.kv, pow2_scales=False)
+    kv64 = kv_rows_bf16(rec)
+    kv_bits = synth.f32_to_bf16_bits(kv64.astype(np.float32))
+    q, idx = to_torch_bf16(w.q), torch.from_numpy(np.ascontiguousarray(w.idx)).cuda()
+    run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, q.device)
+    run.plan(idx)
+    out8, lse8 = (t.clone() for t in run.fwd_fp8(q, torch.from_numpy(rec).cuda(), idx,
+                                                 w.sm_scale, planned=True))
+    out, lse = run.fwd(q, to_torch_bf16(kv_bits), idx, w.sm_scale, planned=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out8.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(lse8.view(torch.int32), lse.view(torch.int32))
+    rng = np.random.default_rng(7)
+    ends = np.cumsum(w.seqlens) - 1
+    toks = np.unique(np.concatenate([ends, rng.choice(w.S, 12, replace=False)]))
+    r_out, r_lse = sparse_mla_fwd(synth.bf16_bits_to_f64(w.q[toks]), kv64, w.idx[toks],
+                                  w.sm_scale)
+    sel = torch.as_tensor(toks, device="cuda")
+    e_out = rel_err(bf16_to_np64(out8.index_select(0, sel)), r_out)
+    e_lse = rel_err(lse8.index_select(0, sel).cpu().numpy().astype(np.float64), r_lse)
+    print(f"[fp8] full size sampled rel errors out {e_out:.3e} lse {e_lse:.3e}", flush=True)
     assert e_out <= TOL and e_lse <= TOL
