@@ -30,7 +30,8 @@
 // latent bytes and scales of a tile are copied directly into an LDS staging
 // buffer two tiles ahead (two buffers); a step before the tile is used, every
 // wave converts 4 of its rows (value = e4m3 * scale, rounded to bf16) from
-// the staging buffer into the same swizzled bf16 tile.  The score waves copy
+// the staging buffer into the same swizzled bf16 tile, right after the
+// step's barrier.  The score waves copy
 // the rope tails directly into the tile.  Everything downstream of the tile
 // is the bf16 kernel's.
 #include "smla_device.h"
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   // separate loops (so each keeps only its own state in registers) with the
   // same count of workgroup barriers, one per step.  fp8: tile j + 2 is
   // staged (into the staging buffer tile j left; its indices landed at this
-  // step's barrier) and, after its role's work, every wave converts its rows
+  // step's barrier) and, before its role's work, every wave converts its rows
   // of tile j + 1 (staged a step ago) into the buffer tile j - 2 used.
   if (score_wave) {
     for (int j = 0; j <= ntiles; ++j) {
@@ -331,8 +332,8 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
       __syncthreads();
       if (j + 1 < ntiles) issue(j + 1);
       if (FP8 && j + 2 < ntiles) fp8_stage(j + 2);
-      if (j < ntiles) score(j);
       if (FP8 && j + 1 < ntiles) fp8_convert(j + 1);
+      if (j < ntiles) score(j);
     }
   } else if constexpr (FP8) {
     for (int j = 0; j <= ntiles; ++j) {
@@ -340,8 +341,8 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
       __syncthreads();
       if (j + 1 < ntiles) issue(j + 1);
       if (j + 2 < ntiles) fp8_stage(j + 2);
-      if (j >= 1) pv(j - 1);
       if (j + 1 < ntiles) fp8_convert(j + 1);
+      if (j >= 1) pv(j - 1);
     }
   } else {
     for (int j = 0; j <= ntiles; ++j) {
