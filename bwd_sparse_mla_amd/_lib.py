@@ -11,6 +11,7 @@ SMLA_DKV_ACCUMULATE = 1
 SMLA_DKV_ATOMIC = 2
 SMLA_PLAN_READY = 4
 SMLA_DKV_STORED_P = 8
+SMLA_FP8_POW2_SCALES = 16
 SMLA_DTYPE_BF16 = 0
 SMLA_DTYPE_F32 = 1
 

@@ -292,7 +292,8 @@ static int fwd_impl(const void* q, const void* kv, const uint8_t* kv8, const int
   if (!kv) kv = kv8;   // the checks below see the one kv given
   int st = check_shape(s_q, s_kv, heads, topk, kv_groups);
   if (st) return st;
-  if (flags & ~SMLA_PLAN_READY) return fail(SMLA_ERR_FLAGS, "unknown flag bits");
+  const uint32_t known = SMLA_PLAN_READY | (kv8 ? SMLA_FP8_POW2_SCALES : 0u);
+  if (flags & ~known) return fail(SMLA_ERR_FLAGS, "unknown flag bits");
   if (!kv || (s_q > 0 && (!q || !indices || !out || !lse)))
     return fail(SMLA_ERR_NULL, "null tensor pointer");
   if (!aligned16(q) || !aligned16(kv) || !aligned16(indices) || !aligned16(out) || !aligned16(lse))
@@ -330,8 +331,10 @@ static int fwd_impl(const void* q, const void* kv, const uint8_t* kv8, const int
   fa.order = reinterpret_cast<int*>(ws + p.off_gorder);
   fa.out = static_cast<uint16_t*>(out);
   fa.lse = lse;
-  if (kv8)
-    return hip_status(timed("fwd_fp8", s, [&] { return launch_fwd(fa, heads, s, true); }), "fwd_fp8");
+  if (kv8) {
+    const int mode = (flags & SMLA_FP8_POW2_SCALES) ? 2 : 1;
+    return hip_status(timed("fwd_fp8", s, [&] { return launch_fwd(fa, heads, s, mode); }), "fwd_fp8");
+  }
   return hip_status(timed("fwd", s, [&] { return launch_fwd(fa, heads, s); }), "fwd");
 }
 

@@ -57,8 +57,18 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, float sc) {
   const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);   // OCP e4m3 -> fp32 (exact)
   return pack_bf2(f[0] * sc, f[1] * sc);
 }
+// The same for a power-of-two scale, in one instruction: the scaled
+// conversion applies only the scale's exponent, which is the whole scale
+// when it is a power of two (the product is then exact in bf16).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2_pow2(uint32_t w, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, sc, HI));
+}
 
-template <int H, bool FP8>
+// FP8: 0 bf16 kv rows; 1 fp8 records with fp32 scales; 2 fp8 records whose
+// scales are powers of two.
+template <int H, int FP8>
 __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
   __shared__ __attribute__((aligned(16))) char sK[FNB][KV32_TILE_BYTES];
@@ -180,14 +190,25 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
       const uint4_t v = *reinterpret_cast<const uint4_t*>(st + FP8_SCALE_OFF * r + 16 * m);
       const float sc = *reinterpret_cast<const float*>(st + SF_LATENT + 16 * r + 4 * (m >> 3));
       uint4_t w0, w1;
-      w0[0] = fp8x2_to_bf16x2<false>(v[0], sc);
-      w0[1] = fp8x2_to_bf16x2<true>(v[0], sc);
-      w0[2] = fp8x2_to_bf16x2<false>(v[1], sc);
-      w0[3] = fp8x2_to_bf16x2<true>(v[1], sc);
-      w1[0] = fp8x2_to_bf16x2<false>(v[2], sc);
-      w1[1] = fp8x2_to_bf16x2<true>(v[2], sc);
-      w1[2] = fp8x2_to_bf16x2<false>(v[3], sc);
-      w1[3] = fp8x2_to_bf16x2<true>(v[3], sc);
+      if constexpr (FP8 == 2) {
+        w0[0] = fp8x2_to_bf16x2_pow2<false>(v[0], sc);
+        w0[1] = fp8x2_to_bf16x2_pow2<true>(v[0], sc);
+        w0[2] = fp8x2_to_bf16x2_pow2<false>(v[1], sc);
+        w0[3] = fp8x2_to_bf16x2_pow2<true>(v[1], sc);
+        w1[0] = fp8x2_to_bf16x2_pow2<false>(v[2], sc);
+        w1[1] = fp8x2_to_bf16x2_pow2<true>(v[2], sc);
+        w1[2] = fp8x2_to_bf16x2_pow2<false>(v[3], sc);
+        w1[3] = fp8x2_to_bf16x2_pow2<true>(v[3], sc);
+      } else {
+        w0[0] = fp8x2_to_bf16x2<false>(v[0], sc);
+        w0[1] = fp8x2_to_bf16x2<true>(v[0], sc);
+        w0[2] = fp8x2_to_bf16x2<false>(v[1], sc);
+        w0[3] = fp8x2_to_bf16x2<true>(v[1], sc);
+        w1[0] = fp8x2_to_bf16x2<false>(v[2], sc);
+        w1[1] = fp8x2_to_bf16x2<true>(v[2], sc);
+        w1[2] = fp8x2_to_bf16x2<false>(v[3], sc);
+        w1[3] = fp8x2_to_bf16x2<true>(v[3], sc);
+      }
       *reinterpret_cast<uint4_t*>(tile + 1024 * r + 16 * ((2 * m) ^ swz_lo(r))) = w0;
       *reinterpret_cast<uint4_t*>(tile + 1024 * r + 16 * ((2 * m + 1) ^ swz_lo(r))) = w1;
     }
@@ -392,7 +413,7 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
 
 }  // namespace
 
-template <bool FP8>
+template <int FP8>
 hipError_t launch_fwd_t(const FwdArgs& a, int heads, hipStream_t stream) {
   dim3 grid((unsigned)a.G), block(FNW * 64);
   switch (heads) {
@@ -405,9 +426,14 @@ hipError_t launch_fwd_t(const FwdArgs& a, int heads, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream, bool fp8) {
+hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream, int fp8) {
   if (a.G == 0) return hipSuccess;
-  return fp8 ? launch_fwd_t<true>(a, heads, stream) : launch_fwd_t<false>(a, heads, stream);
+  switch (fp8) {
+    case 0: return launch_fwd_t<0>(a, heads, stream);
+    case 1: return launch_fwd_t<1>(a, heads, stream);
+    case 2: return launch_fwd_t<2>(a, heads, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace smla

@@ -136,7 +136,8 @@ struct TopkArgs {
 hipError_t launch_fill_u32(void* ptr, size_t n_words, uint32_t value, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream);
-hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream, bool fp8 = false);
+// fp8: 0 bf16 kv rows, 1 fp8 records (fp32 scales), 2 fp8 records with power-of-two scales
+hipError_t launch_fwd(const FwdArgs& a, int heads, hipStream_t stream, int fp8 = 0);
 hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream);
 // Work order of the query groups: decreasing union size (largest first).
 hipError_t launch_order_groups(const int* qcount, const int* xcount, int64_t G, int* order, int* xtotal,

@@ -136,11 +136,13 @@ FP8_REC_BYTES = 656
 
 def sparse_mla_fwd_fp8(q: torch.Tensor, kv_fp8: torch.Tensor, indices: torch.Tensor,
                        sm_scale: float, out: torch.Tensor | None = None,
-                       lse: torch.Tensor | None = None):
+                       lse: torch.Tensor | None = None, pow2_scales: bool = False):
     """Forward over fp8 kv records: kv_fp8 is uint8 [S_kv, 656] (or
     [S_kv, G, 656] with indices [S, G, K]), each row 512 e4m3 latent values,
     four fp32 scales (one per 128 columns) and the 64 bf16 rope values.
-    Returns (out, lse) as sparse_mla_fwd does."""
+    pow2_scales=True promises that every scale is a power of two (faster
+    conversion; other scales then give wrong values).  Returns (out, lse) as
+    sparse_mla_fwd does."""
     lib = _lib.load()
     lead = q.shape[:-1]
     q3 = _prep(_flat_q(q), torch.bfloat16, "q")
@@ -166,8 +168,9 @@ def sparse_mla_fwd_fp8(q: torch.Tensor, kv_fp8: torch.Tensor, indices: torch.Ten
     if lse is None:
         lse = torch.empty(*lead[:-1], H, dtype=torch.float32, device=dev)
     ws, ws_addr = _workspace(fwd_workspace_bytes(S, S_kv, H, K, G), dev)
+    flags = _lib.SMLA_FP8_POW2_SCALES if pow2_scales else 0
     _lib.check(lib.smla_fwd_fp8(_ptr(q3), _ptr(k8), _ptr(ix), S, S_kv, H, G, K, float(sm_scale),
-                                _ptr(out), _ptr(lse), 0, ctypes.c_void_p(ws_addr),
+                                _ptr(out), _ptr(lse), flags, ctypes.c_void_p(ws_addr),
                                 ws.numel() - (ws_addr - ws.data_ptr()), _stream(dev)))
     return out, lse
 
@@ -415,14 +418,18 @@ class SparseMLARunner:
                                        wb, _stream(self.device)))
         return self.out, self.lse
 
-    def fwd_fp8(self, q, kv_fp8, idx, sm_scale, planned: bool = False):
+    def fwd_fp8(self, q, kv_fp8, idx, sm_scale, planned: bool = False,
+                pow2_scales: bool = False):
         """The forward over fp8 kv records (uint8 [s_kv, 656], or [s_kv, G,
-        656]) into the runner's out / lse."""
+        656]) into the runner's out / lse (pow2_scales as in
+        sparse_mla_fwd_fp8)."""
         s_q, s_kv, h, k = self.shape
         ws, wb = (self._bws_addr, self._bb) if planned else (self._fws_addr, self._fb)
+        flags = ((_lib.SMLA_PLAN_READY if planned else 0) |
+                 (_lib.SMLA_FP8_POW2_SCALES if pow2_scales else 0))
         _lib.check(self.lib.smla_fwd_fp8(_ptr(q), _ptr(kv_fp8), _ptr(idx), s_q, s_kv, h, self.G, k,
                                          float(sm_scale), _ptr(self.out), _ptr(self.lse),
-                                         _lib.SMLA_PLAN_READY if planned else 0,
+                                         flags,
                                          ctypes.c_void_p(ws), wb, _stream(self.device)))
         return self.out, self.lse
 

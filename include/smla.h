@@ -90,6 +90,12 @@ enum smla_status {
 #define SMLA_PLAN_READY 4u      /* smla_fwd_ex / smla_bwd: the workspace already
                                    holds the index plan smla_plan built for the
                                    same indices and sizes; skip planning */
+#define SMLA_FP8_POW2_SCALES 16u /* smla_fwd_fp8: every scale of the fp8 kv
+                                   records is a power of two (E8M0-style
+                                   scales); each pair of codes then converts in
+                                   one scaled instruction, which applies only
+                                   the scale's exponent -- with any other scale
+                                   the values are wrong (no error is raised) */
 #define SMLA_DKV_STORED_P 8u    /* smla_bwd: the dq pass stores P and
                                    sm_scale * dS (bf16, per union entry and
                                    query row) in the workspace and the dkv pass
@@ -196,7 +202,8 @@ size_t smla_bwd_workspace_size_g(int64_t s_q, int64_t s_kv, int32_t heads, int32
  * bf16.  Each selected row is decoded as code * scale, rounded to bf16, and
  * the forward then runs as smla_fwd_g does; every other argument, the
  * workspace (smla_fwd_workspace_size_g) and the errors are those of
- * smla_fwd_g.  Codes 0x7F / 0xFF (NaN) must not occur. */
+ * smla_fwd_g; flags: 0, SMLA_PLAN_READY and/or SMLA_FP8_POW2_SCALES.  Codes
+ * 0x7F / 0xFF (NaN) must not occur. */
 int smla_fwd_fp8(const void* q, const void* kv_fp8, const int32_t* indices,
                  int64_t s_q, int64_t s_kv, int32_t heads, int32_t kv_groups, int32_t topk,
                  float sm_scale, void* out, float* lse, uint32_t flags, void* workspace,

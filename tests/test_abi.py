@@ -189,6 +189,13 @@ def test_fp8_forward_argument_errors(lib):
     assert lib.smla_fwd_fp8(P(FAKE), P(FAKE + 8), P(FAKE), 16, 16, 8, 1, 4, *tail) == 3
     assert lib.smla_fwd_fp8(P(FAKE), P(FAKE), P(FAKE), 16, 16, 8, 1, 4, 0.1, P(FAKE), P(FAKE),
                             0, P(FAKE), fws - 1, P(0)) == 4
+    # SMLA_FP8_POW2_SCALES (16) is known to the fp8 forward only
+    assert lib.smla_fwd_fp8(P(FAKE), P(FAKE), P(FAKE), 16, 16, 8, 1, 4, 0.1, P(FAKE), P(FAKE),
+                            16, P(FAKE), fws - 1, P(0)) == 4
+    assert lib.smla_fwd_fp8(P(FAKE), P(FAKE), P(FAKE), 16, 16, 8, 1, 4, 0.1, P(FAKE), P(FAKE),
+                            32, P(FAKE), fws, P(0)) == 5
+    assert lib.smla_fwd_g(P(FAKE), P(FAKE), P(FAKE), 16, 16, 8, 1, 4, 0.1, P(FAKE), P(FAKE),
+                          16, P(FAKE), fws, P(0)) == 5
 
 
 def test_nonfinite_argument_errors(lib):

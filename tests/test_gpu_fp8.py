@@ -4,7 +4,8 @@ latent codes, per-128-column fp32 scales and bf16 rope):
   * bit for bit equal to the bf16 forward over the decoded rows when every
     decoded value is exact in bf16 (power-of-two scales), on records that
     walk through every non-NaN e4m3 code: the decode of every code, the
-    record layout and the tile placement;
+    record layout and the tile placement -- with the general conversion and
+    with the one-instruction conversion for power-of-two scales;
   * against the oracle (decode to bf16 rows, then the fp64 forward) with
     fp32 scales (amax / 448), padding, empty rows and out-of-range indices,
     and bit for bit against the bf16 forward over the oracle's decoded rows;
@@ -62,11 +63,14 @@ def test_fp8_forward_is_the_bf16_forward_on_exact_decoded_rows():
     print(f"[fp8] all codes S={w.S} H={w.H} K={w.K} S_kv={w.S_kv}", flush=True)
     q = to_torch_bf16(w.q)
     idx = torch.from_numpy(w.idx).cuda()
-    out8, lse8 = smla.sparse_mla_fwd_fp8(q, torch.from_numpy(rec).cuda(), idx, w.sm_scale)
+    k8 = torch.from_numpy(rec).cuda()
+    out8, lse8 = smla.sparse_mla_fwd_fp8(q, k8, idx, w.sm_scale)
+    out2, lse2 = smla.sparse_mla_fwd_fp8(q, k8, idx, w.sm_scale, pow2_scales=True)
     out, lse = smla.sparse_mla_fwd(q, to_torch_bf16(kv_bits), idx, w.sm_scale)
     torch.cuda.synchronize()
-    assert torch.equal(out8.view(torch.int16), out.view(torch.int16))
-    assert torch.equal(lse8.view(torch.int32), lse.view(torch.int32))
+    for o, l in ((out8, lse8), (out2, lse2)):   # fp32-scale and power-of-two-scale conversions
+        assert torch.equal(o.view(torch.int16), out.view(torch.int16))
+        assert torch.equal(l.view(torch.int32), lse.view(torch.int32))
 
 
 CASES = {
@@ -157,3 +161,26 @@ def test_fp8_forward_full_size_in_the_bench_configuration():
     e_lse = rel_err(lse8.index_select(0, sel).cpu().numpy().astype(np.float64), r_lse)
     print(f"[fp8] full size sampled rel errors out {e_out:.3e} lse {e_lse:.3e}", flush=True)
     assert e_out <= TOL and e_lse <= TOL
+
+
+def test_fp8_power_of_two_scales_full_size():
+    # power-of-two scales at the packed ragged batch's full size: the
+    # one-instruction conversion gives the general conversion's result and
+    # the bf16 forward's over the decoded rows, bit for bit
+    import bwd_sparse_mla_amd as smla
+    w = synth.WORKLOADS["packed_ragged"]()
+    print(f"[fp8] power-of-two scales, full size {w.name}", flush=True)
+    rec = synth.quantize_kv_fp8(w.kv, pow2_scales=True)
+    kv_bits = synth.f32_to_bf16_bits(kv_rows_bf16(rec).astype(np.float32))
+    q, idx = to_torch_bf16(w.q), torch.from_numpy(np.ascontiguousarray(w.idx)).cuda()
+    k8 = torch.from_numpy(rec).cuda()
+    run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, q.device)
+    run.plan(idx)
+    o2, l2 = (t.clone() for t in run.fwd_fp8(q, k8, idx, w.sm_scale, planned=True,
+                                             pow2_scales=True))
+    o1, l1 = (t.clone() for t in run.fwd_fp8(q, k8, idx, w.sm_scale, planned=True))
+    ob, lb = run.fwd(q, to_torch_bf16(kv_bits), idx, w.sm_scale, planned=True)
+    torch.cuda.synchronize()
+    for o, l in ((o2, l2), (o1, l1)):
+        assert torch.equal(o.view(torch.int16), ob.view(torch.int16))
+        assert torch.equal(l.view(torch.int32), lb.view(torch.int32))
