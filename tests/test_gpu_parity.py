@@ -118,6 +118,16 @@ def test_kv_span_beyond_one_planner_window():
     check_full(w)
 
 
+@pytest.mark.parametrize("H", [8, 64])
+def test_maximum_topk(H):
+    # topk = 16384, the largest the library takes: with 8 tokens per query
+    # group the planner's repeated-slot flags are full (8 x 16384 slots), the
+    # kv span crosses two planner windows, repeats and padding included
+    w = synth.custom(S=16 if H == 8 else 3, H=H, K=16384, S_kv=20000, seed=28 + H, pad_frac=0.2,
+                     empty_frac=0.0, dup_frac=0.05)
+    check_full(w)
+
+
 def test_repeated_indices():
     w = synth.custom(S=30, H=8, K=96, S_kv=80, seed=3, pad_frac=0.2, empty_frac=0.1, dup_frac=0.3)
     assert any(len(set(r[r >= 0].tolist())) < (r >= 0).sum() for r in w.idx)

@@ -26,6 +26,8 @@ CASES = {
     "h64": lambda: synth.custom(S=33, H=64, K=130, S_kv=700, seed=24, pad_frac=0.25, dup_frac=0.05),
     "h128": lambda: synth.custom(S=21, H=128, K=150, S_kv=500, seed=26, pad_frac=0.2,
                                  empty_frac=0.1),
+    "max_topk": lambda: synth.custom(S=16, H=8, K=16384, S_kv=20000, seed=27, pad_frac=0.2,
+                                     empty_frac=0.0, dup_frac=0.05),
     "windows": lambda: synth.custom(S=12, H=16, K=700, S_kv=40000, seed=9, pad_frac=0.2,
                                     empty_frac=0.0),
     "oob": lambda: synth.custom(S=50, H=8, K=64, S_kv=200, seed=25, oob_frac=0.05),
