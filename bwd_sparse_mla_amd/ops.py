@@ -424,6 +424,10 @@ class SparseMLARunner:
         656]) into the runner's out / lse (pow2_scales as in
         sparse_mla_fwd_fp8)."""
         s_q, s_kv, h, k = self.shape
+        if (kv_fp8.dtype != torch.uint8 or not kv_fp8.is_cuda or not kv_fp8.is_contiguous()
+                or kv_fp8.numel() != s_kv * self.G * FP8_REC_BYTES):
+            raise ValueError(f"kv_fp8 must be a contiguous uint8 GPU tensor of "
+                             f"s_kv * kv_groups * {FP8_REC_BYTES} bytes")
         ws, wb = (self._bws_addr, self._bb) if planned else (self._fws_addr, self._fb)
         flags = ((_lib.SMLA_PLAN_READY if planned else 0) |
                  (_lib.SMLA_FP8_POW2_SCALES if pow2_scales else 0))
