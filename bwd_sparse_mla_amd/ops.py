@@ -392,25 +392,31 @@ class SparseMLARunner:
         self._fb, self._bb = fb, bb
         self.device = dev
 
-    def _check(self, q, kv, idx, dout=None):
+    def _check(self, q=None, kv=None, idx=None, dout=None):
+        """Shapes, dtypes and layouts of the given inputs against the runner's
+        (host-side only: no synchronization); raises ValueError."""
         s_q, s_kv, h, k = self.shape
-        assert q.shape == (s_q, h, D_K) and q.dtype == torch.bfloat16 and q.is_contiguous()
-        assert kv.shape == self._kv_shape and kv.dtype == torch.bfloat16 and kv.is_contiguous()
-        assert idx.shape == self._idx_shape and idx.dtype == torch.int32 and idx.is_contiguous()
-        if dout is not None:
-            assert dout.shape == (s_q, h, D_V) and dout.dtype == torch.bfloat16
-            assert dout.is_contiguous()
+        want = (("q", q, (s_q, h, D_K), torch.bfloat16), ("kv", kv, self._kv_shape, torch.bfloat16),
+                ("indices", idx, self._idx_shape, torch.int32),
+                ("dout", dout, (s_q, h, D_V), torch.bfloat16))
+        for name, t, shape, dtype in want:
+            if t is None:
+                continue
+            if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor of shape {shape}")
 
     def plan(self, idx):
         """Build the index plan once (smla_plan) into the backward workspace;
         fwd / bwd with planned=True then reuse it (same indices)."""
         s_q, s_kv, h, k = self.shape
+        self._check(idx=idx)
         _lib.check(self.lib.smla_plan_g(_ptr(idx), s_q, s_kv, h, self.G, k,
                                         ctypes.c_void_p(self._bws_addr), self._bb,
                                         _stream(self.device)))
 
     def fwd(self, q, kv, idx, sm_scale, planned: bool = False):
         s_q, s_kv, h, k = self.shape
+        self._check(q, kv, idx)
         ws, wb = (self._bws_addr, self._bb) if planned else (self._fws_addr, self._fb)
         _lib.check(self.lib.smla_fwd_g(_ptr(q), _ptr(kv), _ptr(idx), s_q, s_kv, h, self.G, k,
                                        float(sm_scale), _ptr(self.out), _ptr(self.lse),
@@ -424,6 +430,7 @@ class SparseMLARunner:
         656]) into the runner's out / lse (pow2_scales as in
         sparse_mla_fwd_fp8)."""
         s_q, s_kv, h, k = self.shape
+        self._check(q=q, idx=idx)
         if (kv_fp8.dtype != torch.uint8 or not kv_fp8.is_cuda or not kv_fp8.is_contiguous()
                 or kv_fp8.numel() != s_kv * self.G * FP8_REC_BYTES):
             raise ValueError(f"kv_fp8 must be a contiguous uint8 GPU tensor of "
@@ -439,6 +446,7 @@ class SparseMLARunner:
 
     def bwd(self, q, kv, dout, idx, sm_scale, planned: bool = False):
         s_q, s_kv, h, k = self.shape
+        self._check(q, kv, idx, dout)
         _lib.check(self.lib.smla_bwd_g(_ptr(q), _ptr(kv), _ptr(self.out), _ptr(dout), _ptr(idx),
                                        _ptr(self.lse), s_q, s_kv, h, self.G, k, float(sm_scale),
                                        _ptr(self.dq), _ptr(self.dkv), ctypes.c_void_p(0),

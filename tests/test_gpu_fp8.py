@@ -184,3 +184,22 @@ def test_fp8_power_of_two_scales_full_size():
     for o, l in ((o2, l2), (o1, l1)):
         assert torch.equal(o.view(torch.int16), ob.view(torch.int16))
         assert torch.equal(l.view(torch.int32), lb.view(torch.int32))
+
+
+def test_runner_rejects_wrong_inputs_before_launching():
+    import bwd_sparse_mla_amd as smla
+    run = smla.SparseMLARunner(8, 64, 8, 16, "cuda")
+    q = torch.zeros(8, 8, 576, dtype=torch.bfloat16, device="cuda")
+    idx = torch.zeros(8, 16, dtype=torch.int32, device="cuda")
+    kv = torch.zeros(64, 576, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        run.fwd(q[:, :4].contiguous(), kv, idx, 0.1)                       # wrong heads
+    with pytest.raises(ValueError):
+        run.fwd(q, kv[:32].contiguous(), idx, 0.1)                         # wrong s_kv
+    with pytest.raises(ValueError):
+        run.plan(idx.to(torch.int64))                                      # wrong dtype
+    with pytest.raises(ValueError):
+        run.fwd_fp8(q, torch.zeros(63, 656, dtype=torch.uint8, device="cuda"), idx, 0.1)
+    with pytest.raises(ValueError):
+        run.bwd(q, kv, torch.zeros(8, 8, 512, dtype=torch.bfloat16, device="cuda").transpose(0, 1), idx,
+                0.1)
