@@ -62,6 +62,35 @@ KernelShape kernel_shape(int64_t s_q, int64_t s_kv, int heads, int kv_groups) {
   return {r, s_kv * kv_groups, hg, 0};
 }
 
+// Group-major staging: with G > 1 kv groups and fewer than 64 heads per
+// group, a 64-row query group of token-major rows would hold rows of several
+// kv groups (disjoint kv rows, each masked for the others).  q, out, dout,
+// lse and the indices are then permuted into the workspace in group-major
+// order (row block g S + s holds token s's heads of group g), the kernels run
+// on those, and out, lse and dq are permuted back.  The staging area leads
+// the workspace; the plan's layout follows it.
+struct Stage {
+  bool on = false;
+  int hg = 0;
+  size_t q = 0, out = 0, dout = 0, lse = 0, dq = 0, idx = 0, bytes = 0;
+};
+Stage make_stage(int64_t s_q, int heads, int kv_groups, int topk) {
+  Stage st;
+  st.hg = heads / kv_groups;
+  if (kv_groups == 1 || st.hg >= 64 || s_q == 0) return st;
+  st.on = true;
+  const size_t rows = (size_t)s_q * heads;
+  size_t o = 0;
+  st.q = o;    o = align256(o + rows * 576 * 2);
+  st.out = o;  o = align256(o + rows * 512 * 2);
+  st.dout = o; o = align256(o + rows * 512 * 2);
+  st.lse = o;  o = align256(o + rows * 4);
+  st.dq = o;   o = align256(o + rows * 576 * 2);
+  st.idx = o;  o = align256(o + (size_t)s_q * kv_groups * topk * 4);
+  st.bytes = o;
+  return st;
+}
+
 // gfx950 check, cached per device ordinal.
 int check_device() {
   static std::mutex mu;
@@ -192,7 +221,8 @@ size_t smla_fwd_workspace_size_g(int64_t s_q, int64_t s_kv, int32_t heads, int32
                                  int32_t topk) {
   if (check_shape(s_q, s_kv, heads, topk, kv_groups) != SMLA_OK) return 0;
   const KernelShape k = kernel_shape(s_q, s_kv, heads, kv_groups);
-  return make_plan(k.s_q, k.s_kv, k.heads, topk, false).bytes;
+  return make_plan(k.s_q, k.s_kv, k.heads, topk, false).bytes +
+         make_stage(s_q, heads, kv_groups, topk).bytes;
 }
 
 size_t smla_fwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk) {
@@ -204,7 +234,8 @@ size_t smla_bwd_workspace_size_g(int64_t s_q, int64_t s_kv, int32_t heads, int32
   if (check_shape(s_q, s_kv, heads, topk, kv_groups) != SMLA_OK) return 0;
   const KernelShape k = kernel_shape(s_q, s_kv, heads, kv_groups);
   return make_plan(k.s_q, k.s_kv, k.heads, topk, true, (flags & SMLA_DKV_ATOMIC) != 0,
-                   (flags & SMLA_DKV_STORED_P) != 0).bytes;
+                   (flags & SMLA_DKV_STORED_P) != 0).bytes +
+         make_stage(s_q, heads, kv_groups, topk).bytes;
 }
 
 size_t smla_bwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
@@ -214,11 +245,13 @@ size_t smla_bwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t
 
 // Fills the planner's arguments for a workspace laid out by make_plan.
 static PlanArgs plan_args(const Plan& p, const int32_t* indices, int64_t s_q, int64_t s_kv,
-                          int topk, int idx_shift, int kv_groups, char* ws, bool backward) {
+                          int topk, int idx_shift, int kv_groups, int64_t gmajor_s, char* ws,
+                          bool backward) {
   PlanArgs pa{};
   pa.idx = indices;
   pa.idx_shift = idx_shift;
   pa.kv_groups = kv_groups;
+  pa.gmajor_s = gmajor_s;
   pa.s_kv_idx = s_kv / kv_groups;
   pa.s_q = s_q;
   pa.s_kv = s_kv;
@@ -260,20 +293,30 @@ int smla_plan_g(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads
   if (st) return st;
   if (s_q > 0 && !indices) return fail(SMLA_ERR_NULL, "indices is null");
   if (!aligned16(indices)) return fail(SMLA_ERR_ALIGN, "indices must be 16-byte aligned");
+  const int64_t s_tok = s_q;
+  const Stage sg = make_stage(s_q, heads, kv_groups, topk);
   const KernelShape k = kernel_shape(s_q, s_kv, heads, kv_groups);
   s_q = k.s_q;
   s_kv = k.s_kv;
   heads = k.heads;
   const Plan p = make_plan(s_q, s_kv, heads, topk, true);
-  if (!workspace || workspace_bytes < p.bytes)
+  if (!workspace || workspace_bytes < p.bytes + sg.bytes)
     return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_bwd_workspace_size()");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(SMLA_ERR_ALIGN, "workspace must be 256-byte aligned");
   if ((st = check_device())) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  return run_plan(p, plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups, ws, true), heads,
-                  true, s);
+  char* base = static_cast<char*>(workspace);
+  char* ws = base + sg.bytes;
+  if (sg.on) {
+    int32_t* ix = reinterpret_cast<int32_t*>(base + sg.idx);
+    if ((st = hip_status(launch_permute_pairs(indices, ix, s_tok, kv_groups, (int64_t)topk * 4, true, s),
+                         "permute")))
+      return st;
+    indices = ix;
+  }
+  return run_plan(p, plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups,
+                               sg.on ? s_tok : 0, ws, true), heads, true, s);
 }
 
 int smla_plan(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk,
@@ -298,6 +341,8 @@ static int fwd_impl(const void* q, const void* kv, const uint8_t* kv8, const int
     return fail(SMLA_ERR_NULL, "null tensor pointer");
   if (!aligned16(q) || !aligned16(kv) || !aligned16(indices) || !aligned16(out) || !aligned16(lse))
     return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const int64_t s_tok = s_q;
+  const Stage sg = make_stage(s_q, heads, kv_groups, topk);
   const KernelShape k = kernel_shape(s_q, s_kv, heads, kv_groups);
   s_q = k.s_q;
   s_kv = k.s_kv;
@@ -305,15 +350,32 @@ static int fwd_impl(const void* q, const void* kv, const uint8_t* kv8, const int
   // The forward fields of the workspace are a prefix of the backward layout,
   // so a plan built by smla_plan serves here too.
   const Plan p = make_plan(s_q, s_kv, heads, topk, false);
-  if (!workspace || workspace_bytes < p.bytes)
+  if (!workspace || workspace_bytes < p.bytes + sg.bytes)
     return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_fwd_workspace_size()");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(SMLA_ERR_ALIGN, "workspace must be 256-byte aligned");
   if ((st = check_device())) return st;
   if (s_q == 0) return SMLA_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups, ws, false);
+  char* base = static_cast<char*>(workspace);
+  char* ws = base + sg.bytes;
+  void* out_u = out;     // the caller's out / lse (token-major)
+  float* lse_u = lse;
+  if (sg.on) {   // group-major copies of q (and the indices, unless planned)
+    const int64_t qb = (int64_t)sg.hg * 576 * 2;
+    if ((st = hip_status(launch_permute_pairs(q, base + sg.q, s_tok, kv_groups, qb, true, s), "permute")))
+      return st;
+    if (!(flags & SMLA_PLAN_READY) &&
+        (st = hip_status(launch_permute_pairs(indices, base + sg.idx, s_tok, kv_groups,
+                                              (int64_t)topk * 4, true, s), "permute")))
+      return st;
+    q = base + sg.q;
+    indices = reinterpret_cast<const int32_t*>(base + sg.idx);
+    out = base + sg.out;
+    lse = reinterpret_cast<float*>(base + sg.lse);
+  }
+  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups,
+                                sg.on ? s_tok : 0, ws, false);
   if (!(flags & SMLA_PLAN_READY) && (st = run_plan(p, pa, heads, false, s))) return st;
 
   FwdArgs fa{};
@@ -333,9 +395,17 @@ static int fwd_impl(const void* q, const void* kv, const uint8_t* kv8, const int
   fa.lse = lse;
   if (kv8) {
     const int mode = (flags & SMLA_FP8_POW2_SCALES) ? 2 : 1;
-    return hip_status(timed("fwd_fp8", s, [&] { return launch_fwd(fa, heads, s, mode); }), "fwd_fp8");
+    st = hip_status(timed("fwd_fp8", s, [&] { return launch_fwd(fa, heads, s, mode); }), "fwd_fp8");
+  } else {
+    st = hip_status(timed("fwd", s, [&] { return launch_fwd(fa, heads, s); }), "fwd");
   }
-  return hip_status(timed("fwd", s, [&] { return launch_fwd(fa, heads, s); }), "fwd");
+  if (st || !sg.on) return st;
+  // out and lse back to token-major order
+  if ((st = hip_status(launch_permute_pairs(out, out_u, s_tok, kv_groups, (int64_t)sg.hg * 512 * 2,
+                                            false, s), "permute")))
+    return st;
+  return hip_status(launch_permute_pairs(lse, lse_u, s_tok, kv_groups, (int64_t)sg.hg * 4, false, s),
+                    "permute");
 }
 
 extern "C" {
@@ -399,20 +469,44 @@ int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
     return fail(SMLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   const bool atomic = (flags & SMLA_DKV_ATOMIC) != 0;
   const bool stored_p = (flags & SMLA_DKV_STORED_P) != 0;
+  const int64_t s_tok = s_q;
+  const Stage sg = make_stage(s_q, heads, kv_groups, topk);
   const KernelShape k = kernel_shape(s_q, s_kv, heads, kv_groups);
   s_q = k.s_q;
   s_kv = k.s_kv;
   heads = k.heads;
   const Plan p = make_plan(s_q, s_kv, heads, topk, true, atomic, stored_p);
-  if (!workspace || workspace_bytes < p.bytes)
+  if (!workspace || workspace_bytes < p.bytes + sg.bytes)
     return fail(SMLA_ERR_WORKSPACE, "workspace smaller than smla_bwd_workspace_size(flags)");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(SMLA_ERR_ALIGN, "workspace must be 256-byte aligned");
   if ((st = check_device())) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
+  char* base = static_cast<char*>(workspace);
+  char* ws = base + sg.bytes;
+  void* dq_u = dq;   // the caller's dq (token-major)
+  if (sg.on) {   // group-major copies of q, out, dout, lse (and the indices, unless planned)
+    const int64_t qb = (int64_t)sg.hg * 576 * 2, ob = (int64_t)sg.hg * 512 * 2;
+    const struct { const void* src; size_t off; int64_t bytes; } cp[] = {
+        {q, sg.q, qb}, {out, sg.out, ob}, {dout, sg.dout, ob}, {lse, sg.lse, (int64_t)sg.hg * 4}};
+    for (const auto& c : cp)
+      if ((st = hip_status(launch_permute_pairs(c.src, base + c.off, s_tok, kv_groups, c.bytes, true, s),
+                           "permute")))
+        return st;
+    if (!(flags & SMLA_PLAN_READY) &&
+        (st = hip_status(launch_permute_pairs(indices, base + sg.idx, s_tok, kv_groups,
+                                              (int64_t)topk * 4, true, s), "permute")))
+      return st;
+    q = base + sg.q;
+    out = base + sg.out;
+    dout = base + sg.dout;
+    lse = reinterpret_cast<const float*>(base + sg.lse);
+    indices = reinterpret_cast<const int32_t*>(base + sg.idx);
+    dq = base + sg.dq;
+  }
 
-  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups, ws, true);
+  const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups,
+                                sg.on ? s_tok : 0, ws, true);
   if (!(flags & SMLA_PLAN_READY) && (st = run_plan(p, pa, heads, true, s))) return st;
   int* gorder = reinterpret_cast<int*>(ws + p.off_gorder);
 
@@ -464,7 +558,12 @@ int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
                  }), "dkv_clear")))
     return st;
   if ((st = hip_status(timed("bwd_dkv", s, [&] { return launch_bwd_dkv(ba, heads, s); }), "bwd_dkv"))) return st;
-  return hip_status(timed("dkv_finalize", s, [&] { return launch_dkv_finalize(ba, heads, s); }), "dkv_finalize");
+  if ((st = hip_status(timed("dkv_finalize", s, [&] { return launch_dkv_finalize(ba, heads, s); }), "dkv_finalize")))
+    return st;
+  if (!sg.on) return SMLA_OK;
+  // dq back to token-major order
+  return hip_status(launch_permute_pairs(dq, dq_u, s_tok, kv_groups, (int64_t)sg.hg * 576 * 2, false, s),
+                    "permute");
 }
 
 int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,

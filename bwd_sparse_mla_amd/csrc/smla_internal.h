@@ -49,6 +49,9 @@ struct PlanArgs {
   // of the [s_kv_idx, kv_groups, 576] kv (s_kv = s_kv_idx * kv_groups rows)
   int kv_groups;
   int64_t s_kv_idx;
+  // group-major rows (0: token-major): index row r belongs to kv group
+  // r / gmajor_s instead of r % kv_groups
+  int64_t gmajor_s;
   int64_t G, NB, qcap, rcap;
   int* qcount;        // [G]   union entries (main + extra) per group
   int* xcount;        // [G]   extra entries (repeated slots) per group
@@ -133,6 +136,12 @@ struct TopkArgs {
   int32_t* out;          // [s_q, topk]
 };
 
+// Pair-block permutation between token-major order (block s G + g) and
+// group-major order (block g S + s) of S x G blocks of `block_bytes` bytes
+// (a multiple of 4; of 16 for the 16-byte path): to_gmajor copies token-major
+// src into group-major dst, else the reverse.
+hipError_t launch_permute_pairs(const void* src, void* dst, int64_t S, int G, int64_t block_bytes,
+                                bool to_gmajor, hipStream_t stream);
 hipError_t launch_fill_u32(void* ptr, size_t n_words, uint32_t value, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream);

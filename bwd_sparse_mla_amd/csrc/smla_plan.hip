@@ -64,10 +64,12 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   // Flat kv row of a valid value v in slot s of the group (KVG: the slot's
   // index row picks the kv group).
   auto flat_row = [&](int v, int s) __attribute__((always_inline)) {
-    if constexpr (KVG)
-      return v * kvg + (int)(((t0 + s / K) >> a.idx_shift) % kvg);
-    else
+    if constexpr (KVG) {
+      const int64_t r = (t0 + s / K) >> a.idx_shift;
+      return v * kvg + (int)(a.gmajor_s ? r / a.gmajor_s : r % kvg);
+    } else {
       return v;
+    }
   };
 
   if (tid == 0) {
@@ -339,6 +341,38 @@ hipError_t launch_plan(const PlanArgs& a, int heads, hipStream_t stream) {
     case 32: kvg ? plan_kernel<2, true><<<grid, block, 0, stream>>>(a) : plan_kernel<2, false><<<grid, block, 0, stream>>>(a); break;
     case 64: kvg ? plan_kernel<1, true><<<grid, block, 0, stream>>>(a) : plan_kernel<1, false><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void permute_pairs_kernel(const E* src, E* dst, int64_t S, int G,
+                                                            int64_t per, bool to_gmajor) {
+  const int64_t n = S * G * per;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t u = i / per, c = i - u * per;   // group-major block u = g S + s
+    const int64_t g = u / S, s = u - g * S;
+    const int64_t t = s * G + g;                  // token-major block
+    if (to_gmajor)
+      dst[u * per + c] = src[t * per + c];
+    else
+      dst[t * per + c] = src[u * per + c];
+  }
+}
+
+hipError_t launch_permute_pairs(const void* src, void* dst, int64_t S, int G, int64_t block_bytes,
+                                bool to_gmajor, hipStream_t stream) {
+  if (S == 0) return hipSuccess;
+  if (block_bytes % 16 == 0) {
+    const int64_t per = block_bytes / 16, n = S * G * per;
+    const int64_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+    permute_pairs_kernel<uint4_t><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+        static_cast<const uint4_t*>(src), static_cast<uint4_t*>(dst), S, G, per, to_gmajor);
+  } else {
+    const int64_t per = block_bytes / 4, n = S * G * per;
+    const int64_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+    permute_pairs_kernel<uint32_t><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+        static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), S, G, per, to_gmajor);
   }
   return hipGetLastError();
 }
