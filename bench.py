@@ -13,6 +13,8 @@ Prints ONE JSON line with the metric (useful TFLOP/s, i.e. 7680*H flops per
 valid (token, slot) pair over the fwd+bwd step time), the roofline of the
 dominant kernel (timed with HIP events on the library's stream) and the CPU
 baseline (the fp64 oracle on a bounded token sample, on the host cores).
+Outside the timed step it also reports the index-production top-k, the
+finite check of dq / dkv and the forward over fp8 kv records.
 """
 from __future__ import annotations
 
