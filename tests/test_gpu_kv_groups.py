@@ -3,8 +3,10 @@ head block g of H / G heads attends over kv group g): forward against the
 grouped oracle; backward (deterministic, stored-P, atomic dkv) against the
 grouped oracle given the GPU's out / lse; rows of a group no slot selects stay
 exact zeros in dkv; empty index rows give zero out and dq; the plan built once
-gives the one-shot results bit for bit.  Cases cover 8 to 128 heads per group,
-padding anywhere, empty rows, repeated and out-of-range indices."""
+gives the one-shot results bit for bit.  Cases cover 8 to 128 heads per group
+(below 64 the calls stage group-major copies in the workspace), padding
+anywhere, empty rows, repeated and out-of-range indices, index rows that are
+not a multiple of 16 bytes."""
 import numpy as np
 import pytest
 
@@ -21,6 +23,8 @@ CASES = {
     "h64_g8_oob": dict(S=25, H=64, G=8, K=64, S_kv=90, seed=43, pad_frac=0.2, oob_frac=0.05),
     "h256_g2": dict(S=9, H=256, G=2, K=100, S_kv=200, seed=44, pad_frac=0.25, empty_frac=0.1),
     "h128_g2_multiblock": dict(S=30, H=128, G=2, K=400, S_kv=1200, seed=45, pad_frac=0.1),
+    # index rows of 600 bytes: the group-major staging copies them in 4-byte words
+    "h32_g2_k150": dict(S=23, H=32, G=2, K=150, S_kv=400, seed=46, pad_frac=0.2, empty_frac=0.1),
 }
 
 
