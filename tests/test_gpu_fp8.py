@@ -106,10 +106,11 @@ def test_fp8_forward_against_the_oracle(case):
         np.testing.assert_allclose(g_lse[empty], EMPTY_ROW_LSE, rtol=1e-6)
 
 
-def test_fp8_forward_with_kv_groups_and_the_plan_built_once():
+@pytest.mark.parametrize("H", [256, 16])   # 128 heads per group; 8 (group-major staging)
+def test_fp8_forward_with_kv_groups_and_the_plan_built_once(H):
     import bwd_sparse_mla_amd as smla
-    w = synth.custom_grouped(S=9, H=256, G=2, K=100, S_kv=200, seed=56, pad_frac=0.25,
-                             empty_frac=0.1)
+    w = synth.custom_grouped(S=9 if H == 256 else 40, H=H, G=2, K=100, S_kv=200, seed=56,
+                             pad_frac=0.25, empty_frac=0.1)
     rec = synth.quantize_kv_fp8(w.kv, pow2_scales=False)            # [S_kv, G, 656]
     print(f"[fp8] kv groups S={w.S} H={w.H} G={w.G} K={w.K}", flush=True)
     q = to_torch_bf16(w.q)
