@@ -154,9 +154,12 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 
     // Union entries, ascending row order.  Thread tid owns bytes tid + 256k
     // (k = 0..7) of the window's bitmap, so a contiguous union spreads over
-    // many threads; each round k is one block-wide scan in row order.
+    // many threads; each round k is one block-wide scan in row order.  Rounds
+    // past the span's last row (2048 rows each) hold no set bit and are
+    // skipped.
+    const int rounds = min(WIN_WORDS * 4 / 256, ((hi - w0) >> 11) + 1);
 #pragma unroll 1
-    for (int k = 0; k < WIN_WORDS * 4 / 256; ++k) {
+    for (int k = 0; k < rounds; ++k) {
       const int byte = tid + 256 * k;
       const int w = byte >> 2, sh = 8 * (byte & 3);
       unsigned tb[T], u = 0;
