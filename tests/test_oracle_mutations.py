@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 from tests.test_oracle_pins import (causal_full_idx, dense_causal_torch,
-                                    gather_autograd_torch, rand_inputs)
+                                    gather_autograd_torch, rand_inputs,
+                                    supplied_lse_shift_ok, supplied_out_perturbation_ok)
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "oracle", "smla_oracle.py")
@@ -32,6 +33,13 @@ MUTATIONS = {
     "dp_uses_keys_tail_shift": ("dp = dout_s @ rows[:, :d_v].T",
                                 "dp = dout_s @ rows[:, -d_v:].T"),
     "duplicates_collapsed": ("np.add.at(dkv, J, contrib)", "dkv[J] += contrib"),
+    # the supplied-out / lse branch (the backward call takes the forward's
+    # saved out and lse)
+    "supplied_lse_ignored": ("p = np.exp(z - lse[s][:, None])",
+                             "p = token_forward(q[s], R, sm_scale, d_v)[2]"),
+    "supplied_out_ignored": ("o = out[s]", "o = token_forward(q[s], R, sm_scale, d_v)[0]"),
+    "supplied_lse_base2": ("p = np.exp(z - lse[s][:, None])",
+                           "p = np.exp2(z - lse[s][:, None])"),
 }
 
 
@@ -75,6 +83,12 @@ def pins_pass(mod) -> bool:
         return False
     r_out, r_lse, r_dq, r_dkv = gather_autograd_torch(q, kv, dout, idx, 0.7, DV)
     ne = ~np.isnan(r_lse)
+    # the supplied-out / lse branch away from its fixed point
+    try:
+        if not (supplied_lse_shift_ok(mod) and supplied_out_perturbation_ok(mod)):
+            return False
+    except Exception:
+        return False
     return (np.allclose(out, r_out, rtol=1e-10, atol=1e-11)
             and np.allclose(lse[ne], r_lse[ne], rtol=1e-10, atol=1e-11)
             and np.allclose(dq, r_dq, rtol=1e-10, atol=1e-11)

@@ -386,6 +386,68 @@ def test_supplied_out_lse_mode_equals_recompute():
         np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-13)
 
 
+# The supplied-out / lse branch away from its fixed point.  The backward call
+# on the pages takes the forward's saved out and lse (slime issue #2201,
+# Strongest repro evidence); with them given, p = exp(z - lse) reads the given
+# lse and delta = <dout, out> the given out, so:
+#   * lse + c multiplies p, dS, dq and every dkv contribution by exp(-c)
+#     (delta does not move);
+#   * out + E changes delta by <dout, E> only: dq[s,h] moves by
+#     -scale <dout[s,h], E[s,h]> sum_k p_k kv[J_k] and each dkv[J_k] by
+#     -scale p_k <dout[s,h], E[s,h]> q[s,h], with p the softmax of the
+#     token's scores (torch's softmax here, not the oracle's).
+
+def supplied_lse_shift_ok(mod, seed=23) -> bool:
+    q, kv, dout, idx, scale, DV = _small_case(seed)
+    out, lse = mod.sparse_mla_fwd(q, kv, idx, scale, d_v=DV)
+    rng = np.random.default_rng(seed + 1)
+    out = out + 0.3 * rng.standard_normal(out.shape)     # off the fixed point
+    base = mod.sparse_mla_bwd(q, kv, dout, idx, scale, d_v=DV, out=out, lse=lse)
+    c = 0.7                                              # one shift: dkv scales too
+    shifted = mod.sparse_mla_bwd(q, kv, dout, idx, scale, d_v=DV, out=out, lse=lse + c)
+    ok = all(np.allclose(y, math.exp(-c) * x, rtol=1e-12, atol=1e-14)
+             for x, y in zip(base, shifted))
+    cr = rng.uniform(-2.0, 2.0, size=lse.shape)          # per (token, head): dq row-wise
+    dq_r, _ = mod.sparse_mla_bwd(q, kv, dout, idx, scale, d_v=DV, out=out, lse=lse + cr)
+    ok = ok and np.allclose(dq_r, np.exp(-cr)[:, :, None] * base[0], rtol=1e-12, atol=1e-14)
+    return bool(ok) and float(np.abs(base[0]).max()) > 0.0
+
+
+def supplied_out_perturbation_ok(mod, seed=24) -> bool:
+    q, kv, dout, idx, scale, DV = _small_case(seed)
+    out, lse = mod.sparse_mla_fwd(q, kv, idx, scale, d_v=DV)
+    rng = np.random.default_rng(seed + 1)
+    E = rng.standard_normal(out.shape)
+    dq0, dkv0 = mod.sparse_mla_bwd(q, kv, dout, idx, scale, d_v=DV, out=out, lse=lse)
+    dq1, dkv1 = mod.sparse_mla_bwd(q, kv, dout, idx, scale, d_v=DV, out=out + E, lse=lse)
+    S, H, DK = q.shape
+    exp_dq = np.zeros_like(dq0)
+    exp_dkv = torch.zeros((kv.shape[0], DK), dtype=torch.float64)
+    for s in range(S):
+        J = idx[s][idx[s] != -1]
+        if J.size == 0:
+            continue
+        rows = torch.tensor(kv[J])
+        qs = torch.tensor(q[s])
+        p = torch.softmax(scale * qs @ rows.T, dim=-1)               # [H, n]
+        d = torch.tensor((dout[s] * E[s]).sum(axis=1))               # <dout, E> per head
+        exp_dq[s] = (-scale * d[:, None] * (p @ rows)).numpy()
+        exp_dkv.index_add_(0, torch.tensor(J), -scale * (p * d[:, None]).T @ qs)
+    return bool(np.allclose(dq1 - dq0, exp_dq, rtol=1e-9, atol=1e-12)
+                and np.allclose(dkv1 - dkv0, exp_dkv.numpy(), rtol=1e-9, atol=1e-12)
+                and float(np.abs(exp_dq).max()) > 0.0)
+
+
+def test_supplied_lse_shift_scales_gradients():
+    import oracle.smla_oracle as mod
+    assert supplied_lse_shift_ok(mod)
+
+
+def test_supplied_out_changes_delta_only():
+    import oracle.smla_oracle as mod
+    assert supplied_out_perturbation_ok(mod)
+
+
 def test_sampled_tokens_and_rows_match_full():
     q, kv, dout, idx, scale, DV = _small_case()
     out, lse = sparse_mla_fwd(q, kv, idx, scale, d_v=DV)
