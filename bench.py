@@ -67,6 +67,8 @@ def parse():
                     help="time the steps without per-kernel HIP events")
     ap.add_argument("--no-topk", action="store_true",
                     help="skip the index-production (top-k) measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads reported beside the headline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (three times) and "
                          "exit: the calibration run for the HBM byte counters")
@@ -221,16 +223,40 @@ def fp8_fwd_measure(run, w, q, kv, idx, steps: int):
             "useful_tflops": round(flops / (ms8 * 1e-3) / 1e12, 1)}
 
 
+def host_info():
+    """Host cores this process may run on, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def cpu_threads() -> int:
+    """Threads for the oracle's BLAS pool: every core the process may run on,
+    capped by OMP_NUM_THREADS when the environment sets a CPU share."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
 def cpu_baseline(w, target_s: float):
     """The fp64 oracle as it stands, on a seeded sample of tokens of the same
-    workload (their forward + backward, dkv scattered into the full kv)."""
+    workload (their forward + backward, dkv scattered into the full kv), with
+    its BLAS pool on cpu_threads() threads."""
     import threadpoolctl
 
     from oracle import sparse_mla_bwd, sparse_mla_fwd
     from workloads import synth
 
-    info = threadpoolctl.threadpool_info()
-    threads = max([d.get("num_threads", 1) for d in info] or [1])
+    threads = cpu_threads()
     kv = synth.bf16_bits_to_f64(w.kv)
     rng = np.random.default_rng(1234)
     order = rng.permutation(w.S)
@@ -247,16 +273,161 @@ def cpu_baseline(w, target_s: float):
         nv = int(np.count_nonzero((ix >= 0) & (ix < w.S_kv)))
         return dt, nv, len(toks)
 
-    dt0, nv0, n0 = run(order[:64])
-    per_pair = dt0 / max(nv0, 1)
-    nv_mean = w.n_valid / w.S
-    n = int(min(w.S, max(64, target_s / max(per_pair * nv_mean, 1e-9))))
-    dt, nv, n = run(order[:n])
+    with threadpoolctl.threadpool_limits(limits=threads):
+        dt0, nv0, n0 = run(order[:64])
+        per_pair = dt0 / max(nv0, 1)
+        nv_mean = w.n_valid / w.S
+        n = int(min(w.S, max(64, target_s / max(per_pair * nv_mean, 1e-9))))
+        dt, nv, n = run(order[:n])
     flops = USEFUL_PER_PAIR_HEAD * w.H * nv
+    host = host_info()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n} of {w.S} tokens (seeded), {nv} valid pairs, fwd+bwd fp64, "
-                      f"{dt:.1f} s wall"}
+                      f"{dt:.1f} s wall",
+            "affinity_cores": host["affinity_cores"], "cpu_model": host["cpu_model"]}
+
+
+def gpu_tensors(w, dev):
+    import torch
+    to_bf16 = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    return (to_bf16(w.q), to_bf16(w.kv), to_bf16(w.dout),
+            torch.from_numpy(np.ascontiguousarray(w.idx)).to(dev))
+
+
+class Case:
+    """One workload on the preallocated runner: the step and its timings."""
+
+    def __init__(self, w, dev, atomic: bool, stored: bool):
+        import bwd_sparse_mla_amd as smla
+        self.w = w
+        self.q, self.kv, self.dout, self.idx = gpu_tensors(w, dev)
+        self.run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, dev, dkv_atomic=atomic,
+                                        dkv_stored_p=stored)
+        self.run._check(self.q, self.kv, self.idx, self.dout)
+        self.stored = stored
+
+    def fwd(self):
+        # the index plan (once: forward and backward take the same indices), then the forward
+        self.run.plan(self.idx)
+        self.run.fwd(self.q, self.kv, self.idx, self.w.sm_scale, planned=True)
+
+    def bwd(self):
+        self.run.bwd(self.q, self.kv, self.dout, self.idx, self.w.sm_scale, planned=True)
+
+    def step(self):
+        # one step of the path: plan, forward, backward
+        self.fwd()
+        self.bwd()
+
+    def timed_mean(self, steps: int, warmup: int):
+        """Mean ms per step over `steps` steps between two events on the
+        library's stream (torch's current stream), after `warmup` steps."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            self.step()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+
+    def per_step(self, n: int, cold: bool = False):
+        """Per-step event timings (plan + forward, backward, total) of n
+        steps, ms each; cold: a 1 GiB buffer is written before every step
+        (outside the events), so the L2 and MALL start without the inputs."""
+        import torch
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=self.q.device) if cold else None
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        for i in range(n):
+            if cold:
+                flush.fill_(float(i))
+            ev[i][0].record()
+            self.fwd()
+            ev[i][1].record()
+            self.bwd()
+            ev[i][2].record()
+        torch.cuda.synchronize()
+        f = [e[0].elapsed_time(e[1]) for e in ev]
+        b = [e[1].elapsed_time(e[2]) for e in ev]
+        t = [e[0].elapsed_time(e[2]) for e in ev]
+        med = lambda x: float(np.median(x))
+        return {"fwd_ms": round(med(f), 5), "bwd_ms": round(med(b), 5),
+                "fwd_bwd_ms": round(med(t), 5), "samples": n}
+
+    def kernel_ms(self, steps: int):
+        """Per-kernel mean durations: `steps` more steps with the library
+        bracketing each of its launches by HIP events on its stream."""
+        import torch
+
+        import bwd_sparse_mla_amd as smla
+        smla.timing_start(32 * steps)
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        smla.timing_stop()
+        kernels = {}
+        for name in ("plan", "order", "fwd", "bwd_dq", "dkv_schedule", "dkv_clear", "bwd_dkv",
+                     "dkv_finalize"):
+            n, tot = smla.timing_read(name)
+            if n:
+                kernels[name] = {"launches": n, "avg_ms": tot / n}
+        return kernels
+
+    def check_finite(self):
+        import torch
+        for name, t in (("out", self.run.out), ("lse", self.run.lse), ("dq", self.run.dq),
+                        ("dkv", self.run.dkv)):
+            bad = int((~torch.isfinite(t.float())).sum())
+            if bad:
+                raise RuntimeError(f"{self.w.name}: {bad} nonfinite values in {name}")
+
+
+def useful_flops(w) -> int:
+    return USEFUL_PER_PAIR_HEAD * w.H * w.n_valid
+
+
+def gather_block(w, ms: float):
+    """Effective gather rate: the algorithmic kv-row gathers of one forward and
+    one backward (1152 bytes per valid pair each) over the step time, against
+    HBM peak; it can exceed 1 because the L2 / MALL serve repeated rows."""
+    nbytes = 2 * 1152 * w.n_valid
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bytes_per_step": nbytes, "GBs": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 3)}
+
+
+# Other configurations of the same path, reported beside the headline: the
+# tiny correctness case, the padding-stress batch, one GPU's share at the
+# production shape (recency-biased picks) and the long context in both dkv
+# modes.  (name, dkv atomic, timed steps, warm-up steps)
+CONFIGS = [("tiny", False, 20, 3), ("padding_stress", False, 20, 3), ("recency", False, 5, 2),
+           ("long_context", False, 3, 1), ("long_context", True, 3, 1)]
+
+
+def config_line(w, dev, atomic: bool, stored: bool, steps: int, warmup: int):
+    import torch
+    case = Case(w, dev, atomic, stored)
+    ms, _ = case.timed_mean(steps, warmup)
+    case.check_finite()
+    parts = case.per_step(max(3, steps))
+    kernels = case.kernel_ms(steps)
+    useful = useful_flops(w)
+    value = useful / (ms * 1e-3) / 1e12
+    rec = {"workload": w.name, "S": w.S, "H": w.H, "topk": w.K, "valid_pairs": w.n_valid,
+           "dkv_mode": "atomic" if atomic else "deterministic", "steps": steps,
+           "ms_per_step": round(ms, 5), "median": parts, "useful_tflops": round(value, 2),
+           "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+           "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kernels.items()},
+           "effective_gather": gather_block(w, ms)}
+    del case
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
@@ -273,77 +444,43 @@ def main():
 
     import torch
 
-    import bwd_sparse_mla_amd as smla
     from workloads import synth
 
     w = synth.WORKLOADS[args.workload]()
     print(f"[bench] workload {w.name}: S={w.S} H={w.H} K={w.K} S_kv={w.S_kv} "
           f"valid pairs={w.n_valid}", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
-    to_bf16 = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(
-        torch.bfloat16).to(dev)
-    q, kv, dout = to_bf16(w.q), to_bf16(w.kv), to_bf16(w.dout)
-    idx = torch.from_numpy(np.ascontiguousarray(w.idx)).to(dev)
-    run = smla.SparseMLARunner(w.S, w.S_kv, w.H, w.K, dev, dkv_atomic=args.dkv_mode == "atomic",
-                               dkv_stored_p=args.dkv_scores == "stored")
-    run._check(q, kv, idx, dout)
+    stored = args.dkv_scores == "stored"
+    case = Case(w, dev, args.dkv_mode == "atomic", stored)
+    run, q, kv, idx = case.run, case.q, case.kv, case.idx
 
-    def step():
-        # one step of the path: the index plan (once: forward and backward
-        # take the same indices), the forward, the backward
-        run.plan(idx)
-        run.fwd(q, kv, idx, w.sm_scale, planned=True)
-        run.bwd(q, kv, dout, idx, w.sm_scale, planned=True)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
     # The timed region: K steps between two events on the library's stream
     # (torch's current stream), no other work inside.
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, wall = case.timed_mean(args.steps, args.warmup)
     print(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)",
           file=sys.stderr, flush=True)
-    for name, t in (("out", run.out), ("lse", run.lse), ("dq", run.dq), ("dkv", run.dkv)):
-        bad = int((~torch.isfinite(t.float())).sum())
-        if bad:
-            raise RuntimeError(f"{bad} nonfinite values in {name}")
+    case.check_finite()
+    # Medians of per-step event timings, warm and with the caches flushed.
+    warm = case.per_step(args.steps)
+    cold = case.per_step(max(5, min(args.steps, 20)), cold=True)
+    print(f"[bench] median warm {warm} cold {cold}", file=sys.stderr, flush=True)
     # Per-kernel durations: the same K steps again, with the library
     # bracketing each of its launch steps by HIP events on that stream (the
     # event records add a few microseconds per launch, so this pass is not the
     # one the headline number comes from).
     timing = not args.no_kernel_timing
-    if timing:
-        smla.timing_start(32 * args.steps)
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        smla.timing_stop()
+    kernels = case.kernel_ms(args.steps) if timing else {}
 
     nv = w.n_valid
-    useful = USEFUL_PER_PAIR_HEAD * w.H * nv
+    useful = useful_flops(w)
     value = useful / (ms * 1e-3) / 1e12
 
-    kernels = {}
     roofline = None
     if timing:
-        for name in ("plan", "order", "fwd", "bwd_dq", "dkv_schedule", "dkv_clear", "bwd_dkv",
-                     "dkv_finalize"):
-            n, tot = smla.timing_read(name)
-            if n:
-                kernels[name] = {"launches": n, "avg_ms": tot / n}
         dom = max((k for k in kernels if k in FLOPS_PER_PAIR_HEAD),
                   key=lambda k: kernels[k]["avg_ms"])
         per_pair = FLOPS_PER_PAIR_HEAD[dom]
-        if dom == "bwd_dkv" and args.dkv_scores == "stored":
+        if dom == "bwd_dkv" and stored:
             per_pair = FLOPS_STORED_DKV   # P and dS come from the dq pass
         flops = per_pair * w.H * nv
         ach = flops / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
@@ -368,6 +505,20 @@ def main():
     if not args.no_topk:
         print("[bench] index production (top-k) ...", file=sys.stderr, flush=True)
         topk = topk_measure(max(5, args.steps // 2))
+    del case, run, q, kv, idx
+    torch.cuda.empty_cache()
+
+    configs = None
+    if not args.no_configs:
+        configs = []
+        for name, atomic, steps, warmup in CONFIGS:
+            if name == args.workload and not atomic:
+                continue
+            wc = synth.WORKLOADS[name]()
+            print(f"[bench] config {wc.name} dkv {'atomic' if atomic else 'deterministic'} "
+                  f"({steps} steps) ...", file=sys.stderr, flush=True)
+            configs.append(config_line(wc, dev, atomic, stored, steps, warmup))
+            del wc
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -392,11 +543,15 @@ def main():
                    "parallelism": "none (one GPU)", "dkv_mode": args.dkv_mode,
                    "dkv_scores": args.dkv_scores},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+        "median": {"warm": warm, "cold_caches": cold},
         "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kernels.items()},
         "kernel_timing": ("per-launch HIP events on the library's stream, in a second pass of "
                           "the same steps after the timed region" if timing else None),
         "roofline": roofline,
+        "effective_gather": gather_block(w, ms),
         "cpu_baseline": cpu,
+        "host": host_info(),
+        "configs": configs,
         "index_topk": topk,
         "nonfinite_check": finite,
         "fwd_fp8_kv": fp8,

@@ -376,7 +376,7 @@ __device__ __forceinline__ void gather_kv_rows_nw(char* tile, const uint16_t* kv
       const int r = PER * wv + i;
       const int row = __builtin_amdgcn_readlane(vrow, i);
       const bool ok = r < count && (uint32_t)row < (uint32_t)s_kv;
-      const uint16_t* src = (ok ? kv : g_zero_row) + (uint32_t)(ok ? row : 0) * (uint32_t)D_K;
+      const uint16_t* src = (ok ? kv : g_zero_row) + (uint64_t)(uint32_t)(ok ? row : 0) * D_K;
       g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), base + 1024u * (uint32_t)r);
     }
   }
@@ -455,7 +455,7 @@ __device__ __forceinline__ void kv_gather_copy(const KvGather<R>& g, int wv, int
     const int r = PER * wv + J;
     const int row = __builtin_amdgcn_readlane(g.vrow, J);
     const bool ok = r < g.count && (uint32_t)row < g.s_kv;
-    const uint16_t* src = (ok ? g.kv : g.zero) + (uint32_t)(ok ? row : 0) * (uint32_t)D_K;
+    const uint16_t* src = (ok ? g.kv : g.zero) + (uint64_t)(uint32_t)(ok ? row : 0) * D_K;
     g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), g.base + 1024u * (uint32_t)r);
   } else if constexpr (J < PER + R / 32) {
     constexpr int j = J - PER;

@@ -68,12 +68,38 @@ def _grouped_idx(idx: torch.Tensor, groups: int) -> torch.Tensor:
     return idx
 
 
-def _prep(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+# Device type the kernels run on (a test on a machine without a GPU may point
+# it at "cpu" together with a stand-in library to reach the checks below).
+_DEVICE_TYPE = "cuda"
+
+
+def _on_device(t: torch.Tensor, device: torch.device | None) -> bool:
+    return t.device.type == _DEVICE_TYPE and (device is None or t.device == device)
+
+
+def _prep(t: torch.Tensor, dtype: torch.dtype, name: str,
+          device: torch.device | None = None) -> torch.Tensor:
+    if not _on_device(t, device):
+        raise ValueError(f"{name} must be a GPU tensor" + (f" on {device}" if device else ""))
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     return t.contiguous()
+
+
+def _dest(t: torch.Tensor, dtype: torch.dtype, numel: int, device: torch.device,
+          name: str) -> torch.Tensor:
+    """A buffer the caller hands in for the kernels to write: it must be
+    exactly what they write (device, dtype, element count, contiguous), or
+    the kernels would write outside it; checked before any launch."""
+    if not isinstance(t, torch.Tensor) or not _on_device(t, device):
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    return t
 
 
 def _workspace(nbytes: int, device) -> tuple[torch.Tensor, int]:
@@ -109,11 +135,11 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_
     lead = q.shape[:-1]
     q3 = _prep(_flat_q(q), torch.bfloat16, "q")
     kv3, G = _grouped_kv(kv)
-    kv3 = _prep(kv3, torch.bfloat16, "kv")
+    kv3 = _prep(kv3, torch.bfloat16, "kv", q3.device)
     ix = _grouped_idx(indices, G)
     if ix.dtype != torch.int32:
         ix = ix.to(torch.int32)
-    ix = _prep(ix, torch.int32, "indices")
+    ix = _prep(ix, torch.int32, "indices", q3.device)
     S, H, _ = q3.shape
     if ix.shape[0] != S:
         raise ValueError("indices must have one row per query token")
@@ -122,8 +148,12 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_
     dev = q3.device
     if out is None:
         out = torch.empty(*lead[:-1], H, D_V, dtype=torch.bfloat16, device=dev)
+    else:
+        _dest(out, torch.bfloat16, S * H * D_V, dev, "out")
     if lse is None:
         lse = torch.empty(*lead[:-1], H, dtype=torch.float32, device=dev)
+    else:
+        _dest(lse, torch.float32, S * H, dev, "lse")
     ws, ws_addr = _workspace(fwd_workspace_bytes(S, S_kv, H, K, G), dev)
     _lib.check(lib.smla_fwd_g(_ptr(q3), _ptr(kv3), _ptr(ix), S, S_kv, H, G, K, float(sm_scale),
                               _ptr(out), _ptr(lse), 0, ctypes.c_void_p(ws_addr),
@@ -151,12 +181,12 @@ def sparse_mla_fwd_fp8(q: torch.Tensor, kv_fp8: torch.Tensor, indices: torch.Ten
         k8 = k8.unsqueeze(1)
     if k8.dim() != 3 or k8.shape[-1] != FP8_REC_BYTES:
         raise ValueError(f"kv_fp8 must be [S_kv, {FP8_REC_BYTES}] or [S_kv, G, {FP8_REC_BYTES}]")
-    k8 = _prep(k8, torch.uint8, "kv_fp8")
+    k8 = _prep(k8, torch.uint8, "kv_fp8", q3.device)
     G = k8.shape[1]
     ix = _grouped_idx(indices, G)
     if ix.dtype != torch.int32:
         ix = ix.to(torch.int32)
-    ix = _prep(ix, torch.int32, "indices")
+    ix = _prep(ix, torch.int32, "indices", q3.device)
     S, H, _ = q3.shape
     if ix.shape[0] != S:
         raise ValueError("indices must have one row per query token")
@@ -165,8 +195,12 @@ def sparse_mla_fwd_fp8(q: torch.Tensor, kv_fp8: torch.Tensor, indices: torch.Ten
     dev = q3.device
     if out is None:
         out = torch.empty(*lead[:-1], H, D_V, dtype=torch.bfloat16, device=dev)
+    else:
+        _dest(out, torch.bfloat16, S * H * D_V, dev, "out")
     if lse is None:
         lse = torch.empty(*lead[:-1], H, dtype=torch.float32, device=dev)
+    else:
+        _dest(lse, torch.float32, S * H, dev, "lse")
     ws, ws_addr = _workspace(fwd_workspace_bytes(S, S_kv, H, K, G), dev)
     flags = _lib.SMLA_FP8_POW2_SCALES if pow2_scales else 0
     _lib.check(lib.smla_fwd_fp8(_ptr(q3), _ptr(k8), _ptr(ix), S, S_kv, H, G, K, float(sm_scale),
@@ -193,15 +227,18 @@ def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, out: torch.Tensor, dout: t
     lib = _lib.load()
     q3 = _prep(_flat_q(q), torch.bfloat16, "q")
     kv3, G = _grouped_kv(kv)
-    kv3 = _prep(kv3, torch.bfloat16, "kv")
+    kv3 = _prep(kv3, torch.bfloat16, "kv", q3.device)
     S, H, _ = q3.shape
-    o3 = _prep(out.reshape(S, H, D_V), torch.bfloat16, "out")
-    do3 = _prep(dout.reshape(S, H, D_V), torch.bfloat16, "dout")
-    ls = _prep(lse.reshape(S, H), torch.float32, "lse")
+    for name, t, n in (("out", out, S * H * D_V), ("dout", dout, S * H * D_V), ("lse", lse, S * H)):
+        if t.numel() != n:
+            raise ValueError(f"{name} must hold {n} elements, got {t.numel()}")
+    o3 = _prep(out.reshape(S, H, D_V), torch.bfloat16, "out", q3.device)
+    do3 = _prep(dout.reshape(S, H, D_V), torch.bfloat16, "dout", q3.device)
+    ls = _prep(lse.reshape(S, H), torch.float32, "lse", q3.device)
     ix = _grouped_idx(indices, G)
     if ix.dtype != torch.int32:
         ix = ix.to(torch.int32)
-    ix = _prep(ix, torch.int32, "indices")
+    ix = _prep(ix, torch.int32, "indices", q3.device)
     if ix.shape[0] != S:
         raise ValueError("indices must have one row per query token")
     K = ix.shape[2]
@@ -213,9 +250,7 @@ def sparse_mla_bwd(q: torch.Tensor, kv: torch.Tensor, out: torch.Tensor, dout: t
             raise ValueError("accumulate=True needs dkv_f32")
         flags |= _lib.SMLA_DKV_ACCUMULATE
     if dkv_f32 is not None:
-        if dkv_f32.dtype != torch.float32 or not dkv_f32.is_contiguous() \
-                or dkv_f32.numel() != S_kv * G * D_K:
-            raise ValueError("dkv_f32 must be a contiguous fp32 tensor of S_kv*G*576 elements")
+        _dest(dkv_f32, torch.float32, S_kv * G * D_K, dev, "dkv_f32")
     dq = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     dkv = torch.empty(kv.shape, dtype=torch.bfloat16, device=dev) if want_bf16_dkv else None
     ws, ws_addr = _workspace(bwd_workspace_bytes(S, S_kv, H, K, flags, G), dev)
@@ -246,15 +281,18 @@ def topk_indices(logits: torch.Tensor, ks: torch.Tensor, ke: torch.Tensor, topk:
     fp32 indexer logits [S, S_kv] inside its range [ks, ke), k capped at the
     range length, ascending, padded with -1 (the layout sparse_mla_fwd takes)."""
     lib = _lib.load()
-    if logits.dim() != 2 or logits.dtype != torch.float32 or logits.stride(1) != 1:
-        raise ValueError("logits must be fp32 [S, S_kv] with contiguous rows")
+    if (not _on_device(logits, None) or logits.dim() != 2 or logits.dtype != torch.float32
+            or logits.stride(1) != 1):
+        raise ValueError("logits must be an fp32 GPU tensor [S, S_kv] with contiguous rows")
     S, S_kv = logits.shape
-    ks = _prep(ks.to(torch.int32), torch.int32, "ks")
-    ke = _prep(ke.to(torch.int32), torch.int32, "ke")
+    ks = _prep(ks.to(torch.int32), torch.int32, "ks", logits.device)
+    ke = _prep(ke.to(torch.int32), torch.int32, "ke", logits.device)
     if ks.shape != (S,) or ke.shape != (S,):
         raise ValueError("ks and ke must be [S]")
     if out is None:
         out = torch.empty(S, topk, dtype=torch.int32, device=logits.device)
+    else:
+        _dest(out, torch.int32, S * topk, logits.device, "out")
     _lib.check(lib.smla_topk_indices(_ptr(logits), S, S_kv, logits.stride(0), _ptr(ks), _ptr(ke),
                                      topk, _ptr(out), _stream(logits.device)))
     return out

@@ -19,7 +19,7 @@ def test_bench_prints_one_json_line(scores):
         pytest.skip("no GPU")
     print(f"[bench] contract, dkv scores {scores}", flush=True)
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny",
-                          "--steps", "3", "--warmup", "1", "--cpu-seconds", "0.5", "--no-topk",
+                          "--steps", "3", "--warmup", "1", "--cpu-seconds", "0.5", "--no-topk", "--no-configs",
                           "--dkv-scores", scores],
                          capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert res.returncode == 0, res.stderr[-2000:]
@@ -28,7 +28,8 @@ def test_bench_prints_one_json_line(scores):
     d = json.loads(lines[0])
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
-                "roofline", "cpu_baseline", "nonfinite_check"):
+                "roofline", "cpu_baseline", "nonfinite_check", "median", "host",
+                "effective_gather"):
         assert key in d, key
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["value"] > 0 and d["ms_per_step"] > 0
     assert d["config"]["dkv_scores"] == scores
@@ -37,4 +38,8 @@ def test_bench_prints_one_json_line(scores):
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1
+    assert 1 <= c["cores"] <= c["affinity_cores"]
+    for part in ("warm", "cold_caches"):
+        m = d["median"][part]
+        assert 0 < m["fwd_ms"] < m["fwd_bwd_ms"] and 0 < m["bwd_ms"] < m["fwd_bwd_ms"]
 

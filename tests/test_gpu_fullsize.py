@@ -2,9 +2,11 @@
 configuration bench.py times (SparseMLARunner: every buffer preallocated, the
 index plan built once, one forward and one backward call on it).
 
-The oracle cannot run on whole tensors of this size in a test, so it checks
-sampled outputs it computes one by one, and the rest is held to properties
-that hold at any size:
+At the two H = 8 workloads (packed ragged batch, padding stress) the oracle
+covers every token in seconds, so out, lse, dq and dkv are compared over
+whole tensors.  At the larger ones (recency, long context, 128 heads) the
+oracle checks sampled outputs it computes one by one, and the rest is held to
+properties that hold at any size:
 
   * out / lse / dq of sampled tokens (first and last token of every sequence,
     empty rows, random tokens) against the oracle's forward and its backward
@@ -140,3 +142,44 @@ def test_full_size_sampled_parity(name, atomic, stored):
     assert not bits[~touched].any(), "dkv written on a row no slot selects"
     nonzero_rows = bits.any(axis=1)
     assert nonzero_rows.sum() == touched.sum(), "a selected kv row got no gradient"
+
+
+@pytest.mark.parametrize("name", ["packed_ragged", "padding_stress"])
+def test_full_size_whole_tensor_parity(name):
+    """Element-by-element parity over whole tensors at the two H = 8 workloads
+    (the oracle covers all 4096 tokens in seconds): out, lse against its
+    forward; dq, dkv of both backward forms against its backward given the
+    GPU's out / lse; the end-to-end error (gradient recomputed from scratch)
+    is printed, and gated at unit variance."""
+    import torch
+
+    w = synth.WORKLOADS[name]()
+    print(f"[fullsize-whole] {w.name} S={w.S} H={w.H} K={w.K} valid={w.n_valid}", flush=True)
+    runs = {stored: _run(w, stored=stored) for stored in (False, True)}
+    base = runs[True]
+    assert torch.equal(runs[False].out, base.out) and torch.equal(runs[False].lse, base.lse)
+    kv64 = synth.bf16_bits_to_f64(w.kv)
+    q64 = synth.bf16_bits_to_f64(w.q)
+    do64 = synth.bf16_bits_to_f64(w.dout)
+    g_out = base.out.float().cpu().numpy().astype(np.float64)
+    g_lse = base.lse.cpu().numpy().astype(np.float64)
+    r_out, r_lse = o_fwd(q64, kv64, w.idx, w.sm_scale)
+    s_dq, s_dkv = o_bwd(q64, kv64, do64, w.idx, w.sm_scale, out=g_out, lse=g_lse)
+    e_dq, e_dkv = o_bwd(q64, kv64, do64, w.idx, w.sm_scale)
+    errs = {"out": rel_err(g_out, r_out), "lse": rel_err(g_lse, r_lse)}
+    assert np.isfinite(g_out).all() and np.isfinite(g_lse).all()
+    for stored, run in runs.items():
+        g_dq = run.dq.float().cpu().numpy().astype(np.float64)
+        g_dkv = run.dkv.float().cpu().numpy().astype(np.float64)
+        assert np.isfinite(g_dq).all() and np.isfinite(g_dkv).all()
+        tag = "stored" if stored else "recompute"
+        errs[f"dq_{tag}"] = rel_err(g_dq, s_dq)
+        errs[f"dkv_{tag}"] = rel_err(g_dkv, s_dkv)
+        e2e = {"dq": rel_err(g_dq, e_dq), "dkv": rel_err(g_dkv, e_dkv)}
+        print(f"[fullsize-whole] {w.name} {tag}: end-to-end {e2e}", flush=True)
+        if name == "packed_ragged":    # unit variance: the end-to-end gate holds too
+            for k, v in e2e.items():
+                assert v <= TOL, f"end-to-end {k} ({tag}) relative error {v:.3e}"
+    print(f"[fullsize-whole] {w.name} rel errors {errs}", flush=True)
+    for k, v in errs.items():
+        assert v <= TOL, f"{k} relative error {v:.3e} > {TOL} over the whole tensor"
