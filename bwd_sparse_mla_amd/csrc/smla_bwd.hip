@@ -868,7 +868,7 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // some index row repeats an entry -- the extra slots' contributions, each
 // computed directly in (group, slot) order.  Output semantics (bf16, fp32,
 // accumulate, rows no slot selects) are applied here.  Bitwise reproducible.
-constexpr int FIN_ROWS = 2;
+constexpr int FIN_ROWS = 4;
 constexpr int FIN_PARTS = TILE_KV / FIN_ROWS;   // workgroups per block
 template <int H>
 __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
@@ -940,22 +940,38 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
                              : a.part + ((w0 + unit) * unit_rows + TILE_KV * hb + FIN_ROWS * part) * D_K;
   const int nsrc = a.acc32 ? (nsplit > 0 ? 1 : 0) : nsplit;
   constexpr int N4 = FIN_ROWS * D_K / 4;  // float4 elements of the rows
+  constexpr int EPT = (N4 + 255) / 256;   // elements per thread
   const int64_t SPLIT = unit_rows * D_K;
-  for (int e = tid; e < N4; e += 256) {
-    // Partials summed left to right in workgroup order; loads go out eight
-    // at a time (indices clamped into range, extra ones unused).  A block no
-    // record touches has no partial: zeros.
-    const float* pe = src + 4 * e;
-    float4_t v = nsrc > 0 ? *reinterpret_cast<const float4_t*>(pe) : (float4_t){0.f, 0.f, 0.f, 0.f};
-    for (int sp = 1; sp < nsrc; sp += 8) {
-      float4_t pp[8];
+  // Partials summed left to right in workgroup order.  All of a thread's
+  // elements load their partials together, eight partials per round
+  // (indices clamped into range, extra loads unused).  A block no record
+  // touches has no partial: zeros.
+  float4_t vs[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = min(tid + 256 * k, N4 - 1);
+    vs[k] = nsrc > 0 ? *reinterpret_cast<const float4_t*>(src + 4 * e) : (float4_t){0.f, 0.f, 0.f, 0.f};
+  }
+  for (int sp = 1; sp < nsrc; sp += 8) {
+    float4_t pp[EPT][8];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const float* pe = src + 4 * min(tid + 256 * k, N4 - 1);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        pp[j] = *reinterpret_cast<const float4_t*>(pe + min(sp + j, nsrc - 1) * SPLIT);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (sp + j < nsrc) v += pp[j];
+        pp[k][j] = *reinterpret_cast<const float4_t*>(pe + min(sp + j, nsrc - 1) * SPLIT);
     }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (sp + j < nsrc) vs[k] += pp[k][j];
+  }
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid + 256 * k;
+    if (e >= N4) break;
+    float4_t v = vs[k];
     if (extras) v += *reinterpret_cast<const float4_t*>(sX + 4 * e);
     const int kvl = (4 * e) / D_K;
     const int col = (4 * e) % D_K;

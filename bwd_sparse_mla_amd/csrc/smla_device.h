@@ -198,6 +198,15 @@ __device__ __forceinline__ void static_for(F&& f) { static_for_from<0, N>(f); }
 
 // s_waitcnt vmcnt(0) (other counters untouched).
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations
+// (loads, stores and LDS copies alike; they complete in issue order) still
+// outstanding.  The 6-bit count sits in bits 3:0 and 15:14; expcnt (6:4) and
+// lgkmcnt (11:8) are left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Reductions across the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
 // with the gfx950 row-swap instructions (VALU, no LDS round trip).
@@ -418,54 +427,63 @@ __device__ __forceinline__ void gather_seq_rows_nw(char* tile, const uint16_t* f
   }
 }
 
-// Incremental form of the gathers: prepare once, then issue copy J (a
-// compile-time index) where it fits in the caller's instruction stream.
+// Incremental form of the gathers: prepare once per tile, then issue copy J
+// (a compile-time index) where it fits in the caller's instruction stream.
 // For a kv gather of R rows, wave wv issues R/4 row copies (J < R/4) and
 // R/32 tail copies (J = R/4 + j); a kv tile thus takes R/4 + R/32 copies per
-// wave (18 for R = 64, 9 for R = 32).  Row selection is branch-free: rows
-// past `count` and indices outside [0, s_kv) read the zero row.
+// wave (18 for R = 64, 9 for R = 32).  The preparation forms every source
+// address at once with vector instructions (lane i < R/4 holds the address of
+// the wave's row i; rows past `count` and indices outside [0, s_kv) get the
+// zero row), so a row copy is two lane reads, one XOR and the copy itself.
 template <int R>
 struct KvGather {
-  const uint16_t* kv;
-  const uint16_t* zero;
-  uint32_t base;      // LDS byte address of the tile
-  uint32_t s_kv;
-  int count;
-  int vrow;           // lane i < R/4: row index of tile row R/4 * wv + i
-  int vtail[R / 32];  // tail copy j: row index of tile row 8 (wv + 4j) + lane / 8
+  uint64_t vaddr;           // lane i < R/4: source of tile row R/4 * wv + i
+  uint32_t vswz;            // 16 (lane ^ swz_lo(R/4 * wv)): this lane's chunk in a row copy
+  uint32_t lds_rows;        // LDS address of tile row R/4 * wv
+  uint64_t vtail[R / 32];   // tail copy j: this lane's 16-byte source
+  uint32_t lds_tail[R / 32];
 };
 template <int R>
 __device__ __forceinline__ KvGather<R> kv_gather_prepare(char* tile, const uint16_t* kv, int64_t s_kv,
                                                          const int* rows, int count, int wv, int lane) {
+  constexpr int PER = R / 4;
+  static_assert(PER == 8 || PER == 16, "row copies per wave: 8 or 16");
   KvGather<R> g;
-  g.kv = kv;
-  g.zero = g_zero_row;
-  g.base = lds_offset(tile);
-  g.s_kv = (uint32_t)s_kv;
-  g.count = count;
-  g.vrow = rows[(R / 4) * wv + (lane & (R / 4 - 1))];
+  const uint32_t base = lds_offset(tile);
+  const uint64_t kva = reinterpret_cast<uint64_t>(kv);
+  const uint64_t zero = reinterpret_cast<uint64_t>(g_zero_row);
+  {
+    const int r = PER * wv + (lane & (PER - 1));
+    const int row = rows[r];
+    const bool ok = r < count && (uint32_t)row < (uint32_t)s_kv;
+    g.vaddr = ok ? kva + (uint64_t)(uint32_t)row * (2 * D_K) : zero;
+  }
+  // swz_lo(PER wv + J) = swz_lo(PER wv) ^ J for J < PER (PER wv mod 16 is 0 or 8)
+  g.vswz = 16u * (uint32_t)(lane ^ ((PER * wv) & 15));
+  g.lds_rows = base + 1024u * (uint32_t)(PER * wv);
 #pragma unroll
-  for (int j = 0; j < R / 32; ++j) g.vtail[j] = rows[8 * (wv + 4 * j) + (lane >> 3)];
+  for (int j = 0; j < R / 32; ++j) {
+    const int jj = wv + 4 * j;
+    const int r = 8 * jj + (lane >> 3);
+    const int row = rows[r];
+    const bool ok = r < count && (uint32_t)row < (uint32_t)s_kv;
+    g.vtail[j] = (ok ? kva + (uint64_t)(uint32_t)row * (2 * D_K) : zero) +
+                 2u * (uint32_t)(D_V + 8 * ((lane & 7) ^ swz_hi(r)));
+    g.lds_tail[j] = base + (uint32_t)(R * 1024 + 1024 * jj);
+  }
   return g;
 }
 template <int R, int J>
 __device__ __forceinline__ void kv_gather_copy(const KvGather<R>& g, int wv, int lane) {
   constexpr int PER = R / 4;
   if constexpr (J < PER) {
-    const int r = PER * wv + J;
-    const int row = __builtin_amdgcn_readlane(g.vrow, J);
-    const bool ok = r < g.count && (uint32_t)row < g.s_kv;
-    const uint16_t* src = (ok ? g.kv : g.zero) + (uint64_t)(uint32_t)(ok ? row : 0) * D_K;
-    g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), g.base + 1024u * (uint32_t)r);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)g.vaddr, J);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(g.vaddr >> 32), J);
+    const void* src = reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+    g2lds16_s(src, g.vswz ^ (16u * J), g.lds_rows + 1024u * J);
   } else if constexpr (J < PER + R / 32) {
     constexpr int j = J - PER;
-    const int jj = wv + 4 * j;
-    const int r = 8 * jj + (lane >> 3);
-    const int row = g.vtail[j];
-    const bool ok = r < g.count && (uint32_t)row < g.s_kv;
-    const uint16_t* src = (ok ? g.kv + (uint64_t)(uint32_t)row * D_K : g.zero) + D_V +
-                          8 * ((lane & 7) ^ swz_hi(r));
-    g2lds16_u(src, g.base + (uint32_t)(R * 1024 + 1024 * jj));
+    g2lds16_u(reinterpret_cast<const void*>(g.vtail[j]), g.lds_tail[j]);
   }
 }
 // Copy J of a gather of R contiguous rows of CH chunks starting at `first`

@@ -132,12 +132,19 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
         g2lds16_u(rec + FP8_ROPE_OFF + 16 * ((lane_id & 7) ^ swz_hi(r)),
                   lds_offset(sK[b]) + (uint32_t)(FT * 1024 + 1024 * wv));
       }
-    } else if (score_wave) {
-      gather_kv_rows_nw<FT, ROW_CHUNKS, 4, false, true>(sK[b], a.kv, a.s_kv, sRow[b],
-                                                        min(FT, n_ent - t * FT), wv, lane_id);
     } else {
-      gather_kv_rows_nw<FT, ROW_CHUNKS, 4, true, false>(sK[b], a.kv, a.s_kv, sRow[b],
-                                                        min(FT, n_ent - t * FT), wv - 4, lane_id);
+      // the rope tails of rows 8 w .. 8 w + 7 (score wave w), the first 1 KB
+      // of rows 8 c .. 8 c + 7 (PV wave 4 + c)
+      const int lw = score_wave ? wv : wv - 4;
+      const KvGather<FT> g =
+          kv_gather_prepare<FT>(sK[b], a.kv, a.s_kv, sRow[b], min(FT, n_ent - t * FT), lw, lane_id);
+      if (score_wave) {
+        kv_gather_copy<FT, FT / 4>(g, lw, lane_id);
+      } else {
+        static_for<FT / 4>([&](auto J) __attribute__((always_inline)) {
+          kv_gather_copy<FT, decltype(J)::value>(g, lw, lane_id);
+        });
+      }
     }
     copy_union_entries(nullptr, sMask[b], erow, emask, t * FT, n_ent, FT, wv, 5, 4, lane_id);
     // Row indices of the tile the next copies need: t + 1, or t + 2 for fp8

@@ -30,7 +30,7 @@ constexpr int WIN_BITS = 16384;            // kv rows per bitmap window
 constexpr int WIN_WORDS = WIN_BITS / 32;   // 512: two per thread
 constexpr int WIN_BLOCKS = WIN_BITS / 64;  // 256: one per thread
 constexpr int XFLAG_WORDS = 4096;          // T * topk <= 8 * 16384 slots
-constexpr int PLAN_LOADS = 16;             // index loads in flight per thread
+constexpr int PLAN_LOADS = 64;             // index loads in flight per thread (a group's slots in one round at T K = 16384)
 
 __device__ __forceinline__ int wave_min(int v) {
 #pragma unroll
@@ -85,12 +85,12 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   if (skv > WIN_BITS) {
     lo = 0x7fffffff;
     hi = -1;
-    for (int s0 = tid; s0 < nslots; s0 += 256 * 16) {   // 16 loads in flight per thread
-      int v[16];
+    for (int s0 = tid; s0 < nslots; s0 += 256 * PLAN_LOADS) {   // PLAN_LOADS loads in flight per thread
+      int v[PLAN_LOADS];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = s0 + 256 * j < nslots ? ix[s0 + 256 * j] : -1;
+      for (int j = 0; j < PLAN_LOADS; ++j) v[j] = s0 + 256 * j < nslots ? ix[s0 + 256 * j] : -1;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < PLAN_LOADS; ++j)
         if (v[j] >= 0 && v[j] < sidx) {
           lo = min(lo, v[j]);
           hi = max(hi, v[j]);
