@@ -14,6 +14,7 @@ SMLA_DKV_STORED_P = 8
 SMLA_FP8_POW2_SCALES = 16
 SMLA_DTYPE_BF16 = 0
 SMLA_DTYPE_F32 = 1
+SMLA_NOALLOC_SCRATCH_BYTES = 64 << 20   # smla_fwd_noalloc's per-device scratch
 
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_ALIGN",
                 4: "SMLA_ERR_WORKSPACE", 5: "SMLA_ERR_FLAGS", 6: "SMLA_ERR_HIP",
@@ -31,6 +32,8 @@ SIGNATURES = {
                                    _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "smla_plan": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _SZ, _P]),
     "smla_fwd_workspace_size": (_SZ, [_I64, _I64, _I32, _I32]),
+    "smla_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, ctypes.c_float,
+                                        _P, _P, _P]),
     "smla_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, ctypes.c_float,
                                 _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "smla_bwd_workspace_size": (_SZ, [_I64, _I64, _I32, _I32, ctypes.c_uint32]),

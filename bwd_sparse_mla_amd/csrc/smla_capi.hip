@@ -145,6 +145,38 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
 
 }  // namespace
 
+// Scratch space of smla_fwd_noalloc: one buffer per device, resident from
+// module load until the process ends.  In host code its name stands for a
+// host-side symbol, not a device address: the device address is looked up
+// (hipGetSymbolAddress, with the device current) on the first call on each
+// device and kept in g_scratch_ptr, and only that pointer is handed to the
+// kernels.
+static __device__ __align__(256) char scratch[SMLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};   // device address of `scratch`, per device ordinal
+
+// The current device's scratch buffer (its address looked up once per device).
+int scratch_for_current_device(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SMLA_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(SMLA_ERR_DEVICE, "device ordinal out of range");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SMLA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SMLA_OK;
+}
+
+}  // namespace
+
 Plan make_plan(int64_t s_q, int64_t s_kv, int heads, int topk, bool backward, bool atomic,
                bool stored_p) {
   Plan p;
@@ -445,6 +477,27 @@ int smla_fwd(const void* q, const void* kv, const int32_t* indices, int64_t s_q,
              void* workspace, size_t workspace_bytes, void* stream) {
   return smla_fwd_g(q, kv, indices, s_q, s_kv, heads, 1, topk, sm_scale, out, lse, 0u, workspace,
                     workspace_bytes, stream);
+}
+
+int smla_fwd_noalloc(const void* q, const void* kv, const int32_t* indices, int64_t s_q,
+                     int64_t s_kv, int32_t heads, int32_t topk, float sm_scale, void* out,
+                     float* lse, void* stream) {
+  g_last_error.clear();
+  int st = check_shape(s_q, s_kv, heads, topk);
+  if (st) return st;
+  const size_t need = smla_fwd_workspace_size(s_q, s_kv, heads, topk);
+  if (need > SMLA_NOALLOC_SCRATCH_BYTES)
+    return fail(SMLA_ERR_WORKSPACE,
+                "smla_fwd_noalloc: this shape needs " + std::to_string(need) +
+                    " bytes of scratch, more than the library's " +
+                    std::to_string(SMLA_NOALLOC_SCRATCH_BYTES) +
+                    " bytes per device; call smla_fwd with a workspace");
+  if (!kv) return fail(SMLA_ERR_NULL, "null tensor pointer");
+  if ((st = check_device())) return st;
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws))) return st;
+  return fwd_impl(q, kv, nullptr, indices, s_q, s_kv, heads, 1, topk, sm_scale, out, lse, 0u, ws,
+                  SMLA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,

@@ -137,6 +137,24 @@ int smla_fwd_ex(const void* q, const void* kv, const int32_t* indices,
                 void* out, float* lse, uint32_t flags, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/* smla_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, bit for bit, with its scratch space in a buffer the
+ * library holds on each device -- SMLA_NOALLOC_SCRATCH_BYTES, 64 MiB, from
+ * the first call on a device until the process ends -- so the call itself
+ * allocates nothing.  The caller still owns q, kv, indices, out and lse.
+ * Shapes whose smla_fwd_workspace_size(s_q, s_kv, heads, topk) exceeds
+ * SMLA_NOALLOC_SCRATCH_BYTES (about s_q * topk * 5 bytes; e.g. s_q = 4096,
+ * topk = 2048 needs 42 MB) return SMLA_ERR_WORKSPACE before anything is
+ * launched.  All calls on one device share its buffer: calls that may run
+ * concurrently on that device (different streams, or different host threads
+ * without ordering) race and must not overlap; calls on one stream are
+ * ordered.  Nothing in the buffer needs to start cleared. */
+#define SMLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int smla_fwd_noalloc(const void* q, const void* kv, const int32_t* indices,
+                     int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk, float sm_scale,
+                     void* out, float* lse, void* stream);
+
 size_t smla_fwd_workspace_size(int64_t s_q, int64_t s_kv, int32_t heads, int32_t topk);
 
 /* Backward.

@@ -220,3 +220,20 @@ def test_nonfinite_argument_errors(lib):
     # a reference that overlaps the buffer (other than the buffer itself) is refused
     assert lib.smla_nonfinite_replace(P(FAKE), P(FAKE + 16), 1, 64, cnt, P(0)) == 2
     assert b"overlaps" in lib.smla_last_error()
+
+
+def test_fwd_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """smla_fwd_noalloc has a fixed per-device scratch buffer: a shape whose
+    forward workspace exceeds it is refused before anything is launched (no
+    GPU needed to see the refusal)."""
+    from bwd_sparse_mla_amd import _lib
+    cap = _lib.SMLA_NOALLOC_SCRATCH_BYTES
+    assert lib.smla_fwd_workspace_size(4096, 4096, 8, 2048) <= cap      # the packed ragged batch fits
+    assert lib.smla_fwd_workspace_size(8192, 8192, 16, 2048) > cap      # the recency workload does not
+    P = ctypes.c_void_p
+    st = lib.smla_fwd_noalloc(P(16), P(16), P(16), 8192, 8192, 16, 2048, 0.1, P(16), P(16), None)
+    assert _lib.STATUS_NAMES[st] == "SMLA_ERR_WORKSPACE"
+    msg = lib.smla_last_error().decode()
+    assert "smla_fwd_noalloc" in msg and str(cap) in msg
+    st = lib.smla_fwd_noalloc(P(16), P(16), P(16), 64, 64, 12, 64, 0.1, P(16), P(16), None)
+    assert _lib.STATUS_NAMES[st] == "SMLA_ERR_SHAPE"      # unsupported head count
