@@ -3,18 +3,21 @@
 //
 // One workgroup of 8 waves owns a query group: T = 64/H consecutive tokens,
 // 64 query rows.  It walks the union of the group's selected KV rows in tiles
-// of 32 rows, gathered into LDS with direct global->LDS copies (three
-// buffers), and splits the work in two roles that run one tile apart:
+// of 32 rows, gathered into LDS with direct global->LDS copies two tiles
+// ahead of their use (four buffers), and splits the work in two roles that
+// run one tile apart:
 //   score waves 0-3: wave w scores rows 16w..16w+15 against the tile
 //            (S^T = K Q^T: K from LDS as the A operand, the wave's Q rows
 //            held in registers as the B operand, 36 MFMA 16x16x32), then the
 //            row softmax, and leaves P (bf16) and the rescale factors in LDS;
 //   PV waves 4-7:    wave 4+c accumulates out[:, 128c .. 128c+127] for all 64
 //            rows from the previous tile's P and V (32 MFMA).
-// Per step every wave waits for its copies and the workgroup syncs once; then
-// the next tile's copies are issued (8-9 per PV wave, one per score wave) and
-// the PV waves take tile j-1 while the score waves take tile j.  Two waves share each SIMD, so
-// one's softmax, copies and LDS waits overlap the other's MFMAs.
+// Per step every wave waits for the copies it issued two steps before (its
+// copies of the previous step may still be in flight) and the workgroup syncs
+// once; then the copies of tile j+2 are issued (8-9 per PV wave, one per
+// score wave) and the PV waves take tile j-1 while the score waves take tile
+// j.  Two waves share each SIMD, so one's softmax, copies and LDS waits
+// overlap the other's MFMAs.
 //
 // The running max starts at a finite -1e30, so a tile with no valid entry
 // never forms exp(-inf - -inf); the final denominator is floored at 1e-30, a
@@ -71,11 +74,14 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2_pow2(uint32_t w, float sc) {
 template <int H, int FP8>
 __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
-  __shared__ __attribute__((aligned(16))) char sK[FNB][KV32_TILE_BYTES];
+  // bf16 kv: four tile buffers (tiles j-1 .. j+2: copies run two tiles
+  // ahead); fp8 kv: three (its staging buffers take the rest of the LDS)
+  constexpr int NBUF = FP8 ? FNB : FNB + 1;
+  __shared__ __attribute__((aligned(16))) char sK[NBUF][KV32_TILE_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char sF[2][FP8 ? SF_BYTES : 16];   // fp8 staging
   __shared__ __attribute__((aligned(16))) unsigned short sP[2][GROUP_ROWS * SPS];
-  __shared__ __attribute__((aligned(16))) unsigned char sMask[FNB][256];  // token masks (word copies)
-  __shared__ __attribute__((aligned(16))) int sRow[FNB][64];             // kv rows of a tile's entries
+  __shared__ __attribute__((aligned(16))) unsigned char sMask[NBUF][256];  // token masks (word copies)
+  __shared__ __attribute__((aligned(16))) int sRow[NBUF][64];             // kv rows of a tile's entries
   __shared__ float sAlpha[2][GROUP_ROWS];                               // rescale factor per row
   __shared__ int sMoved[2][4];                                          // per score wave: a max moved
   __shared__ float sL[GROUP_ROWS];
@@ -116,12 +122,15 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   const int tl = (16 * wv + (lane_id & 15)) / H;
   float m_run = M_INIT, lsum = 0.f;
 
-  // Copies of tile t (its rows' indices are in sRow[t % 3]): the first 1 KB
+  // Copies of tile t (its rows' indices are in sRow[t % NBUF]): the first 1 KB
   // of 8 kv rows per PV wave, the rope tails of 8 rows per score wave (the
   // score waves carry more of the per-tile work), the token masks by wave 4,
-  // the row indices of tile t + 1 by wave 5.
+  // the row indices of tile t + 2 by wave 5.  Per call each wave issues a
+  // fixed number of copies (bf16 kv: score waves 1, waves 4 and 5 nine,
+  // waves 6 and 7 eight; past the union they copy zero rows), which the
+  // counted waits of the main loop rely on.
   auto issue = [&](int t) __attribute__((always_inline)) {
-    const int b = t % FNB;
+    const int b = t % NBUF;
     if constexpr (FP8) {
       if (score_wave && wv < FT / 8) {   // rope tails of rows 8 wv .. 8 wv + 7
         const int r = 8 * wv + (lane_id >> 3);
@@ -147,12 +156,12 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
       }
     }
     copy_union_entries(nullptr, sMask[b], erow, emask, t * FT, n_ent, FT, wv, 5, 4, lane_id);
-    // Row indices of the tile the next copies need: t + 1, or t + 2 for fp8
-    // kv, whose PV-wave loads run a tile further ahead.  The buffer it lands
-    // in is read by no wave during this step.
-    const int ti = t + (FP8 ? 2 : 1);
-    if (ti < ntiles)
-      copy_union_entries(sRow[ti % FNB], nullptr, erow, emask, ti * FT, n_ent, FT, wv, 5, 4,
+    // Row indices of tile t + 2, the tile the copies two steps on need (the
+    // copies run two tiles ahead of their use, for fp8 kv the staging
+    // loads).  The buffer it lands in is read by no wave during this step.
+    const int ti = t + 2;
+    if (!FP8 || ti < ntiles)
+      copy_union_entries(sRow[ti % NBUF], nullptr, erow, emask, ti * FT, n_ent, FT, wv, 5, 4,
                          lane_id);
   };
 
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   // tile's count, and indices outside [0, s_kv), read the zero row (all-zero
   // bytes: value 0, scale 0).
   auto fp8_stage = [&](int t) __attribute__((always_inline)) {
-    const int b = t % FNB;
+    const int b = t % NBUF;
     const int count = min(FT, n_ent - t * FT);
     const uint32_t st = lds_offset(sF[t & 1]);
     const int half = lane_id >> 5, m = lane_id & 31;
@@ -189,7 +198,7 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   // which become bf16 chunks 2 (l mod 32) and 2 (l mod 32) + 1 of the row.
   auto fp8_convert = [&](int t) __attribute__((always_inline)) {
     const unsigned char* st = sF[t & 1];
-    char* tile = sK[t % FNB];
+    char* tile = sK[t % NBUF];
     const int half = lane_id >> 5, m = lane_id & 31;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -223,8 +232,8 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
 
   // Scores and softmax of tile t (score waves).
   auto score = [&](int t) __attribute__((always_inline)) {
-    const char* kt = sK[t % FNB];
-    const unsigned char* mkb = sMask[t % FNB];
+    const char* kt = sK[t % NBUF];
+    const unsigned char* mkb = sMask[t % NBUF];
     int lane = lane_id;
     asm volatile("" : "+v"(lane));   // offsets recomputed per tile, not kept live
     const int g16 = lane >> 4, r16 = lane & 15;
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
   // PV of tile t (PV waves): columns 128c .. 128c+127 for all 64 rows.
   auto pv = [&](int t) __attribute__((always_inline)) {
     const int c = wv - 4;
-    const char* vt = sK[t % FNB];
+    const char* vt = sK[t % NBUF];
     const unsigned short* pt = sP[t & 1];
     int lane = lane_id;
     asm volatile("" : "+v"(lane));
@@ -322,20 +331,19 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
     short8_t vb[VPF + 1];
 #pragma unroll
     for (int d = 0; d < VPF; ++d) vb[d] = ld_bt_rs_lo<FT>(vt, 0, 128 * c + 16 * d, lane);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      if (n + VPF < 8) vb[(n + VPF) % (VPF + 1)] = ld_bt_rs_lo<FT>(vt, 0, 128 * c + 16 * (n + VPF), lane);
+    static_for<8>([&](auto N) __attribute__((always_inline)) {
+      constexpr int n = decltype(N)::value;
+      if constexpr (n + VPF < 8) vb[(n + VPF) % (VPF + 1)] = ld_bt_rs_lo<FT>(vt, 0, 128 * c + 16 * (n + VPF), lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(pa[rb], vb[n % (VPF + 1)], acc[rb][n]);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
 
   if (ntiles > 0) {
     copy_union_entries(sRow[0], nullptr, erow, emask, 0, n_ent, FT, wv, 5, 4, lane_id);
-    if (FP8 && ntiles > 1)
-      copy_union_entries(sRow[1], nullptr, erow, emask, FT, n_ent, FT, wv, 5, 4, lane_id);
+    copy_union_entries(sRow[1], nullptr, erow, emask, FT, n_ent, FT, wv, 5, 4, lane_id);
     wait_vmcnt0();
     __syncthreads();
     issue(0);
@@ -345,25 +353,55 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
       wait_vmcnt0();
       __syncthreads();
       fp8_convert(0);
+    } else {
+      issue(1);            // (tile 2's and 3's row indices come with these)
     }
   }
-  // Step j: the score waves take tile j, the PV waves tile j - 1; tile j + 1
-  // is copied meanwhile into the buffer tile j - 2 used.  The two roles run
+  // Step j: the score waves take tile j, the PV waves tile j - 1; the next
+  // tile's copies go into a buffer no wave reads in this step.  The two roles run
   // separate loops (so each keeps only its own state in registers) with the
   // same count of workgroup barriers, one per step.  fp8: tile j + 2 is
   // staged (into the staging buffer tile j left; its indices landed at this
   // step's barrier) and, before its role's work, every wave converts its rows
   // of tile j + 1 (staged a step ago) into the buffer tile j - 2 used.
-  if (score_wave) {
+  if constexpr (!FP8) {
+    // bf16 kv: step j issues tile j + 2 (into the buffer of tile j - 2) and
+    // waits at its start only for what step j - 2 and earlier issued -- the
+    // wave's own copies of step j - 1 (a fixed count per wave) may still be
+    // in flight -- so a tile's gather has two steps to land.
+    if (ntiles > 0) {
+      if (score_wave) {
+        for (int j = 0; j <= ntiles; ++j) {
+          if (j == 0) wait_vmcnt0(); else wait_vmcnt<1>();
+          __syncthreads();
+          issue(j + 2);
+          if (j < ntiles) score(j);
+        }
+      } else {
+        for (int j = 0; j <= ntiles; ++j) {
+          if (j == 0) {
+            wait_vmcnt0();
+          } else if (wv == 4 || wv == 5) {
+            wait_vmcnt<FT / 4 + 1>();
+          } else {
+            wait_vmcnt<FT / 4>();
+          }
+          __syncthreads();
+          issue(j + 2);
+          if (j >= 1) pv(j - 1);
+        }
+      }
+    }
+  } else if (score_wave) {
     for (int j = 0; j <= ntiles; ++j) {
       wait_vmcnt0();
       __syncthreads();
       if (j + 1 < ntiles) issue(j + 1);
-      if (FP8 && j + 2 < ntiles) fp8_stage(j + 2);
-      if (FP8 && j + 1 < ntiles) fp8_convert(j + 1);
+      if (j + 2 < ntiles) fp8_stage(j + 2);
+      if (j + 1 < ntiles) fp8_convert(j + 1);
       if (j < ntiles) score(j);
     }
-  } else if constexpr (FP8) {
+  } else {
     for (int j = 0; j <= ntiles; ++j) {
       wait_vmcnt0();
       __syncthreads();
@@ -372,17 +410,12 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
       if (j + 1 < ntiles) fp8_convert(j + 1);
       if (j >= 1) pv(j - 1);
     }
-  } else {
-    for (int j = 0; j <= ntiles; ++j) {
-      wait_vmcnt0();
-      __syncthreads();
-      if (j + 1 < ntiles) issue(j + 1);
-      if (j >= 1) pv(j - 1);
-    }
   }
 
   // Epilogue: LSE from the score waves; the PV waves normalise their columns
-  // and stage them through LDS (the tile buffers are free) for 16-byte stores.
+  // and stage them through LDS (the tile buffers are free once the last
+  // copies, zero rows past the union, have landed) for 16-byte stores.
+  wait_vmcnt0();
   if (score_wave && (lane_id >> 4) == 0) {
     const int rr = 16 * wv + (lane_id & 15);
     sL[rr] = lsum;
