@@ -794,26 +794,120 @@ __device__ __forceinline__ void dkv_segment_pair(const BwdArgs& a, int64_t unit,
   }
 }
 
+// Sub-chunk prefix of the dkv units computed by the calling workgroup (NT
+// threads) instead of read from spre / wstart: with few units every
+// workgroup redoing the scan costs less than a launch of its own.  Thread t
+// sums units [t c, (t + 1) c), c = ceil(NU / NT); a block-wide exclusive scan
+// of those sums gives each thread the prefix at its first unit.  Returns the
+// total; with wg >= 0 also the unit whose sub-chunks [pre, pre + 2 nchunk)
+// hold the first sub-chunk of dkv workgroup wg's range (min(total, wg per),
+// per = max(1, ceil(total / DKV_WGS))) and its pre (unit -1 when the range is
+// empty); with unit >= 0 the prefix at unit and at unit + 1.
+struct UnitScan {
+  int total;
+  int t_unit, t_pre;   // unit holding workgroup wg's first sub-chunk, and its prefix
+  int u_pre, u_end;    // prefix at `unit` and at unit + 1
+};
+template <int NT>
+__device__ __forceinline__ UnitScan dkv_unit_scan(const BwdArgs& a, int wg, int64_t unit, int* red) {
+  constexpr int NWV = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t cnt = (a.NU + NT - 1) / NT;
+  const int64_t b0 = min<int64_t>(a.NU, tid * cnt), b1 = min<int64_t>(a.NU, b0 + cnt);
+  int sum = 0;
+  for (int64_t b = b0; b < b1; ++b) sum += 2 * a.nchunk[b];
+  int x = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) red[wv] = x;
+  if (tid == 0) {
+    red[NWV] = -1;
+    red[NWV + 2] = 0;
+    red[NWV + 3] = 0;
+  }
+  __syncthreads();
+  int base = x - sum, total = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    if (w < wv) base += red[w];
+    total += red[w];
+  }
+  const int target = wg >= 0 ? min(total, wg * max(1, (total + DKV_WGS - 1) / DKV_WGS)) : -1;
+  if (target >= 0 && target < total && base <= target && target < base + sum) {
+    int p = base;
+    for (int64_t b = b0; b < b1; ++b) {
+      const int v = 2 * a.nchunk[b];
+      if (target < p + v) {
+        red[NWV] = (int)b;
+        red[NWV + 1] = p;
+        break;
+      }
+      p += v;
+    }
+  }
+  if (unit >= b0 && unit < b1) {
+    int p = base;
+    for (int64_t b = b0; b < unit; ++b) p += 2 * a.nchunk[b];
+    red[NWV + 2] = p;
+    red[NWV + 3] = p + 2 * a.nchunk[unit];
+  }
+  __syncthreads();
+  UnitScan r;
+  r.total = total;
+  r.t_unit = red[NWV];
+  r.t_pre = red[NWV + 1];
+  r.u_pre = red[NWV + 2];
+  r.u_end = red[NWV + 3];
+  __syncthreads();   // red is reused by the caller
+  return r;
+}
+
 // The dkv pass: workgroup w takes sub-chunks [w per, (w+1) per) of all
 // blocks' sub-chunks in block order (per = ceil(total / DKV_WGS)), as one
-// segment per block it meets, starting from block wstart[w].
+// segment per block it meets, starting from block wstart[w] (with few units
+// the workgroup finds its start and the prefix itself).
 template <int H, bool PDS>
 __global__ __launch_bounds__(DKV_NW * 64, 1) void bwd_dkv_kernel(BwdArgs a) {
   __shared__ std::conditional_t<PDS, DkvPairLds, DkvLds> lds;
-  const int total = a.spre[a.NU];
-  const int per = max(1, (total + DKV_WGS - 1) / DKV_WGS);
-  int lo = min(total, (int)blockIdx.x * per);
-  const int hi = min(total, lo + per);
-  if (lo >= hi) return;
-  for (int64_t blk = a.wstart[blockIdx.x]; lo < hi; ++blk) {
-    const int sb = a.spre[blk], se = a.spre[blk + 1];
-    if (se <= lo) continue;   // a block with no records
+  __shared__ int red[DKV_NW + 4];
+  const bool inl = a.NU <= DKV_INLINE_UNITS;
+  int total, per, lo, hi;
+  int64_t blk0;
+  int sb;
+  if (inl) {
+    const UnitScan us = dkv_unit_scan<DKV_NW * 64>(a, (int)blockIdx.x, -1, red);
+    total = us.total;
+    per = max(1, (total + DKV_WGS - 1) / DKV_WGS);
+    lo = min(total, (int)blockIdx.x * per);
+    hi = min(total, lo + per);
+    if (lo >= hi) return;
+    blk0 = us.t_unit;
+    sb = us.t_pre;
+  } else {
+    total = a.spre[a.NU];
+    per = max(1, (total + DKV_WGS - 1) / DKV_WGS);
+    lo = min(total, (int)blockIdx.x * per);
+    hi = min(total, lo + per);
+    if (lo >= hi) return;
+    blk0 = a.wstart[blockIdx.x];
+    sb = a.spre[blk0];
+  }
+  for (int64_t blk = blk0; lo < hi; ++blk) {
+    const int se = sb + 2 * a.nchunk[blk];
+    if (se <= lo) {   // a block with no records
+      sb = se;
+      continue;
+    }
     const int end = min(hi, se);
     if constexpr (PDS)
       dkv_segment_pair<H>(a, blk, lo - sb, end - sb, (int64_t)blockIdx.x + blk, lds);
     else
       dkv_segment<H>(a, blk, lo - sb, end - sb, (int64_t)blockIdx.x + blk, lds);
     lo = end;
+    sb = se;
     __syncthreads();   // the next segment refills the LDS buffers
   }
 }
@@ -875,6 +969,7 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
   __shared__ float sX[FIN_ROWS * D_K];   // extra-slot contributions of the rows
   __shared__ float red[4];
+  __shared__ int red_i[8];
   const int tid = threadIdx.x;
   const int64_t blk = blockIdx.x / FIN_PARTS;
   const int part = blockIdx.x % FIN_PARTS;
@@ -884,9 +979,18 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
   // cover its sub-chunks, added in w order.
   const int64_t unit = blk / a.ub;
   const int hb = (int)(blk - unit * a.ub);   // the block's half of the unit
-  const int total = a.spre[a.NU];
+  int total, sb, se;
+  if (a.NU <= DKV_INLINE_UNITS) {
+    const UnitScan us = dkv_unit_scan<256>(a, -1, unit, red_i);
+    total = us.total;
+    sb = us.u_pre;
+    se = us.u_end;
+  } else {
+    total = a.spre[a.NU];
+    sb = a.spre[unit];
+    se = a.spre[unit + 1];
+  }
   const int per = max(1, (total + DKV_WGS - 1) / DKV_WGS);
-  const int sb = a.spre[unit], se = a.spre[unit + 1];
   const int w0 = sb / per;
   const int nsplit = se > sb ? (se - 1) / per - w0 + 1 : 0;
   unsigned long long touched = 0ull;
@@ -1023,6 +1127,7 @@ hipError_t launch_dkv_schedule(const BwdArgs& a, bool lists_built, hipStream_t s
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (a.NU <= DKV_INLINE_UNITS) return hipSuccess;   // the dkv and finalize kernels scan themselves
   dkv_prefix_kernel<<<dim3(1), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }

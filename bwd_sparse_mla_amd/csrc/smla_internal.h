@@ -162,6 +162,9 @@ hipError_t launch_dkv_finalize(const BwdArgs& a, int heads, hipStream_t stream);
 // equal share of all sub-chunks in block order (stream-K style); a workgroup
 // w that covers sub-chunks of block b leaves its partial in slot w + b.
 constexpr int DKV_WGS = 256;
+// Up to this many dkv units the dkv and finalize workgroups compute the
+// sub-chunk prefix themselves (no prefix launch, spre / wstart unused).
+constexpr int64_t DKV_INLINE_UNITS = 2048;
 // Nonfinite diagnostics over n elements of es (2: bf16, 4: fp32) bytes at
 // x: count the NaN / Inf entries, or replace them from ref (null: zero);
 // the count is added into *count.
