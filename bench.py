@@ -404,10 +404,11 @@ def gather_block(w, ms: float):
 
 # Other configurations of the same path, reported beside the headline: the
 # tiny correctness case, the padding-stress batch, one GPU's share at the
-# production shape (recency-biased picks) and the long context in both dkv
-# modes.  (name, dkv atomic, timed steps, warm-up steps)
+# production shape (recency-biased picks), the long context in both dkv
+# modes, and the packed batch with 0.1% repeated slots (the cost of the
+# repeated-slot path).  (name, dkv atomic, timed steps, warm-up steps)
 CONFIGS = [("tiny", False, 20, 3), ("padding_stress", False, 20, 3), ("recency", False, 5, 2),
-           ("long_context", False, 3, 1), ("long_context", True, 3, 1)]
+           ("long_context", False, 3, 1), ("long_context", True, 3, 1), ("repeated_slots", False, 5, 2)]
 
 
 def config_line(w, dev, atomic: bool, stored: bool, steps: int, warmup: int):

@@ -946,17 +946,6 @@ __global__ __launch_bounds__(256) void dkv_prefix_kernel(BwdArgs a) {
   }
 }
 
-// Sum of 256 per-thread values, identical on every thread (fixed order).
-__device__ __forceinline__ float block_sum256(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const float r = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
-  return r;
-}
-
 // Writes dkv for FIN_ROWS rows of a block (64 / FIN_ROWS workgroups per
 // block): the block's partials added in workgroup order, plus -- only when
 // some index row repeats an entry -- the extra slots' contributions, each
@@ -964,12 +953,18 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // accumulate, rows no slot selects) are applied here.  Bitwise reproducible.
 constexpr int FIN_ROWS = 4;
 constexpr int FIN_PARTS = TILE_KV / FIN_ROWS;   // workgroups per block
+constexpr int FIN_XCAP = 512;   // extra slots listed per pass
+constexpr int FIN_XB = 16;      // extra slots per batch
 template <int H>
 __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
   __shared__ float sX[FIN_ROWS * D_K];   // extra-slot contributions of the rows
-  __shared__ float red[4];
   __shared__ int red_i[8];
+  __shared__ int scr_i[8];
+  __shared__ int64_t sXe[FIN_XCAP];      // listed extra slots (union entry index)
+  __shared__ float sXp[FIN_XB][H];       // P and dS of a batch's extras per head
+  __shared__ float sXd[FIN_XB][H];
+  __shared__ unsigned s_xt;              // rows the extras touch
   const int tid = threadIdx.x;
   const int64_t blk = blockIdx.x / FIN_PARTS;
   const int part = blockIdx.x % FIN_PARTS;
@@ -999,42 +994,136 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
 
   const bool extras = *a.xtotal > 0;
   if (extras) {
-    for (int e = tid; e < FIN_ROWS * D_K; e += 256) sX[e] = 0.f;
-    __syncthreads();
-    for (int64_t g = 0; g < a.G; ++g) {
-      const int xc = a.xcount[g];
-      if (xc == 0) continue;
-      const int n_main = a.qcount[g] - xc;
-      for (int x = 0; x < xc; ++x) {
-        const int64_t row = a.qrow[g * a.qcap + n_main + x];
-        if (row < r0 || row >= r0 + FIN_ROWS || row >= a.s_kv) continue;
-        int64_t t = g * T + (__ffs((unsigned)a.qmask[g * a.qcap + n_main + x]) - 1);
-        t = t < 0 ? 0 : (t >= a.s_q ? a.s_q - 1 : t);
-        const int rl = (int)(row - r0);
-        touched |= 1ull << rl;
-        const uint16_t* kr = a.kv + row * D_K;
-        for (int h = 0; h < H; ++h) {
-          const uint16_t* qr = a.q + (t * H + h) * D_K;
-          const uint16_t* dr = a.dout + (t * H + h) * D_V;
-          float z = 0.f, dp = 0.f;
-          for (int c = tid; c < D_K; c += 256) {
-            const float k = bf2f(kr[c]);
-            z += bf2f(qr[c]) * k;
-            if (c < D_V) dp += bf2f(dr[c]) * k;
+    // Extra slots whose row lies in r0 .. r0 + FIN_ROWS - 1, in (group, slot)
+    // order.  Thread t scans groups t, t + 256, ... (a group's extras in slot
+    // order); one block scan per round of 256 groups keeps the order.  Up to
+    // FIN_XCAP matches are listed per pass (another pass takes the next ones),
+    // and handled FIN_XB at a time: first P and dS of every head (one wave
+    // per extra), then every thread adds the batch's terms to its columns in
+    // (extra, head) order.
+    if (tid == 0) s_xt = 0u;
+    const int wv = tid >> 6, lane = tid & 63;
+    float xa[FIN_ROWS][3];   // the terms of columns tid, tid + 256, tid + 512 (< 576) per row
+#pragma unroll
+    for (int r = 0; r < FIN_ROWS; ++r)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) xa[r][k] = 0.f;
+    int n_done = 0;
+    for (;;) {
+      int seen = 0;
+      for (int64_t g0 = 0; g0 < a.G; g0 += 256) {
+        const int64_t g = g0 + tid;
+        int cnt = 0, xc = 0, n_main = 0;
+        if (g < a.G) {
+          xc = a.xcount[g];
+          n_main = a.qcount[g] - xc;
+          const int32_t* xr = a.qrow + g * a.qcap + n_main;
+          for (int x0 = 0; x0 < xc; x0 += 8) {   // eight loads in flight
+            int rr[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) rr[j] = x0 + j < xc ? xr[x0 + j] : -1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cnt += rr[j] >= r0 && rr[j] < r0 + FIN_ROWS && rr[j] < a.s_kv;
           }
-          z = block_sum256(z, red);
-          dp = block_sum256(dp, red);
-          const float p = fast_exp2(z * a.scale_log2 - a.lse[t * H + h] * LOG2E);
-          const float ds = p * (dp - a.delta[t * H + h]) * a.scale;
-          for (int c = tid; c < D_K; c += 256) {
-            float v = ds * bf2f(qr[c]);
-            if (c < D_V) v += p * bf2f(dr[c]);
-            sX[rl * D_K + c] += v;
-          }
-          __syncthreads();
         }
+        int tot;
+        int m = seen + block_exclusive_scan256(cnt, scr_i, &tot);
+        if (cnt > 0 && m + cnt > n_done && m < n_done + FIN_XCAP) {
+          const int32_t* xr = a.qrow + g * a.qcap + n_main;
+          for (int x0 = 0; x0 < xc; x0 += 8) {   // eight loads in flight
+            int rr[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) rr[j] = x0 + j < xc ? xr[x0 + j] : -1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              if (rr[j] >= r0 && rr[j] < r0 + FIN_ROWS && rr[j] < a.s_kv) {
+                if (m >= n_done && m < n_done + FIN_XCAP) {
+                  sXe[m - n_done] = g * a.qcap + n_main + x0 + j;
+                  atomicOr(&s_xt, 1u << (int)(rr[j] - r0));
+                }
+                ++m;
+              }
+            }
+          }
+        }
+        seen += tot;
       }
+      __syncthreads();
+      const int npass = min(FIN_XCAP, seen - n_done);
+      for (int b0 = 0; b0 < npass; b0 += FIN_XB) {
+        const int nb = min(FIN_XB, npass - b0);
+        for (int e = wv; e < nb; e += 4) {   // P and dS of extra b0 + e, every head
+          const int64_t ent = sXe[b0 + e];
+          const int64_t row = a.qrow[ent];
+          const int64_t g = ent / a.qcap;
+          int64_t t = g * T + (__ffs((unsigned)a.qmask[ent]) - 1);
+          t = t < 0 ? 0 : (t >= a.s_q ? a.s_q - 1 : t);
+          float kk[9];
+#pragma unroll
+          for (int i = 0; i < 9; ++i) kk[i] = bf2f(a.kv[row * D_K + lane + 64 * i]);
+#pragma unroll 4
+          for (int h = 0; h < H; ++h) {
+            const uint16_t* qr = a.q + (t * H + h) * D_K;
+            const uint16_t* dr = a.dout + (t * H + h) * D_V;
+            float z = 0.f, dp = 0.f;
+#pragma unroll
+            for (int i = 0; i < 9; ++i) {
+              z += bf2f(qr[lane + 64 * i]) * kk[i];
+              if (i < 8) dp += bf2f(dr[lane + 64 * i]) * kk[i];
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+              z += __shfl_xor(z, o);
+              dp += __shfl_xor(dp, o);
+            }
+            const float pv = fast_exp2(z * a.scale_log2 - a.lse[t * H + h] * LOG2E);
+            if (lane == 0) {
+              sXp[e][h] = pv;
+              sXd[e][h] = pv * (dp - a.delta[t * H + h]) * a.scale;
+            }
+          }
+        }
+        __syncthreads();
+        for (int e = 0; e < nb; ++e) {   // the batch's terms, in (extra, head) order
+          const int64_t ent = sXe[b0 + e];
+          const int rl = (int)(a.qrow[ent] - r0);
+          const int64_t g = ent / a.qcap;
+          int64_t t = g * T + (__ffs((unsigned)a.qmask[ent]) - 1);
+          t = t < 0 ? 0 : (t >= a.s_q ? a.s_q - 1 : t);
+          float v[3] = {0.f, 0.f, 0.f};
+#pragma unroll 8
+          for (int h = 0; h < H; ++h) {
+            const uint16_t* qr = a.q + (t * H + h) * D_K;
+            const uint16_t* dr = a.dout + (t * H + h) * D_V;
+            const float pv = sXp[e][h], dsv = sXd[e][h];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+              const int c = tid + 256 * k;
+              if (c < D_K) {
+                float x = dsv * bf2f(qr[c]);
+                if (c < D_V) x += pv * bf2f(dr[c]);
+                v[k] += x;
+              }
+            }
+          }
+          // (per extra: its heads' terms summed first, then added to the row)
+#pragma unroll
+          for (int r = 0; r < FIN_ROWS; ++r)
+            if (rl == r)
+#pragma unroll
+              for (int k = 0; k < 3; ++k) xa[r][k] += v[k];
+        }
+        __syncthreads();
+      }
+      n_done += npass;
+      if (n_done >= seen) break;
     }
+#pragma unroll
+    for (int r = 0; r < FIN_ROWS; ++r)
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        if (tid + 256 * k < D_K) sX[r * D_K + tid + 256 * k] = xa[r][k];
+    touched |= (unsigned long long)s_xt;
     __syncthreads();
   }
 

@@ -243,6 +243,26 @@ def packed_ragged(seed: int = 1) -> Workload:
     return Workload("packed_ragged_s4096_h8_k2048", q, kv, dout, idx, SM_SCALE, seqlens, seed)
 
 
+def repeated_slots(seed: int = 6, dup_frac: float = 0.001) -> Workload:
+    """The packed ragged batch with a fraction `dup_frac` of the valid slots
+    overwritten by a copy of another valid slot of the same row, so some rows
+    list a kv row twice (each slot stays its own softmax term): the input
+    class that takes the planner's and the dkv finalize's repeated-slot path."""
+    w = packed_ragged(seed)
+    rng = np.random.default_rng(seed + 100)
+    idx = w.idx.copy()
+    for s in range(w.S):
+        nv = int((idx[s] >= 0).sum())
+        if nv < 2:
+            continue
+        m = np.nonzero(rng.random(nv) < dup_frac)[0]
+        if m.size:
+            src = rng.integers(0, nv, size=m.size)
+            idx[s, m] = idx[s, src]
+    return Workload(f"repeated_slots_s{w.S}_h{w.H}_k{w.K}_dup{dup_frac:g}", w.q, w.kv, w.dout, idx,
+                    SM_SCALE, w.seqlens, seed)
+
+
 def padding_stress(seed: int = 2, sigma: float = 2.0) -> Workload:
     """S=4096 packed as 16 sequences with lengths uniform in [16, 512] (nudged to
     sum to 4096), H=8, topk=2048, q/kv ~ N(0, sigma^2) with sigma=2 (variance 4)
@@ -305,6 +325,7 @@ WORKLOADS = {
     "recency": recency_hot_rows,
     "long_context": long_context,
     "heads128": heads128,
+    "repeated_slots": repeated_slots,
 }
 
 
