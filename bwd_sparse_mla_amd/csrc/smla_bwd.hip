@@ -38,11 +38,39 @@ namespace {
 // the stored-P form a unit is a pair of blocks: a group with records in
 // either block is a chunk, with, per block, its first union entry there and
 // the rows it selects (zero where it has none).
+// Exclusive prefix sum over a block of NT threads (a multiple of 64);
+// returns this thread's exclusive prefix and writes the block total to
+// *total.  `scratch` holds at least NT / 64 ints of LDS.  Must be called by
+// all threads.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan_nt(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int s = scratch[w];
+    if (w < wave) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+template <int NT>
 __device__ __forceinline__ void dkv_schedule_unit(const BwdArgs& a, int64_t unit) {
-  __shared__ int scratch[8];
+  __shared__ int scratch[NT / 64];
   const int tid = threadIdx.x;
   int base = 0;
-  for (int64_t gb = 0; gb < a.G; gb += 256) {
+  for (int64_t gb = 0; gb < a.G; gb += NT) {
     const int64_t g = gb + tid;
     int2 e = make_int2(0, 0), e1 = make_int2(0, 0);
     if (a.ub == 2) {
@@ -53,7 +81,7 @@ __device__ __forceinline__ void dkv_schedule_unit(const BwdArgs& a, int64_t unit
     }
     const int nz = (e.y > 0 || e1.y > 0) ? 1 : 0;
     int total;
-    const int pos = base + block_exclusive_scan256(nz, scratch, &total);
+    const int pos = base + block_exclusive_scan_nt<NT>(nz, scratch, &total);
     if (nz) {
       a.clist[unit * a.G + pos] = make_int2((int)g, e.x);
       if (a.ub == 2) {   // stored-P form: per block, the first union entry and the rows
@@ -71,271 +99,277 @@ __device__ __forceinline__ void dkv_schedule_unit(const BwdArgs& a, int64_t unit
 }
 
 __global__ __launch_bounds__(256) void dkv_schedule_kernel(BwdArgs a) {
-  dkv_schedule_unit(a, blockIdx.x);
+  dkv_schedule_unit<256>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
 // dq pass
 // ---------------------------------------------------------------------------
-// Query group of T = 64/H tokens (64 rows), union tiles of 32 kv rows,
-// double buffered.  dout of the group's rows lives in LDS (it is the A operand
-// of dP), Q in registers; per tile each wave computes scores and dP for its 16
-// rows, then dq += dS . K for all 64 rows and its 144 output columns (128
-// main columns and 16 of the 64 tail columns).
+// Query group of T = 64/H tokens (64 rows), union tiles of 32 kv rows.  One
+// workgroup of 8 waves, two roles one tile apart (two waves per SIMD, so one
+// role's softmax, copies and LDS waits overlap the other's MFMAs):
+//   score waves 0-3: wave w takes rows 16w .. 16w+15 of tile j: S^T = K Q^T
+//       and dP^T = V dO^T sharing the K fragments (K from LDS as the A
+//       operand, the wave's Q and dout rows held in registers as B operands,
+//       36 + 32 MFMA 16x16x32), then P = exp(S - lse), dS = P (dP - delta)
+//       to LDS (and, in the stored-P form, P and scale * dS staged in the
+//       workspace's layout);
+//   dq waves 4-7:    wave 4+c accumulates dq[64 rows, 128c .. 128c+127 and
+//       tail block 512 + 16c] += dS . K for tile j - 1 (K^T through
+//       transposing LDS reads, 36 MFMA), and writes tile j - 1's staged P and
+//       dS out.
+// One barrier per step: every wave waits for its copies, the workgroup syncs,
+// then the copies of tile j + 1 are issued (8 kv rows per dq wave, one tail
+// block per score wave, the masks of tile j + 1 and the row indices of tile
+// j + 2) and the roles work.  delta = rowsum(dout * out) is formed by the
+// score waves from their dout registers in the prologue.
 constexpr int DQ_TILE = 32;
+constexpr int DQ_NW = 8;                 // waves per dq workgroup
+constexpr int SDS = DQ_TILE + 8;         // dS row stride (bf16): 80 bytes, conflict-free reads
 
 template <int H>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
-  constexpr int SDS = DQ_TILE + 8;  // dS row stride (bf16): 80 bytes, conflict-free reads
-  __shared__ __attribute__((aligned(16))) char sK[2][KV32_TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char sDO[GROUP_ROWS * D_V * 2];   // swizzled 64-row tile
-  __shared__ __attribute__((aligned(16))) unsigned short sdS[GROUP_ROWS * SDS];
+  __shared__ __attribute__((aligned(16))) char sK[3][KV32_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned short sdS[2][GROUP_ROWS * SDS];
   __shared__ __attribute__((aligned(16))) unsigned char sMask[2][256];   // token masks (copied as words)
   __shared__ __attribute__((aligned(16))) int sRow[2][64];   // kv row indices of a tile's entries
-  __shared__ float sDelta[GROUP_ROWS];
-  __shared__ float sLse2[GROUP_ROWS];
-  // stored-P form: the tile's P and scale * dS as [entry, {P, dS}, 64 rows]
+  // stored-P form: a tile's P and scale * dS as [entry, {P, dS}, 64 rows]
   // bf16, the layout of the workspace, for one contiguous 8 KB copy out
-  __shared__ __attribute__((aligned(16))) unsigned short sPDS[DQ_TILE * 2 * GROUP_ROWS];
+  __shared__ __attribute__((aligned(16))) unsigned short sPDS[2][DQ_TILE * 2 * GROUP_ROWS];
 
   // The first NU workgroups build the dkv pass's chunk lists (they depend on
   // the plan only, so they run beside the dq work instead of in a launch of
   // their own).
   if ((int64_t)blockIdx.x < a.NU) {
-    dkv_schedule_unit(a, blockIdx.x);
+    dkv_schedule_unit<DQ_NW * 64>(a, blockIdx.x);
     return;
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool score_wave = wv < 4;
+  const int lw = wv & 3;                   // index within the role
   const int g16 = lane >> 4, r16 = lane & 15;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int64_t grp = a.gorder[blockIdx.x - a.NU];
   const int64_t t0 = grp * T;
   const int n_ent = a.qcount[grp];
   const int32_t* erow = a.qrow + grp * a.qcap;
   const uint8_t* emask = a.qmask + grp * a.qcap;
   const int ntiles = (n_ent + DQ_TILE - 1) / DQ_TILE;
-
-  // dout rows of the group (contiguous: token-major, then head) into a
-  // swizzled 64-row tile, 16 row copies per wave; rows past the sequence end
-  // read the zero row.
-  gather_seq_rows<GROUP_ROWS, DO_CHUNKS>(sDO, a.dout + t0 * H * D_V,
-                                         (int)min<int64_t>(GROUP_ROWS, (a.s_q - t0) * H), wv, lane);
-  // Row indices and masks of tile 0 and the row indices of tile 1, in the
-  // same round trip.
-  if (ntiles > 0) {
-    copy_union_entries(sRow[0], sMask[0], erow, emask, 0, n_ent, DQ_TILE, wv, 0, 1, lane);
-    if (ntiles > 1) copy_union_entries(sRow[1], nullptr, erow, emask, DQ_TILE, n_ent, DQ_TILE, wv, 2, 2, lane);
-  }
-  short8_t qf[18];
-  {
-    const int rr = 16 * wave + r16;
-    const int64_t tok = t0 + rr / H;
-    if (tok < a.s_q) {
-      const uint16_t* qrow = a.q + (tok * H + rr % H) * D_K + 8 * g16;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) qf[ks] = ld16_global(qrow + 32 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) qf[ks] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-  // delta = rowsum(dout * out) for the group's 64 rows: 4 threads per row,
-  // thread p of a row takes chunks p, p+4, ... of out (four threads read 64
-  // contiguous bytes per load; all 16 loads are issued at once) and the same
-  // chunks of dout from the LDS tile once its copies have landed.
-  {
-    const int row = tid >> 2, part = tid & 3;
-    const int64_t tok = t0 + row / H;
-    short8_t y[16];
-    float lse_row = 0.f;
-    if (tok < a.s_q) {
-      const int64_t o = (tok * H + row % H) * D_V + 8 * part;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) y[c] = ld16_global(a.out + o + 32 * c);
-      lse_row = a.lse[tok * H + row % H];
-    } else {
-#pragma unroll
-      for (int c = 0; c < 16; ++c) y[c] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
-    }
-    wait_vmcnt0();
-    __syncthreads();   // the dout tile (and the tile-0 indices) are in LDS
-    float d = 0.f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int gc = part + 4 * c;   // 16-byte chunk of the row
-      const short8_t x = ld16_lds(sDO + row * 1024 + 16 * (gc ^ swz_lo(row)));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) d += bf2f((unsigned short)x[j]) * bf2f((unsigned short)y[c][j]);
-    }
-    d += __shfl_xor(d, 1);
-    d += __shfl_xor(d, 2);
-    if (part == 0) {
-      sDelta[row] = d;
-      float l2 = 0.f;
-      if (tok < a.s_q) {
-        a.delta[tok * H + row % H] = d;
-        l2 = lse_row * LOG2E;
-      }
-      sLse2[row] = l2;
-    }
-  }
-  __syncthreads();
-  // Scores and dP are computed transposed (K Q^T, K dO^T): lane (g, r) of
-  // wave w holds row 16w + r of the group and kv entries 16nt + 4g + i.
-  const int tl = (16 * wave + r16) / H;   // group-local token of the lane's row
-  const float del = sDelta[16 * wave + r16];
-  const float ls2 = sLse2[16 * wave + r16];
-
-  float4_t acc[4][9];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
-
-  // kv rows of tile 0 (count entries at rows_t in LDS) into a swizzled
-  // 32-row tile.
-  auto gather = [&](char* kbuf, const int* rows_t, int count) __attribute__((always_inline)) {
-    gather_kv_rows<DQ_TILE, ROW_CHUNKS>(kbuf, a.kv, a.s_kv, rows_t, count, wv, lane);
+  const bool stored = a.pds != nullptr;
+  auto tile_count = [&](int t) __attribute__((always_inline)) {
+    return max(0, min(DQ_TILE, n_ent - t * DQ_TILE));
   };
 
-  auto step = [&](int tile, const char* kt, const unsigned char* mkb, char* knext,
-                  unsigned char* mnext, const int* rnext, int* rcur) __attribute__((always_inline)) {
-    wait_vmcnt0();
-    __syncthreads();
-    // Prefetch into the other buffers (free: every wave has passed the
-    // barrier above, so the previous tile's reads are done): masks of tile+1
-    // and row indices of tile+2 now, the 9 kv copies of tile+1 spread over
-    // the score loop below (after the last tile they read the zero row into
-    // the spare buffer, which nothing reads).
-    const bool pre = tile + 1 < ntiles;
-    if (pre) {
-      copy_union_entries(nullptr, mnext, erow, emask, (tile + 1) * DQ_TILE, n_ent, DQ_TILE, wv, 1, 1,
-                         lane);
-      if (tile + 2 < ntiles)
-        copy_union_entries(rcur, nullptr, erow, emask, (tile + 2) * DQ_TILE, n_ent, DQ_TILE, wv, 2, 2,
-                           lane);
+  // Row indices of tile 0 (wave 5).
+  copy_union_entries(sRow[0], nullptr, erow, emask, 0, n_ent, DQ_TILE, wv, 5, -1, lane);
+
+  // Copies of tile t into sK[t % 3] (its row indices in sRow[t & 1]): the
+  // first 1 KB of rows 8c .. 8c+7 by dq wave 4+c, the tails of rows 8w ..
+  // 8w+7 by score wave w; the masks of tile t (wave 4) and the row indices of
+  // tile t + 1 (wave 5).  Past the union they read the zero row into buffers
+  // no live tile uses.
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const KvGather<DQ_TILE> g = kv_gather_prepare<DQ_TILE>(sK[t % 3], a.kv, a.s_kv, sRow[t & 1],
+                                                           tile_count(t), lw, lane);
+    if (score_wave) {
+      kv_gather_copy<DQ_TILE, DQ_TILE / 4>(g, lw, lane);
+    } else {
+      static_for<DQ_TILE / 4>([&](auto J) __attribute__((always_inline)) {
+        kv_gather_copy<DQ_TILE, decltype(J)::value>(g, lw, lane);
+      });
     }
-    const KvGather<DQ_TILE> gnext = kv_gather_prepare<DQ_TILE>(
-        knext, a.kv, a.s_kv, rnext, pre ? min(DQ_TILE, n_ent - (tile + 1) * DQ_TILE) : 0, wv, lane);
-    float4_t s[2], dp[2];
+    copy_union_entries(nullptr, sMask[t & 1], erow, emask, t * DQ_TILE, n_ent, DQ_TILE, wv, -1, 4, lane);
+    copy_union_entries(sRow[(t + 1) & 1], nullptr, erow, emask, (t + 1) * DQ_TILE, n_ent, DQ_TILE, wv, 5,
+                       -1, lane);
+  };
+
+  if (score_wave) {
+    // Q and dout of row 16w + r as B fragments (k-step ks: columns 32 ks +
+    // 8g .. +7), delta and lse of the row.
+    const int rr = 16 * wv + r16;
+    const int64_t tok = t0 + rr / H;
+    const int tl = rr / H;                 // group-local token of the lane's row
+    short8_t qf[18], df[16];
+    float del, ls2 = 0.f;
+    {
+      short8_t of[16];
+      if (tok < a.s_q) {
+        const int64_t row = tok * H + rr % H;
+        const uint16_t* qp = a.q + row * D_K + 8 * g16;
+        const uint16_t* dp = a.dout + row * D_V + 8 * g16;
+        const uint16_t* op = a.out + row * D_V + 8 * g16;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      s[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
-      dp[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    }
-    // K fragments (and this wave's dout fragments) KPF k-steps ahead of
-    // their MFMAs (a ring of KPF + 1 register sets); the scheduling barriers
-    // keep the reads from sinking onto their uses.
-    constexpr int KPF = 3;
-    short8_t kb[KPF + 1][2], db[KPF + 1];
+        for (int ks = 0; ks < 18; ++ks) qf[ks] = ld16_global(qp + 32 * ks);
 #pragma unroll
-    for (int d = 0; d < KPF; ++d) {
+        for (int ks = 0; ks < 16; ++ks) {
+          df[ks] = ld16_global(dp + 32 * ks);
+          of[ks] = ld16_global(op + 32 * ks);
+        }
+        ls2 = a.lse[row] * LOG2E;
+      } else {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) kb[d][nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * d, lane);
-      db[d] = ld_b_rs<GROUP_ROWS>(sDO, 16 * wave, 32 * d, lane);   // A fragments of dout
-    }
-    static_for<18>([&](auto KS) __attribute__((always_inline)) {
-      constexpr int ks = decltype(KS)::value;
-      constexpr int cur = ks % (KPF + 1), nxt = (ks + KPF) % (KPF + 1);
-      if constexpr (ks + KPF < 18) {
+        for (int ks = 0; ks < 18; ++ks) qf[ks] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) kb[nxt][nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * (ks + KPF), lane);
-        if constexpr (ks + KPF < 16) db[nxt] = ld_b_rs<GROUP_ROWS>(sDO, 16 * wave, 32 * (ks + KPF), lane);
+        for (int ks = 0; ks < 16; ++ks) {
+          df[ks] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
+          of[ks] = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
+        }
       }
-      if constexpr (ks % 2 == 0) kv_gather_copy<DQ_TILE, ks / 2>(gnext, wv, lane);
-      __builtin_amdgcn_sched_barrier(0);
+      // delta = rowsum(dout * out): the lane's 128 columns, then the row's
+      // four lanes (g = 0..3: lanes r, r + 16, r + 32, r + 48).
+      float d = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d += bf2f((unsigned short)df[ks][j]) * bf2f((unsigned short)of[ks][j]);
+      d += __shfl_xor(d, 16);
+      d += __shfl_xor(d, 32);
+      del = d;
+      if (g16 == 0 && tok < a.s_q) a.delta[tok * H + rr % H] = d;
+    }
+    wait_vmcnt0();
+    __syncthreads();   // row indices of tile 0
+    if (ntiles > 0) issue(0);
+
+    for (int j = 0; j <= ntiles; ++j) {
+      wait_vmcnt0();
+      __syncthreads();
+      if (j + 1 < ntiles) issue(j + 1);
+      if (j >= ntiles) continue;
+      // Scores and dP of tile j: lane (g, r) holds kv entries 16 nt + 4g + i.
+      const char* kt = sK[j % 3];
+      const unsigned char* mkb = sMask[j & 1];
+      float4_t s[2], dp[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        s[nt] = mfma_bf16(kb[cur][nt], qf[ks], s[nt]);
-        if constexpr (ks < 16) dp[nt] = mfma_bf16(kb[cur][nt], db[cur], dp[nt]);
+        s[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        dp[nt] = (float4_t){0.f, 0.f, 0.f, 0.f};
       }
-      __builtin_amdgcn_sched_barrier(0);
-    });
+      // K fragments KPF k-steps ahead of their MFMAs.
+      constexpr int KPF = 3;
+      short8_t kb[KPF + 1][2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const unsigned mk = *reinterpret_cast<const unsigned*>(mkb + nt * 16 + 4 * g16);
-      float d[4], pr[4];
+      for (int d = 0; d < KPF; ++d)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool v = (mk >> (8 * i + tl)) & 1u;
-        pr[i] = v ? fast_exp2(s[nt][i] * a.scale_log2 - ls2) : 0.f;
-        d[i] = pr[i] * (dp[nt][i] - del);
-      }
-      uint2 pk;
-      pk.x = pack_bf2(d[0], d[1]);
-      pk.y = pack_bf2(d[2], d[3]);
-      *reinterpret_cast<uint2*>(&sdS[(16 * wave + r16) * SDS + nt * 16 + 4 * g16]) = pk;
-      if (a.pds) {
-        // Stored-P form: P and scale * dS of the lane's row for its four
-        // entries, staged in LDS in the workspace's layout.
-        unsigned short* st = sPDS + (nt * 16 + 4 * g16) * 2 * GROUP_ROWS + 16 * wave + r16;
+        for (int nt = 0; nt < 2; ++nt) kb[d][nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * d, lane);
+      static_for<18>([&](auto KS) __attribute__((always_inline)) {
+        constexpr int ks = decltype(KS)::value;
+        constexpr int cur = ks % (KPF + 1), nxt = (ks + KPF) % (KPF + 1);
+        if constexpr (ks + KPF < 18) {
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) kb[nxt][nt] = ld_b_rs<DQ_TILE>(kt, nt * 16, 32 * (ks + KPF), lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          s[nt] = mfma_bf16(kb[cur][nt], qf[ks], s[nt]);
+          if constexpr (ks < 16) dp[nt] = mfma_bf16(kb[cur][nt], df[ks], dp[nt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      unsigned short* pt = sPDS[j & 1];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const unsigned mk = *reinterpret_cast<const unsigned*>(mkb + nt * 16 + 4 * g16);
+        float d[4], pr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          st[i * 2 * GROUP_ROWS] = f2bf(pr[i]);
-          st[i * 2 * GROUP_ROWS + GROUP_ROWS] = f2bf(d[i] * a.scale);
+          const bool v = (mk >> (8 * i + tl)) & 1u;
+          pr[i] = v ? fast_exp2(s[nt][i] * a.scale_log2 - ls2) : 0.f;
+          d[i] = pr[i] * (dp[nt][i] - del);
+        }
+        uint2 pk;
+        pk.x = pack_bf2(d[0], d[1]);
+        pk.y = pack_bf2(d[2], d[3]);
+        *reinterpret_cast<uint2*>(&sdS[j & 1][rr * SDS + nt * 16 + 4 * g16]) = pk;
+        if (stored) {
+          // P and scale * dS of the lane's row for its four entries, staged
+          // in the workspace's layout.
+          unsigned short* st = pt + (nt * 16 + 4 * g16) * 2 * GROUP_ROWS + rr;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            st[i * 2 * GROUP_ROWS] = f2bf(pr[i]);
+            st[i * 2 * GROUP_ROWS + GROUP_ROWS] = f2bf(d[i] * a.scale);
+          }
         }
       }
     }
+    wait_vmcnt0();
+    __syncthreads();   // (the dq waves stage their results)
     __syncthreads();
-    if (a.pds) {   // the tile's 32 entries x 256 bytes, contiguous in the workspace
-      uint4_t* dst = reinterpret_cast<uint4_t*>(a.pds + (grp * a.qcap + tile * DQ_TILE) * 2 * GROUP_ROWS);
-      const uint4_t* src = reinterpret_cast<const uint4_t*>(sPDS);
+  } else {
+    const int c = lw;                      // column blocks 128c + 16n (n < 8), tail 512 + 16c
+    float4_t acc[4][9];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) dst[tid + 256 * k] = src[tid + 256 * k];
-    }
-    short8_t dsa[4];
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) dsa[rb] = ld16_lds(&sdS[(16 * rb + r16) * SDS + 8 * g16]);
-    // Column blocks n < 8: 128 w + 16 n; block 8: tail columns 512 + 16 w.
-    // The transposed K fragments run two column blocks ahead of their MFMAs.
-    auto kt_frag = [&](int n) __attribute__((always_inline)) {
-      return n < 8 ? ld_bt_rs_lo<DQ_TILE>(kt, 0, 128 * wave + 16 * n, lane)
-                   : ld_bt_rs_hi<DQ_TILE>(kt, 0, D_V + 16 * wave, lane);
-    };
-    constexpr int BPF = 2;
-    short8_t bb[BPF + 1];
-#pragma unroll
-    for (int d = 0; d < BPF; ++d) bb[d] = kt_frag(d);
-#pragma unroll
-    for (int n = 0; n < 9; ++n) {
-      if (n + BPF < 9) bb[(n + BPF) % (BPF + 1)] = kt_frag(n + BPF);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(dsa[rb], bb[n % (BPF + 1)], acc[rb][n]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
+      for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    wait_vmcnt0();
+    __syncthreads();
+    if (ntiles > 0) issue(0);
 
-  if (ntiles > 0) gather(sK[0], sRow[0], min(DQ_TILE, n_ent));   // indices landed before the barrier above
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int b = tile & 1;
-    step(tile, sK[b], sMask[b], sK[b ^ 1], sMask[b ^ 1], sRow[b ^ 1], sRow[b]);
+    for (int j = 0; j <= ntiles; ++j) {
+      wait_vmcnt0();
+      __syncthreads();
+      if (j + 1 < ntiles) issue(j + 1);
+      if (j == 0) continue;
+      const int jj = j - 1;
+      if (stored) {   // tile jj's P and dS: 32 entries x 256 bytes, contiguous in the workspace
+        uint4_t* dst = reinterpret_cast<uint4_t*>(a.pds + (grp * a.qcap + jj * DQ_TILE) * 2 * GROUP_ROWS);
+        const uint4_t* src = reinterpret_cast<const uint4_t*>(sPDS[jj & 1]);
+        const int t4 = tid - 256;   // dq waves' thread index, 0..255
+        dst[t4] = src[t4];
+        dst[t4 + 256] = src[t4 + 256];
+      }
+      // dq += dS . K for tile jj: all 64 rows, the wave's column blocks; the
+      // transposed K fragments run two column blocks ahead of their MFMAs.
+      const char* kt = sK[jj % 3];
+      short8_t dsa[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) dsa[rb] = ld16_lds(&sdS[jj & 1][(16 * rb + r16) * SDS + 8 * g16]);
+      auto kt_frag = [&](int n) __attribute__((always_inline)) {
+        return n < 8 ? ld_bt_rs_lo<DQ_TILE>(kt, 0, 128 * c + 16 * n, lane)
+                     : ld_bt_rs_hi<DQ_TILE>(kt, 0, D_V + 16 * c, lane);
+      };
+      constexpr int BPF = 2;
+      short8_t bb[BPF + 1];
+#pragma unroll
+      for (int d = 0; d < BPF; ++d) bb[d] = kt_frag(d);
+#pragma unroll
+      for (int n = 0; n < 9; ++n) {
+        if (n + BPF < 9) bb[(n + BPF) % (BPF + 1)] = kt_frag(n + BPF);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(dsa[rb], bb[n % (BPF + 1)], acc[rb][n]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // Epilogue: dq = scale * acc, staged through LDS (sK[0] holds rows 0..31,
+    // sK[1] rows 32..63) once every wave is done with the K tiles.
+    wait_vmcnt0();
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      unsigned short* so = reinterpret_cast<unsigned short*>(sK[rb >> 1]);
+#pragma unroll
+      for (int n = 0; n < 9; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          so[(16 * (rb & 1) + 4 * g16 + i) * D_K + (n < 8 ? 128 * c + 16 * n : D_V + 16 * c) + r16] =
+              f2bf(acc[rb][n][i] * a.scale);
+    }
+    __syncthreads();
   }
 
-  // Epilogue: dq = scale * acc, staged through LDS in two halves of 32 rows
-  // (sK[0] holds rows 0..31, sK[1] rows 32..63), then 16-byte stores (the
-  // spare buffer's last copies are drained first).
-  wait_vmcnt0();
-  __syncthreads();
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    unsigned short* so = reinterpret_cast<unsigned short*>(sK[rb >> 1]);
-#pragma unroll
-    for (int n = 0; n < 9; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        so[(16 * (rb & 1) + 4 * g16 + i) * D_K + (n < 8 ? 128 * wave + 16 * n : D_V + 16 * wave) +
-           r16] = f2bf(acc[rb][n][i] * a.scale);
-  }
-  __syncthreads();
-  for (int p = tid; p < GROUP_ROWS * ROW_CHUNKS; p += 256) {
-    const int row = p / ROW_CHUNKS, c = p - row * ROW_CHUNKS;
-    const int64_t tok = t0 + row / H;
+  // dq rows stored with 16-byte writes.
+  for (int p = tid; p < GROUP_ROWS * ROW_CHUNKS; p += DQ_NW * 64) {
+    const int row = p / ROW_CHUNKS, ch = p - row * ROW_CHUNKS;
+    const int64_t tk = t0 + row / H;
     const unsigned short* so = reinterpret_cast<const unsigned short*>(sK[row >> 5]);
-    if (tok < a.s_q)
-      *reinterpret_cast<uint4_t*>(a.dq + (tok * H + row % H) * D_K + 8 * c) =
-          *reinterpret_cast<const uint4_t*>(so + (row & 31) * D_K + 8 * c);
+    if (tk < a.s_q)
+      *reinterpret_cast<uint4_t*>(a.dq + (tk * H + row % H) * D_K + 8 * ch) =
+          *reinterpret_cast<const uint4_t*>(so + (row & 31) * D_K + 8 * ch);
   }
 }
 
@@ -1198,7 +1232,7 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int heads, hipStream_t stream) {
   if (a.G == 0) return hipSuccess;
-  dim3 grid((unsigned)(a.NU + a.G)), block(256);   // NU schedule workgroups, then the groups
+  dim3 grid((unsigned)(a.NU + a.G)), block(DQ_NW * 64);   // NU schedule workgroups, then the groups
   switch (heads) {
     case 8: bwd_dq_kernel<8><<<grid, block, 0, stream>>>(a); break;
     case 16: bwd_dq_kernel<16><<<grid, block, 0, stream>>>(a); break;
