@@ -119,8 +119,8 @@ __global__ __launch_bounds__(256) void dkv_schedule_kernel(BwdArgs a) {
 //       transposing LDS reads, 36 MFMA), and writes tile j - 1's staged P and
 //       dS out.
 // One barrier per step: every wave waits for its copies, the workgroup syncs,
-// then the copies of tile j + 1 are issued (8 kv rows per dq wave, one tail
-// block per score wave, the masks of tile j + 1 and the row indices of tile
+// then the dq waves issue the copies of tile j + 1 (8 kv rows and their
+// tails per dq wave, the masks of tile j + 1 and the row indices of tile
 // j + 2) and the roles work.  delta = rowsum(dout * out) is formed by the
 // score waves from their dout registers in the prologue.
 constexpr int DQ_TILE = 32;
@@ -164,21 +164,17 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
   // Row indices of tile 0 (wave 5).
   copy_union_entries(sRow[0], nullptr, erow, emask, 0, n_ent, DQ_TILE, wv, 5, -1, lane);
 
-  // Copies of tile t into sK[t % 3] (its row indices in sRow[t & 1]): the
-  // first 1 KB of rows 8c .. 8c+7 by dq wave 4+c, the tails of rows 8w ..
-  // 8w+7 by score wave w; the masks of tile t (wave 4) and the row indices of
-  // tile t + 1 (wave 5).  Past the union they read the zero row into buffers
-  // no live tile uses.
+  // Copies of tile t into sK[t % 3] (its row indices in sRow[t & 1]), all by
+  // the dq waves (the score waves carry more of a step's work): dq wave 4+c
+  // copies the first 1 KB of rows 8c .. 8c+7 and their tails; wave 4 the
+  // masks of tile t, wave 5 the row indices of tile t + 1.  Past the union
+  // they read the zero row into buffers no live tile uses.
   auto issue = [&](int t) __attribute__((always_inline)) {
     const KvGather<DQ_TILE> g = kv_gather_prepare<DQ_TILE>(sK[t % 3], a.kv, a.s_kv, sRow[t & 1],
                                                            tile_count(t), lw, lane);
-    if (score_wave) {
-      kv_gather_copy<DQ_TILE, DQ_TILE / 4>(g, lw, lane);
-    } else {
-      static_for<DQ_TILE / 4>([&](auto J) __attribute__((always_inline)) {
-        kv_gather_copy<DQ_TILE, decltype(J)::value>(g, lw, lane);
-      });
-    }
+    static_for<DQ_TILE / 4 + 1>([&](auto J) __attribute__((always_inline)) {
+      kv_gather_copy<DQ_TILE, decltype(J)::value>(g, lw, lane);
+    });
     copy_union_entries(nullptr, sMask[t & 1], erow, emask, t * DQ_TILE, n_ent, DQ_TILE, wv, -1, 4, lane);
     copy_union_entries(sRow[(t + 1) & 1], nullptr, erow, emask, (t + 1) * DQ_TILE, n_ent, DQ_TILE, wv, 5,
                        -1, lane);
@@ -230,12 +226,10 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     }
     wait_vmcnt0();
     __syncthreads();   // row indices of tile 0
-    if (ntiles > 0) issue(0);
 
     for (int j = 0; j <= ntiles; ++j) {
       wait_vmcnt0();
       __syncthreads();
-      if (j + 1 < ntiles) issue(j + 1);
       if (j >= ntiles) continue;
       // Scores and dP of tile j: lane (g, r) holds kv entries 16 nt + 4g + i.
       const char* kt = sK[j % 3];
