@@ -161,8 +161,18 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     return max(0, min(DQ_TILE, n_ent - t * DQ_TILE));
   };
 
-  // Row indices of tile 0 (wave 5).
-  copy_union_entries(sRow[0], nullptr, erow, emask, 0, n_ent, DQ_TILE, wv, 5, -1, lane);
+  // Tile 0 is gathered at once by the dq waves, its row indices read straight
+  // from the union list (so the gather overlaps the score waves' prologue
+  // loads); the masks of tile 0 (wave 4) and the row indices of tile 1
+  // (wave 5) go to LDS.
+  copy_union_entries(nullptr, sMask[0], erow, emask, 0, n_ent, DQ_TILE, wv, -1, 4, lane);
+  copy_union_entries(sRow[1], nullptr, erow, emask, DQ_TILE, n_ent, DQ_TILE, wv, 5, -1, lane);
+  if (!score_wave && ntiles > 0) {
+    const KvGather<DQ_TILE> g = kv_gather_prepare<DQ_TILE>(sK[0], a.kv, a.s_kv, erow, tile_count(0), lw, lane);
+    static_for<DQ_TILE / 4 + 1>([&](auto J) __attribute__((always_inline)) {
+      kv_gather_copy<DQ_TILE, decltype(J)::value>(g, lw, lane);
+    });
+  }
 
   // Copies of tile t into sK[t % 3] (its row indices in sRow[t & 1]), all by
   // the dq waves (the score waves carry more of a step's work): dq wave 4+c
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
       if (g16 == 0 && tok < a.s_q) a.delta[tok * H + rr % H] = d;
     }
     wait_vmcnt0();
-    __syncthreads();   // row indices of tile 0
+    __syncthreads();   // tile 0, its masks and the row indices of tile 1
 
     for (int j = 0; j <= ntiles; ++j) {
       wait_vmcnt0();
@@ -301,7 +311,6 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
       for (int n = 0; n < 9; ++n) acc[rb][n] = (float4_t){0.f, 0.f, 0.f, 0.f};
     wait_vmcnt0();
     __syncthreads();
-    if (ntiles > 0) issue(0);
 
     for (int j = 0; j <= ntiles; ++j) {
       wait_vmcnt0();
