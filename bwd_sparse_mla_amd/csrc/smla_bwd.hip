@@ -115,9 +115,10 @@ __global__ __launch_bounds__(256) void dkv_schedule_kernel(BwdArgs a) {
 //       to LDS (and, in the stored-P form, P and scale * dS staged in the
 //       workspace's layout);
 //   dq waves 4-7:    wave 4+c accumulates dq[64 rows, 128c .. 128c+127 and
-//       tail block 512 + 16c] += dS . K for tile j - 1 (K^T through
-//       transposing LDS reads, 36 MFMA), and writes tile j - 1's staged P and
-//       dS out.
+//       tail block 512 + 16c] += dS . K for tile j - 1 (as dq^T = K^T dS^T,
+//       K^T through transposing LDS reads as the A operand, 36 MFMA), writes
+//       tile j - 1's staged P and dS out, and at the end stores its dq
+//       columns straight from its registers (16-byte row pieces).
 // One barrier per step: every wave waits for its copies, the workgroup syncs,
 // then the dq waves issue the copies of tile j + 1 (8 kv rows and their
 // tails per dq wave, the masks of tile j + 1 and the row indices of tile
@@ -299,11 +300,8 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
-    wait_vmcnt0();
-    __syncthreads();   // (the dq waves stage their results)
-    __syncthreads();
   } else {
-    const int c = lw;                      // column blocks 128c + 16n (n < 8), tail 512 + 16c
+    const int c = lw;   // column pairs 128c + 32m (blocks 2m, 2m + 1), tail block 512 + 16c
     float4_t acc[4][9];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
@@ -325,14 +323,16 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         dst[t4] = src[t4];
         dst[t4 + 256] = src[t4 + 256];
       }
-      // dq += dS . K for tile jj: all 64 rows, the wave's column blocks; the
+      // dq^T += K^T . dS^T for tile jj: all 64 rows, the wave's column blocks
+      // (K^T as the A operand, so a lane's outputs are adjacent columns of one
+      // row: blocks 2m and 2m + 1 together hold 8 adjacent columns); the
       // transposed K fragments run two column blocks ahead of their MFMAs.
       const char* kt = sK[jj % 3];
       short8_t dsa[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) dsa[rb] = ld16_lds(&sdS[jj & 1][(16 * rb + r16) * SDS + 8 * g16]);
       auto kt_frag = [&](int n) __attribute__((always_inline)) {
-        return n < 8 ? ld_bt_rs_lo<DQ_TILE>(kt, 0, 128 * c + 16 * n, lane)
+        return n < 8 ? ld_bt_rs_pair<DQ_TILE>(kt, 0, 128 * c + 32 * (n >> 1), n & 1, lane)
                      : ld_bt_rs_hi<DQ_TILE>(kt, 0, D_V + 16 * c, lane);
       };
       constexpr int BPF = 2;
@@ -344,35 +344,34 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         if (n + BPF < 9) bb[(n + BPF) % (BPF + 1)] = kt_frag(n + BPF);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(dsa[rb], bb[n % (BPF + 1)], acc[rb][n]);
+        for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(bb[n % (BPF + 1)], dsa[rb], acc[rb][n]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // Epilogue: dq = scale * acc, staged through LDS (sK[0] holds rows 0..31,
-    // sK[1] rows 32..63) once every wave is done with the K tiles.
-    wait_vmcnt0();
-    __syncthreads();
+    // Epilogue: dq = scale * acc straight from the registers: lane (g, r)
+    // holds columns 128c + 32m + 8g .. +7 (blocks 2m, 2m + 1) and tail
+    // columns 512 + 16c + 4g .. +3 of rows 16 rb + r.
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      unsigned short* so = reinterpret_cast<unsigned short*>(sK[rb >> 1]);
+      const int row = 16 * rb + r16;
+      const int64_t tk = t0 + row / H;
+      if (tk < a.s_q) {
+        uint16_t* drow = a.dq + (tk * H + row % H) * D_K;
 #pragma unroll
-      for (int n = 0; n < 9; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          so[(16 * (rb & 1) + 4 * g16 + i) * D_K + (n < 8 ? 128 * c + 16 * n : D_V + 16 * c) + r16] =
-              f2bf(acc[rb][n][i] * a.scale);
+        for (int m = 0; m < 4; ++m) {
+          uint4_t v;
+          v[0] = pack_bf2(acc[rb][2 * m][0] * a.scale, acc[rb][2 * m][1] * a.scale);
+          v[1] = pack_bf2(acc[rb][2 * m][2] * a.scale, acc[rb][2 * m][3] * a.scale);
+          v[2] = pack_bf2(acc[rb][2 * m + 1][0] * a.scale, acc[rb][2 * m + 1][1] * a.scale);
+          v[3] = pack_bf2(acc[rb][2 * m + 1][2] * a.scale, acc[rb][2 * m + 1][3] * a.scale);
+          *reinterpret_cast<uint4_t*>(drow + 128 * c + 32 * m + 8 * g16) = v;
+        }
+        uint2 t;
+        t.x = pack_bf2(acc[rb][8][0] * a.scale, acc[rb][8][1] * a.scale);
+        t.y = pack_bf2(acc[rb][8][2] * a.scale, acc[rb][8][3] * a.scale);
+        *reinterpret_cast<uint2*>(drow + D_V + 16 * c + 4 * g16) = t;
+      }
     }
-    __syncthreads();
-  }
-
-  // dq rows stored with 16-byte writes.
-  for (int p = tid; p < GROUP_ROWS * ROW_CHUNKS; p += DQ_NW * 64) {
-    const int row = p / ROW_CHUNKS, ch = p - row * ROW_CHUNKS;
-    const int64_t tk = t0 + row / H;
-    const unsigned short* so = reinterpret_cast<const unsigned short*>(sK[row >> 5]);
-    if (tk < a.s_q)
-      *reinterpret_cast<uint4_t*>(a.dq + (tk * H + row % H) * D_K + 8 * ch) =
-          *reinterpret_cast<const uint4_t*>(so + (row & 31) * D_K + 8 * ch);
   }
 }
 

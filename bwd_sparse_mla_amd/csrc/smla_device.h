@@ -137,6 +137,26 @@ __device__ __forceinline__ short8_t ld_bt_rs_lo(const char* tile, int k0, int n0
   return v;
 }
 
+// Half h (0 or 1) of a pair of column blocks over columns n0 .. n0+31 (n0 a
+// multiple of 32, n0 + 32 <= 512), rows k0 .. k0+31 as the reduction index:
+// lane (g, L) holds rows k0 + 8g .. +7 of column n0 + 8 (L / 4) + 4h + L % 4.
+// As the A operand of an MFMA (rows = these columns), output row 4g + i is
+// column n0 + 8g + 4h + i, so a lane's outputs of the two halves are 8
+// adjacent columns.
+template <int R>
+__device__ __forceinline__ short8_t ld_bt_rs_pair(const char* tile, int k0, int n0, int h, int lane) {
+  const int g = (lane >> 4) & 3, L = lane & 15;
+  const int row = k0 + 8 * g + (L >> 2);
+  const int chunk = (n0 >> 3) + (L & 3);
+  const char* p = tile + 8 * h + 16 * chunk;
+  short4_t lo = ld_tr16(p + row * 1024 + 16 * ((chunk ^ swz_lo(row)) - chunk));
+  short4_t hi = ld_tr16(p + (row + 4) * 1024 + 16 * ((chunk ^ swz_lo(row + 4)) - chunk));
+  short8_t v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return v;
+}
+
 // ld_bt_rs for columns 512..575 only (n0 >= 512): tail addressing.
 template <int R>
 __device__ __forceinline__ short8_t ld_bt_rs_hi(const char* tile, int k0, int n0, int lane) {

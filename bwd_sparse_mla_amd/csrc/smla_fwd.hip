@@ -11,7 +11,9 @@
 //            held in registers as the B operand, 36 MFMA 16x16x32), then the
 //            row softmax, and leaves P (bf16) and the rescale factors in LDS;
 //   PV waves 4-7:    wave 4+c accumulates out[:, 128c .. 128c+127] for all 64
-//            rows from the previous tile's P and V (32 MFMA).
+//            rows from the previous tile's P and V (32 MFMA, as out^T = V^T
+//            P^T so that a lane holds adjacent columns of one row, stored
+//            straight from the registers at the end).
 // Per step every wave waits for the copies it issued two steps before (its
 // copies of the previous step may still be in flight) and the workgroup syncs
 // once; then the copies of tile j+2 are issued (8-9 per PV wave, one per
@@ -315,28 +317,30 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
     if (mv[0] | mv[1] | mv[2] | mv[3]) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = sAlpha[t & 1][16 * rb + 4 * g16 + i];
+        const float al = sAlpha[t & 1][16 * rb + r16];
 #pragma unroll
         for (int n = 0; n < 8; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[rb][n][i] *= al[i];
+          for (int i = 0; i < 4; ++i) acc[rb][n][i] *= al;
       }
     }
     short8_t pa[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) pa[rb] = ld16_lds(&pt[(16 * rb + r16) * SPS + 8 * g16]);
+    // out^T += V^T P^T (V^T as the A operand): lane (g, r) accumulates row
+    // 16 rb + r, columns 128c + 32m + 8g + 4h .. +3 in block n = 2m + h, so
+    // blocks 2m and 2m + 1 hold 8 adjacent columns of one row.
     constexpr int VPF = 2;   // V fragments this many n-tiles ahead
     short8_t vb[VPF + 1];
 #pragma unroll
-    for (int d = 0; d < VPF; ++d) vb[d] = ld_bt_rs_lo<FT>(vt, 0, 128 * c + 16 * d, lane);
+    for (int d = 0; d < VPF; ++d) vb[d] = ld_bt_rs_pair<FT>(vt, 0, 128 * c + 32 * (d >> 1), d & 1, lane);
     static_for<8>([&](auto N) __attribute__((always_inline)) {
       constexpr int n = decltype(N)::value;
-      if constexpr (n + VPF < 8) vb[(n + VPF) % (VPF + 1)] = ld_bt_rs_lo<FT>(vt, 0, 128 * c + 16 * (n + VPF), lane);
+      if constexpr (n + VPF < 8)
+        vb[(n + VPF) % (VPF + 1)] = ld_bt_rs_pair<FT>(vt, 0, 128 * c + 32 * ((n + VPF) >> 1), (n + VPF) & 1, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(pa[rb], vb[n % (VPF + 1)], acc[rb][n]);
+      for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_bf16(vb[n % (VPF + 1)], pa[rb], acc[rb][n]);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -412,9 +416,8 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
     }
   }
 
-  // Epilogue: LSE from the score waves; the PV waves normalise their columns
-  // and stage them through LDS (the tile buffers are free once the last
-  // copies, zero rows past the union, have landed) for 16-byte stores.
+  // Epilogue: LSE from the score waves; the PV waves normalise their rows'
+  // columns and store them straight from their registers (16-byte pieces).
   wait_vmcnt0();
   if (score_wave && (lane_id >> 4) == 0) {
     const int rr = 16 * wv + (lane_id & 15);
@@ -426,28 +429,26 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
     }
   }
   __syncthreads();
-  unsigned short* so = reinterpret_cast<unsigned short*>(&sK[0][0]);  // [64][520]
   if (!score_wave) {
     const int c = wv - 4, g16 = lane_id >> 4, r16 = lane_id & 15;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      float inv[4];
+      const int row = 16 * rb + r16;
+      const int64_t tok = t0 + row / H;
+      const float inv = 1.0f / fmaxf(sL[row], SUMEXP_FLOOR);
+      if (tok < a.s_q) {
+        uint16_t* orow = a.out + (tok * H + row % H) * D_V + 128 * c + 8 * g16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) inv[i] = 1.0f / fmaxf(sL[16 * rb + 4 * g16 + i], SUMEXP_FLOOR);
-#pragma unroll
-      for (int n = 0; n < 8; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          so[(16 * rb + 4 * g16 + i) * 520 + 128 * c + 16 * n + r16] = f2bf(acc[rb][n][i] * inv[i]);
+        for (int m = 0; m < 4; ++m) {
+          uint4_t v;
+          v[0] = pack_bf2(acc[rb][2 * m][0] * inv, acc[rb][2 * m][1] * inv);
+          v[1] = pack_bf2(acc[rb][2 * m][2] * inv, acc[rb][2 * m][3] * inv);
+          v[2] = pack_bf2(acc[rb][2 * m + 1][0] * inv, acc[rb][2 * m + 1][1] * inv);
+          v[3] = pack_bf2(acc[rb][2 * m + 1][2] * inv, acc[rb][2 * m + 1][3] * inv);
+          *reinterpret_cast<uint4_t*>(orow + 32 * m) = v;
+        }
+      }
     }
-  }
-  __syncthreads();
-  for (int p = tid; p < GROUP_ROWS * 64; p += FNW * 64) {
-    const int row = p >> 6, c = p & 63;
-    const int64_t tok = t0 + row / H;
-    if (tok < a.s_q)
-      *reinterpret_cast<uint4_t*>(a.out + (tok * H + row % H) * D_V + 8 * c) =
-          *reinterpret_cast<const uint4_t*>(so + row * 520 + 8 * c);
   }
 }
 
