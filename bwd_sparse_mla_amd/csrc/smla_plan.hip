@@ -49,6 +49,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   __shared__ unsigned xflag[XFLAG_WORDS];    // slots that repeat an earlier slot's row
   __shared__ int scratch[8];
   __shared__ int s_lo, s_hi;
+  __shared__ int s_rep;                      // window check: slots minus distinct rows
 
   const int tid = threadIdx.x;
   const int64_t g = blockIdx.x;
@@ -127,30 +128,58 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   // Windows start on a 64-row block boundary so kv blocks never straddle two.
   for (int w0 = (hi >= 0 ? (lo & ~63) : 1); w0 <= hi; w0 += WIN_BITS) {
     const int qbase0 = qbase;   // union entries before this window
-    for (int i = tid; i < T * WIN_WORDS; i += 256) (&bm[0][0])[i] = 0u;
-    __syncthreads();
-    // PLAN_LOADS index loads in flight per thread before their bitmap updates.
-    for (int s0 = tid; s0 < nslots; s0 += 256 * PLAN_LOADS) {
-      int v[PLAN_LOADS];
+    // Bitmap pass: PLAN_LOADS index loads in flight per thread before their
+    // bitmap updates.  The first pass sets the bits with no-return atomics
+    // and counts the window's valid slots; a token that lists a row twice
+    // leaves fewer bits than slots, and only then does a second pass redo
+    // the window with returning atomics that flag every slot whose row was
+    // already set (the repeats).
+    auto bitmap_pass = [&](auto RTN) __attribute__((always_inline)) {
+      constexpr bool rtn = decltype(RTN)::value;
+      for (int i = tid; i < T * WIN_WORDS; i += 256) (&bm[0][0])[i] = 0u;
+      if (tid == 0) s_rep = 0;
+      __syncthreads();
+      int cnt = 0;
+      for (int s0 = tid; s0 < nslots; s0 += 256 * PLAN_LOADS) {
+        int v[PLAN_LOADS];
 #pragma unroll
-      for (int j = 0; j < PLAN_LOADS; ++j) {
-        const int s = s0 + 256 * j;
-        v[j] = s < nslots ? ix[s] : -1;
-      }
+        for (int j = 0; j < PLAN_LOADS; ++j) {
+          const int s = s0 + 256 * j;
+          v[j] = s < nslots ? ix[s] : -1;
+        }
 #pragma unroll
-      for (int j = 0; j < PLAN_LOADS; ++j) {
-        const int s = s0 + 256 * j;
-        const int m = v[j] >= 0 && v[j] < sidx ? flat_row(v[j], s) : -1;
-        if (m >= w0 && m < w0 + WIN_BITS) {
-          const int t = s / K;
-          const int bit = m - w0;
-          const unsigned m = 1u << (bit & 31);
-          const unsigned old = atomicOr(&bm[t][bit >> 5], m);
-          if (old & m) atomicOr(&xflag[s >> 5], 1u << (s & 31));
+        for (int j = 0; j < PLAN_LOADS; ++j) {
+          const int s = s0 + 256 * j;
+          const int m = v[j] >= 0 && v[j] < sidx ? flat_row(v[j], s) : -1;
+          if (m >= w0 && m < w0 + WIN_BITS) {
+            const int t = s / K;
+            const int bit = m - w0;
+            const unsigned mb = 1u << (bit & 31);
+            if constexpr (rtn) {
+              const unsigned old = atomicOr(&bm[t][bit >> 5], mb);
+              if (old & mb) atomicOr(&xflag[s >> 5], 1u << (s & 31));
+            } else {
+              __hip_atomic_fetch_or(&bm[t][bit >> 5], mb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              ++cnt;
+            }
+          }
         }
       }
+      __syncthreads();
+      return cnt;
+    };
+    {
+      int cnt = bitmap_pass(Int<0>{});
+      for (int i = tid; i < T * WIN_WORDS; i += 256) cnt -= __popc((&bm[0][0])[i]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+      if ((tid & 63) == 0 && cnt != 0) atomicAdd(&s_rep, cnt);
+      __syncthreads();
+      if (s_rep != 0) {   // (uniform) some token lists a row twice in this window
+        __syncthreads();   // every thread has read s_rep before the clear
+        bitmap_pass(Int<1>{});
+      }
     }
-    __syncthreads();
 
     // Union entries, ascending row order.  Thread tid owns bytes tid + 256k
     // (k = 0..7) of the window's bitmap, so a contiguous union spreads over
