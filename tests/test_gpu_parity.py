@@ -128,6 +128,44 @@ def test_maximum_topk(H):
     check_full(w)
 
 
+@pytest.mark.parametrize("stored", [False, True])
+def test_repeats_in_one_planner_window(stored):
+    # The planner sets a window's bitmap bits without reading them back and
+    # redoes only a window whose bit count falls short of its slot count with
+    # returning atomics that flag the repeats.  Here only rows below 16000
+    # repeat (the first of three 16384-row windows), so one window takes the
+    # second pass and the others keep the first.
+    import dataclasses
+    w = synth.custom(S=12, H=16, K=700, S_kv=40000, seed=11, pad_frac=0.2, empty_frac=0.0)
+    idx = w.idx.copy()
+    rng = np.random.default_rng(5)
+    n_rep = 0
+    for s in range(idx.shape[0]):
+        low = np.nonzero((idx[s] >= 0) & (idx[s] < 16000))[0]
+        if s % 3 == 0 and low.size >= 2:
+            a_, b_ = rng.choice(low, size=2, replace=False)
+            idx[s, b_] = idx[s, a_]
+            n_rep += 1
+    assert n_rep > 0
+    w = dataclasses.replace(w, idx=idx, name=w.name + "_rep_window0")
+    print(f"[parity] {w.name} stored={stored}", flush=True)
+    if stored:
+        import bwd_sparse_mla_amd as smla
+        q, kv, dout, gidx = gpu_inputs(w)
+        out, lse = smla.sparse_mla_fwd(q, kv, gidx, w.sm_scale)
+        dq_s, dkv_s = smla.sparse_mla_bwd(q, kv, out, dout, gidx, lse, w.sm_scale, stored_p=True)
+        dq_r, dkv_r = smla.sparse_mla_bwd(q, kv, out, dout, gidx, lse, w.sm_scale, stored_p=False)
+        torch.cuda.synchronize()
+        q64, kv64, do64 = oracle_inputs(w)
+        s_dq, s_dkv = o_bwd(q64, kv64, do64, w.idx, w.sm_scale, out=bf16_to_np64(out),
+                            lse=lse.cpu().numpy().astype(np.float64))
+        for g_dq, g_dkv in ((dq_s, dkv_s), (dq_r, dkv_r)):
+            assert rel_err(bf16_to_np64(g_dq), s_dq) <= TOL
+            assert rel_err(bf16_to_np64(g_dkv), s_dkv) <= TOL
+    else:
+        check_full(w)
+
+
 def test_repeated_indices():
     w = synth.custom(S=30, H=8, K=96, S_kv=80, seed=3, pad_frac=0.2, empty_frac=0.1, dup_frac=0.3)
     assert any(len(set(r[r >= 0].tolist())) < (r >= 0).sum() for r in w.idx)
