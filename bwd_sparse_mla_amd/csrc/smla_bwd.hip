@@ -990,7 +990,7 @@ __global__ __launch_bounds__(256) void dkv_prefix_kernel(BwdArgs a) {
 constexpr int FIN_ROWS = 4;
 constexpr int FIN_PARTS = TILE_KV / FIN_ROWS;   // workgroups per block
 constexpr int FIN_XCAP = 512;   // extra slots listed per pass
-constexpr int FIN_XB = 16;      // extra slots per batch
+constexpr int FIN_XB = 8;       // extra slots per batch
 template <int H>
 __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
   constexpr int T = GROUP_ROWS / H;
@@ -998,8 +998,8 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
   __shared__ int red_i[8];
   __shared__ int scr_i[8];
   __shared__ int64_t sXe[FIN_XCAP];      // listed extra slots (union entry index)
-  __shared__ float sXp[FIN_XB][H];       // P and dS of a batch's extras per head
-  __shared__ float sXd[FIN_XB][H];
+  __shared__ float sXc[FIN_XB][D_K];     // a batch's extras: contribution to their row
+  __shared__ int sXr[FIN_XB];            // and that row's index among the workgroup's rows
   __shared__ unsigned s_xt;              // rows the extras touch
   const int tid = threadIdx.x;
   const int64_t blk = blockIdx.x / FIN_PARTS;
@@ -1034,9 +1034,10 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
     // order.  Thread t scans groups t, t + 256, ... (a group's extras in slot
     // order); one block scan per round of 256 groups keeps the order.  Up to
     // FIN_XCAP matches are listed per pass (another pass takes the next ones),
-    // and handled FIN_XB at a time: first P and dS of every head (one wave
-    // per extra), then every thread adds the batch's terms to its columns in
-    // (extra, head) order.
+    // and handled FIN_XB at a time: one wave per extra forms P and dS of every
+    // head and the extra's contribution to its row, summed over the heads;
+    // then every thread adds the batch's contributions to its columns in
+    // extra order.
     if (tid == 0) s_xt = 0u;
     const int wv = tid >> 6, lane = tid & 63;
     float xa[FIN_ROWS][3];   // the terms of columns tid, tid + 256, tid + 512 (< 576) per row
@@ -1088,66 +1089,80 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
       const int npass = min(FIN_XCAP, seen - n_done);
       for (int b0 = 0; b0 < npass; b0 += FIN_XB) {
         const int nb = min(FIN_XB, npass - b0);
-        for (int e = wv; e < nb; e += 4) {   // P and dS of extra b0 + e, every head
+        // Wave w takes extras w, w + 4, ... of the batch.  Eight heads of the
+        // extra's token at a time: lane 8 hl + j takes head 8 hp + hl and the
+        // 16-byte chunks j + 8 i of its q row (i < 9), dout row (i < 8) and
+        // the kv row; the head's 8 lanes reduce q.k and dout.v, giving P and
+        // scale * dS; then each chunk's terms dS q + P dout are summed over
+        // the 8 heads by lanes 8 apart and added into sXc[e] (head passes in
+        // order, so the sum order is fixed).
+        for (int e = wv; e < nb; e += 4) {
           const int64_t ent = sXe[b0 + e];
           const int64_t row = a.qrow[ent];
           const int64_t g = ent / a.qcap;
           int64_t t = g * T + (__ffs((unsigned)a.qmask[ent]) - 1);
           t = t < 0 ? 0 : (t >= a.s_q ? a.s_q - 1 : t);
-          float kk[9];
-#pragma unroll
-          for (int i = 0; i < 9; ++i) kk[i] = bf2f(a.kv[row * D_K + lane + 64 * i]);
-#pragma unroll 4
-          for (int h = 0; h < H; ++h) {
-            const uint16_t* qr = a.q + (t * H + h) * D_K;
-            const uint16_t* dr = a.dout + (t * H + h) * D_V;
+          if (lane == 0) sXr[e] = (int)(row - r0);
+          const int j = lane & 7, hl = lane >> 3;
+          const uint16_t* kr = a.kv + row * D_K + 8 * j;
+          for (int hp = 0; hp < H / 8; ++hp) {
+            const int h = 8 * hp + hl;
+            const uint16_t* qr = a.q + (t * H + h) * D_K + 8 * j;
+            const uint16_t* dr = a.dout + (t * H + h) * D_V + 8 * j;
+            const float lse2 = a.lse[t * H + h] * LOG2E, dl = a.delta[t * H + h];
             float z = 0.f, dp = 0.f;
+#pragma unroll 3
+            for (int i = 0; i < 9; ++i) {   // (three chunks' loads in flight: the kernel stays within 128 registers)
+              const short8_t kc = ld16_global(kr + 64 * i);
+              const short8_t qc = ld16_global(qr + 64 * i);
+              short8_t dc = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
+              if (i < 8) dc = ld16_global(dr + 64 * i);
 #pragma unroll
-            for (int i = 0; i < 9; ++i) {
-              z += bf2f(qr[lane + 64 * i]) * kk[i];
-              if (i < 8) dp += bf2f(dr[lane + 64 * i]) * kk[i];
+              for (int x = 0; x < 8; ++x) {
+                const float kx = bf2f((unsigned short)kc[x]);
+                z += bf2f((unsigned short)qc[x]) * kx;
+                if (i < 8) dp += bf2f((unsigned short)dc[x]) * kx;
+              }
             }
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
+            for (int o = 1; o < 8; o <<= 1) {
               z += __shfl_xor(z, o);
               dp += __shfl_xor(dp, o);
             }
-            const float pv = fast_exp2(z * a.scale_log2 - a.lse[t * H + h] * LOG2E);
-            if (lane == 0) {
-              sXp[e][h] = pv;
-              sXd[e][h] = pv * (dp - a.delta[t * H + h]) * a.scale;
+            const float pv = fast_exp2(z * a.scale_log2 - lse2);
+            const float dsv = pv * (dp - dl) * a.scale;
+#pragma unroll 3
+            for (int i = 0; i < 9; ++i) {
+              const short8_t qc = ld16_global(qr + 64 * i);
+              short8_t dc = (short8_t){0, 0, 0, 0, 0, 0, 0, 0};
+              if (i < 8) dc = ld16_global(dr + 64 * i);
+              float cv[8];
+#pragma unroll
+              for (int x = 0; x < 8; ++x) {
+                cv[x] = dsv * bf2f((unsigned short)qc[x]);
+                if (i < 8) cv[x] += pv * bf2f((unsigned short)dc[x]);
+              }
+#pragma unroll
+              for (int o = 8; o < 64; o <<= 1)
+#pragma unroll
+                for (int x = 0; x < 8; ++x) cv[x] += __shfl_xor(cv[x], o);
+              if (hl == 0) {
+                float* dst = &sXc[e][8 * (j + 8 * i)];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) dst[x] = hp == 0 ? cv[x] : dst[x] + cv[x];
+              }
             }
           }
         }
         __syncthreads();
-        for (int e = 0; e < nb; ++e) {   // the batch's terms, in (extra, head) order
-          const int64_t ent = sXe[b0 + e];
-          const int rl = (int)(a.qrow[ent] - r0);
-          const int64_t g = ent / a.qcap;
-          int64_t t = g * T + (__ffs((unsigned)a.qmask[ent]) - 1);
-          t = t < 0 ? 0 : (t >= a.s_q ? a.s_q - 1 : t);
-          float v[3] = {0.f, 0.f, 0.f};
-#pragma unroll 8
-          for (int h = 0; h < H; ++h) {
-            const uint16_t* qr = a.q + (t * H + h) * D_K;
-            const uint16_t* dr = a.dout + (t * H + h) * D_V;
-            const float pv = sXp[e][h], dsv = sXd[e][h];
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-              const int c = tid + 256 * k;
-              if (c < D_K) {
-                float x = dsv * bf2f(qr[c]);
-                if (c < D_V) x += pv * bf2f(dr[c]);
-                v[k] += x;
-              }
-            }
-          }
-          // (per extra: its heads' terms summed first, then added to the row)
+        for (int e = 0; e < nb; ++e) {   // the batch's terms, in extra order
+          const int rl = sXr[e];
 #pragma unroll
           for (int r = 0; r < FIN_ROWS; ++r)
             if (rl == r)
 #pragma unroll
-              for (int k = 0; k < 3; ++k) xa[r][k] += v[k];
+              for (int k = 0; k < 3; ++k)
+                if (tid + 256 * k < D_K) xa[r][k] += sXc[e][tid + 256 * k];
         }
         __syncthreads();
       }

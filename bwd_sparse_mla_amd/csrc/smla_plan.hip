@@ -257,33 +257,59 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     for (int w = tid; w < nxw; w += 256) anyx |= (xflag[w] != 0u);
     if (__syncthreads_or(anyx)) {
       const int wv = tid >> 6, lane = tid & 63;
-      for (int w = wv; w < nxw; w += 4) {
-        unsigned f = __builtin_amdgcn_readfirstlane(xflag[w]);
-        while (f) {
-          const int b = __ffs(f) - 1;
-          f &= f - 1;
-          const int s = 32 * w + b;
-          const int t = s / K, k = s - t * K;
-          const int32_t* row = ix + (int64_t)t * K;
-          const int v = __builtin_amdgcn_readfirstlane(row[k]);
-          bool earlier = false;
-          for (int i0 = 0; i0 < k && !earlier; i0 += 64) {
-            const int i = i0 + lane;
-            earlier = __ballot(i < k && row[i] == v) != 0ull;
-          }
-          if (earlier) continue;
-          int later = -1;
-          for (int i0 = k + 1; i0 < K && later < 0; i0 += 64) {
-            const int i = i0 + lane;
-            const int si = t * K + i;
-            const bool hit = i < K && row[i] == v && !((xflag[si >> 5] >> (si & 31)) & 1u);
-            const unsigned long long bal = __ballot(hit);
-            if (bal) later = i0 + __ffsll((long long)bal) - 1;
-          }
-          if (lane == 0 && later >= 0) {
-            const int sx = t * K + later;
-            atomicOr(&xflag[sx >> 5], 1u << (sx & 31));
-            atomicAnd(&xflag[w], ~(1u << b));
+      // A wave reads 64 flag words at once and visits the nonzero ones.
+      for (int w0 = 64 * wv; w0 < nxw; w0 += 256) {
+        const unsigned fw = w0 + lane < nxw ? xflag[w0 + lane] : 0u;
+        unsigned long long nz = __ballot(fw != 0u);
+        while (nz) {
+          const int wl = __ffsll((long long)nz) - 1;
+          nz &= nz - 1;
+          const int w = w0 + wl;
+          unsigned f = (unsigned)__builtin_amdgcn_readlane((int)fw, wl);
+          while (f) {
+            const int b = __ffs(f) - 1;
+            f &= f - 1;
+            const int s = 32 * w + b;
+            const int t = s / K, k = s - t * K;
+            const int32_t* row = ix + (int64_t)t * K;
+            const int v = __builtin_amdgcn_readfirstlane(row[k]);
+            // The row is scanned 512 slots per round (eight loads in flight per
+            // lane), not 64: each round is one memory round trip.
+            bool earlier = false;
+            for (int i0 = 0; i0 < k && !earlier; i0 += 512) {
+              int rv[8];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const int i = i0 + lane + 64 * j;
+                rv[j] = i < k ? row[i] : ~v;
+              }
+              bool hit = false;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) hit |= rv[j] == v;
+              earlier = __ballot(hit) != 0ull;
+            }
+            if (earlier) continue;
+            int later = -1;
+            for (int i0 = k + 1; i0 < K && later < 0; i0 += 512) {
+              int rv[8];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const int i = i0 + lane + 64 * j;
+                rv[j] = i < K ? row[i] : ~v;
+              }
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {   // in slot order: the first unflagged match
+                const int si = min(t * K + i0 + lane + 64 * j, nslots - 1);   // (past the row: no hit)
+                const bool hit = rv[j] == v && !((xflag[si >> 5] >> (si & 31)) & 1u);
+                const unsigned long long bal = __ballot(hit);
+                if (bal && later < 0) later = i0 + 64 * j + __ffsll((long long)bal) - 1;
+              }
+            }
+            if (lane == 0 && later >= 0) {
+              const int sx = t * K + later;
+              atomicOr(&xflag[sx >> 5], 1u << (sx & 31));
+              atomicAnd(&xflag[w], ~(1u << b));
+            }
           }
         }
       }
