@@ -205,7 +205,7 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         const int64_t row = tok * H + rr % H;
         const uint16_t* qp = a.q + row * D_K + 8 * g16;
         const uint16_t* dp = a.dout + row * D_V + 8 * g16;
-        const uint16_t* op = a.out + row * D_V + 8 * g16;
+        const uint16_t* op = a.out + (caller_token(tok, a.pair_s, a.pair_g) * H + rr % H) * D_V + 8 * g16;
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks) qf[ks] = ld16_global(qp + 32 * ks);
 #pragma unroll
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
       const int row = 16 * rb + r16;
       const int64_t tk = t0 + row / H;
       if (tk < a.s_q) {
-        uint16_t* drow = a.dq + (tk * H + row % H) * D_K;
+        uint16_t* drow = a.dq + (caller_token(tk, a.pair_s, a.pair_g) * H + row % H) * D_K;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           uint4_t v;

@@ -62,17 +62,19 @@ KernelShape kernel_shape(int64_t s_q, int64_t s_kv, int heads, int kv_groups) {
   return {r, s_kv * kv_groups, hg, 0};
 }
 
-// Group-major staging: with G > 1 kv groups and fewer than 64 heads per
-// group, a 64-row query group of token-major rows would hold rows of several
-// kv groups (disjoint kv rows, each masked for the others).  q, out, dout,
-// lse and the indices are then permuted into the workspace in group-major
-// order (row block g S + s holds token s's heads of group g), the kernels run
-// on those, and out, lse and dq are permuted back.  The staging area leads
-// the workspace; the plan's layout follows it.
+// Group-major order: with G > 1 kv groups and fewer than 64 heads per group,
+// a 64-row query group of token-major rows would hold rows of several kv
+// groups (disjoint kv rows, each masked for the others).  The kernels then
+// walk (group, token) pairs in group-major order (pair g S + s holds token
+// s's heads of group g): the forward reads q and writes out and lse at the
+// caller's token-major rows directly, the dq pass reads out and writes dq
+// there too, and the indices and the backward's q, dout and lse (which the
+// dkv pass reads as contiguous runs of rows) are permuted into the workspace.
+// The staging area leads the workspace; the plan's layout follows it.
 struct Stage {
   bool on = false;
   int hg = 0;
-  size_t q = 0, out = 0, dout = 0, lse = 0, dq = 0, idx = 0, bytes = 0;
+  size_t q = 0, dout = 0, lse = 0, idx = 0, bytes = 0;
 };
 Stage make_stage(int64_t s_q, int heads, int kv_groups, int topk) {
   Stage st;
@@ -82,10 +84,8 @@ Stage make_stage(int64_t s_q, int heads, int kv_groups, int topk) {
   const size_t rows = (size_t)s_q * heads;
   size_t o = 0;
   st.q = o;    o = align256(o + rows * 576 * 2);
-  st.out = o;  o = align256(o + rows * 512 * 2);
   st.dout = o; o = align256(o + rows * 512 * 2);
   st.lse = o;  o = align256(o + rows * 4);
-  st.dq = o;   o = align256(o + rows * 576 * 2);
   st.idx = o;  o = align256(o + (size_t)s_q * kv_groups * topk * 4);
   st.bytes = o;
   return st;
@@ -391,20 +391,12 @@ static int fwd_impl(const void* q, const void* kv, const uint8_t* kv8, const int
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   char* ws = base + sg.bytes;
-  void* out_u = out;     // the caller's out / lse (token-major)
-  float* lse_u = lse;
-  if (sg.on) {   // group-major copies of q (and the indices, unless planned)
-    const int64_t qb = (int64_t)sg.hg * 576 * 2;
-    if ((st = hip_status(launch_permute_pairs(q, base + sg.q, s_tok, kv_groups, qb, true, s), "permute")))
-      return st;
+  if (sg.on) {   // group-major copies of the indices (unless planned)
     if (!(flags & SMLA_PLAN_READY) &&
         (st = hip_status(launch_permute_pairs(indices, base + sg.idx, s_tok, kv_groups,
                                               (int64_t)topk * 4, true, s), "permute")))
       return st;
-    q = base + sg.q;
     indices = reinterpret_cast<const int32_t*>(base + sg.idx);
-    out = base + sg.out;
-    lse = reinterpret_cast<float*>(base + sg.lse);
   }
   const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups,
                                 sg.on ? s_tok : 0, ws, false);
@@ -425,19 +417,15 @@ static int fwd_impl(const void* q, const void* kv, const uint8_t* kv8, const int
   fa.order = reinterpret_cast<int*>(ws + p.off_gorder);
   fa.out = static_cast<uint16_t*>(out);
   fa.lse = lse;
+  fa.pair_s = s_tok;
+  fa.pair_g = sg.on ? kv_groups : 1;
   if (kv8) {
     const int mode = (flags & SMLA_FP8_POW2_SCALES) ? 2 : 1;
     st = hip_status(timed("fwd_fp8", s, [&] { return launch_fwd(fa, heads, s, mode); }), "fwd_fp8");
   } else {
     st = hip_status(timed("fwd", s, [&] { return launch_fwd(fa, heads, s); }), "fwd");
   }
-  if (st || !sg.on) return st;
-  // out and lse back to token-major order
-  if ((st = hip_status(launch_permute_pairs(out, out_u, s_tok, kv_groups, (int64_t)sg.hg * 512 * 2,
-                                            false, s), "permute")))
-    return st;
-  return hip_status(launch_permute_pairs(lse, lse_u, s_tok, kv_groups, (int64_t)sg.hg * 4, false, s),
-                    "permute");
+  return st;
 }
 
 extern "C" {
@@ -537,11 +525,10 @@ int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   char* ws = base + sg.bytes;
-  void* dq_u = dq;   // the caller's dq (token-major)
-  if (sg.on) {   // group-major copies of q, out, dout, lse (and the indices, unless planned)
+  if (sg.on) {   // group-major copies of q, dout, lse (and the indices, unless planned)
     const int64_t qb = (int64_t)sg.hg * 576 * 2, ob = (int64_t)sg.hg * 512 * 2;
     const struct { const void* src; size_t off; int64_t bytes; } cp[] = {
-        {q, sg.q, qb}, {out, sg.out, ob}, {dout, sg.dout, ob}, {lse, sg.lse, (int64_t)sg.hg * 4}};
+        {q, sg.q, qb}, {dout, sg.dout, ob}, {lse, sg.lse, (int64_t)sg.hg * 4}};
     for (const auto& c : cp)
       if ((st = hip_status(launch_permute_pairs(c.src, base + c.off, s_tok, kv_groups, c.bytes, true, s),
                            "permute")))
@@ -551,11 +538,9 @@ int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
                                               (int64_t)topk * 4, true, s), "permute")))
       return st;
     q = base + sg.q;
-    out = base + sg.out;
     dout = base + sg.dout;
     lse = reinterpret_cast<const float*>(base + sg.lse);
     indices = reinterpret_cast<const int32_t*>(base + sg.idx);
-    dq = base + sg.dq;
   }
 
   const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups,
@@ -601,6 +586,8 @@ int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
   ba.cmask = stored_p ? reinterpret_cast<unsigned long long*>(ws + p.off_cmask) : nullptr;
   ba.pds = stored_p ? reinterpret_cast<uint16_t*>(ws + p.off_pds) : nullptr;
   ba.dq = static_cast<uint16_t*>(dq);
+  ba.pair_s = s_tok;
+  ba.pair_g = sg.on ? kv_groups : 1;
   ba.dkv = static_cast<uint16_t*>(dkv);
   ba.dkv_f32 = dkv_f32;
   ba.accumulate = (flags & SMLA_DKV_ACCUMULATE) ? 1 : 0;
@@ -613,10 +600,7 @@ int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
   if ((st = hip_status(timed("bwd_dkv", s, [&] { return launch_bwd_dkv(ba, heads, s); }), "bwd_dkv"))) return st;
   if ((st = hip_status(timed("dkv_finalize", s, [&] { return launch_dkv_finalize(ba, heads, s); }), "dkv_finalize")))
     return st;
-  if (!sg.on) return SMLA_OK;
-  // dq back to token-major order
-  return hip_status(launch_permute_pairs(dq, dq_u, s_tok, kv_groups, (int64_t)sg.hg * 576 * 2, false, s),
-                    "permute");
+  return SMLA_OK;
 }
 
 int smla_bwd(const void* q, const void* kv, const void* out, const void* dout,

@@ -534,6 +534,14 @@ __device__ __forceinline__ void seq_gather_copy(char* tile, const uint16_t* firs
 // Bytes of swizzled tiles.
 constexpr int KV64_TILE_BYTES = 64 * D_K * 2;   // 73728
 constexpr int KV32_TILE_BYTES = 32 * D_K * 2;   // 36864
+
+// The caller's token of a kernel token.  With several kv groups (G > 1) the
+// kernels walk (group, token) pairs in group-major order, tok = g S + s, so
+// that a query group holds one kv group's rows; the caller's rows are
+// token-major, pair (s, g) at s G + g.  With one group the orders coincide.
+__device__ __forceinline__ int64_t caller_token(int64_t tok, int64_t S, int G) {
+  return G > 1 ? (tok % S) * G + tok / S : tok;
+}
 constexpr int DO32_TILE_BYTES = 32 * D_V * 2;   // 32768
 
 // Copies `tile_rows` entries [first, first + tile_rows) of a query group's

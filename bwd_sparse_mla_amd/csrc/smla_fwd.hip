@@ -111,7 +111,7 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
     const int rr = 16 * wv + r16;
     const int64_t tok = t0 + rr / H;
     if (tok < a.s_q) {
-      const uint16_t* qrow = a.q + (tok * H + rr % H) * D_K + 8 * g16;
+      const uint16_t* qrow = a.q + (caller_token(tok, a.pair_s, a.pair_g) * H + rr % H) * D_K + 8 * g16;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks)
         acc[ks >> 3][ks & 7] = __builtin_bit_cast(float4_t, ld16_global(qrow + 32 * ks));
@@ -425,7 +425,8 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
     const int64_t tok = t0 + rr / H;
     if (tok < a.s_q) {
       const float m_eff = lsum > 0.f ? m_run : 0.f;
-      a.lse[tok * H + rr % H] = (m_eff + fast_log2(fmaxf(lsum, SUMEXP_FLOOR))) * LN2;
+      a.lse[caller_token(tok, a.pair_s, a.pair_g) * H + rr % H] =
+          (m_eff + fast_log2(fmaxf(lsum, SUMEXP_FLOOR))) * LN2;
     }
   }
   __syncthreads();
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(FNW * 64, 1) void fwd_kernel(FwdArgs a) {
       const int64_t tok = t0 + row / H;
       const float inv = 1.0f / fmaxf(sL[row], SUMEXP_FLOOR);
       if (tok < a.s_q) {
-        uint16_t* orow = a.out + (tok * H + row % H) * D_V + 128 * c + 8 * g16;
+        uint16_t* orow = a.out + (caller_token(tok, a.pair_s, a.pair_g) * H + row % H) * D_V + 128 * c + 8 * g16;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           uint4_t v;

@@ -85,6 +85,11 @@ struct FwdArgs {
   const int* order;   // [G] groups by decreasing union size: workgroup i runs order[i]
   uint16_t* out;
   float* lse;
+  // Several kv groups (pair_g > 1): the kernel's token tok is the (group,
+  // token) pair g pair_s + s, and q, out and lse are the caller's token-major
+  // rows (see caller_token).
+  int64_t pair_s;
+  int pair_g;
 };
 
 struct BwdArgs {
@@ -106,6 +111,10 @@ struct BwdArgs {
   const int2* ktab;
   const unsigned long long* krmask;
   const int* gorder;  // [G] groups by decreasing union size (dq pass)
+  // Several kv groups (pair_g > 1): out and dq are the caller's token-major
+  // rows (see caller_token); q, dout and lse are group-major copies.
+  int64_t pair_s;
+  int pair_g;
   int* spre;          // [NU + 1] dkv sub-chunks before each unit (exclusive prefix; [NU] = total)
   int* wstart;        // [DKV_WGS] first dkv unit of each dkv workgroup's range
   float* delta;       // [s_q * H] rowsum(dout * out), written by the dq pass
