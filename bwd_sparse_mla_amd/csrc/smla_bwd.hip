@@ -202,10 +202,11 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     {
       short8_t of[16];
       if (tok < a.s_q) {
-        const int64_t row = tok * H + rr % H;
-        const uint16_t* qp = a.q + row * D_K + 8 * g16;
-        const uint16_t* dp = a.dout + row * D_V + 8 * g16;
-        const uint16_t* op = a.out + (caller_token(tok, a.pair_s, a.pair_g) * H + rr % H) * D_V + 8 * g16;
+        const int64_t row = tok * H + rr % H;                                        // lse (group-major)
+        const int64_t crw = caller_token(tok, a.pair_s, a.pair_g) * H + rr % H;   // q, dout, out
+        const uint16_t* qp = a.q + crw * D_K + 8 * g16;
+        const uint16_t* dp = a.dout + crw * D_V + 8 * g16;
+        const uint16_t* op = a.out + crw * D_V + 8 * g16;
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks) qf[ks] = ld16_global(qp + 32 * ks);
 #pragma unroll
@@ -492,8 +493,8 @@ __device__ __forceinline__ void dkv_segment(const BwdArgs& a, int64_t blk, int u
       int64_t nrow0;
       int nvalid;
       rows_of(cen, u + 1, nrow0, nvalid);
-      gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW>(nq, a.q + nrow0 * D_K, nvalid, wv, lane);
-      gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW>(nd, a.dout + nrow0 * D_V, nvalid, wv, lane);
+      gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW, H>(nq, a.q, nrow0, nvalid, a.pair_s, a.pair_g, wv, lane);
+      gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW, H>(nd, a.dout, nrow0, nvalid, a.pair_s, a.pair_g, wv, lane);
       small_copy(cen, nrow0, nm, nl, ne, lane);
     }
     int lane = lane_id;
@@ -604,8 +605,8 @@ __device__ __forceinline__ void dkv_segment(const BwdArgs& a, int64_t blk, int u
     int64_t row0;
     int nvalid;
     rows_of(ce_cur, u0, row0, nvalid);
-    gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW>(sQ[0], a.q + row0 * D_K, nvalid, wv, lane_id);
-    gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW>(sD[0], a.dout + row0 * D_V, nvalid, wv, lane_id);
+    gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW, H>(sQ[0], a.q, row0, nvalid, a.pair_s, a.pair_g, wv, lane_id);
+    gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW, H>(sD[0], a.dout, row0, nvalid, a.pair_s, a.pair_g, wv, lane_id);
     small_copy(ce_cur, row0, sM[0], sL[0], sE[0], lane_id);
   }
   for (int u = u0; u < u1; ++u) {
@@ -730,8 +731,8 @@ __device__ __forceinline__ void dkv_segment_pair(const BwdArgs& a, int64_t unit,
   auto copies = [&](int g, int u, char* nq, char* nd, int lane) __attribute__((always_inline)) {
     const int64_t row0 = (int64_t)g * GROUP_ROWS + DKV_SUB * (u & 1);
     const int nvalid = (int)max((int64_t)0, min((int64_t)DKV_SUB, qrows - row0));
-    gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW>(nq, a.q + row0 * D_K, nvalid, wv, lane);
-    gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW>(nd, a.dout + row0 * D_V, nvalid, wv, lane);
+    gather_seq_rows_nw<DKV_SUB, ROW_CHUNKS, DKV_NW, H>(nq, a.q, row0, nvalid, a.pair_s, a.pair_g, wv, lane);
+    gather_seq_rows_nw<DKV_SUB, DO_CHUNKS, DKV_NW, H>(nd, a.dout, row0, nvalid, a.pair_s, a.pair_g, wv, lane);
   };
 
   copies(c_cur.g, u0, sQ[0], sD[0], lane_id);
@@ -1107,8 +1108,9 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
           const uint16_t* kr = a.kv + row * D_K + 8 * j;
           for (int hp = 0; hp < H / 8; ++hp) {
             const int h = 8 * hp + hl;
-            const uint16_t* qr = a.q + (t * H + h) * D_K + 8 * j;
-            const uint16_t* dr = a.dout + (t * H + h) * D_V + 8 * j;
+            const int64_t ct = caller_token(t, a.pair_s, a.pair_g);
+            const uint16_t* qr = a.q + (ct * H + h) * D_K + 8 * j;
+            const uint16_t* dr = a.dout + (ct * H + h) * D_V + 8 * j;
             const float lse2 = a.lse[t * H + h] * LOG2E, dl = a.delta[t * H + h];
             float z = 0.f, dp = 0.f;
 #pragma unroll 3

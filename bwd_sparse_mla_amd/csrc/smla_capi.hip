@@ -66,15 +66,14 @@ KernelShape kernel_shape(int64_t s_q, int64_t s_kv, int heads, int kv_groups) {
 // a 64-row query group of token-major rows would hold rows of several kv
 // groups (disjoint kv rows, each masked for the others).  The kernels then
 // walk (group, token) pairs in group-major order (pair g S + s holds token
-// s's heads of group g): the forward reads q and writes out and lse at the
-// caller's token-major rows directly, the dq pass reads out and writes dq
-// there too, and the indices and the backward's q, dout and lse (which the
-// dkv pass reads as contiguous runs of rows) are permuted into the workspace.
-// The staging area leads the workspace; the plan's layout follows it.
+// s's heads of group g) and read and write q, out, dout, dq and the forward's
+// lse at the caller's token-major rows (caller_token); the indices and the
+// backward's lse are permuted into the workspace.  The staging area leads
+// the workspace; the plan's layout follows it.
 struct Stage {
   bool on = false;
   int hg = 0;
-  size_t q = 0, dout = 0, lse = 0, idx = 0, bytes = 0;
+  size_t lse = 0, idx = 0, bytes = 0;
 };
 Stage make_stage(int64_t s_q, int heads, int kv_groups, int topk) {
   Stage st;
@@ -83,8 +82,6 @@ Stage make_stage(int64_t s_q, int heads, int kv_groups, int topk) {
   st.on = true;
   const size_t rows = (size_t)s_q * heads;
   size_t o = 0;
-  st.q = o;    o = align256(o + rows * 576 * 2);
-  st.dout = o; o = align256(o + rows * 512 * 2);
   st.lse = o;  o = align256(o + rows * 4);
   st.idx = o;  o = align256(o + (size_t)s_q * kv_groups * topk * 4);
   st.bytes = o;
@@ -525,20 +522,14 @@ int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   char* ws = base + sg.bytes;
-  if (sg.on) {   // group-major copies of q, dout, lse (and the indices, unless planned)
-    const int64_t qb = (int64_t)sg.hg * 576 * 2, ob = (int64_t)sg.hg * 512 * 2;
-    const struct { const void* src; size_t off; int64_t bytes; } cp[] = {
-        {q, sg.q, qb}, {dout, sg.dout, ob}, {lse, sg.lse, (int64_t)sg.hg * 4}};
-    for (const auto& c : cp)
-      if ((st = hip_status(launch_permute_pairs(c.src, base + c.off, s_tok, kv_groups, c.bytes, true, s),
-                           "permute")))
-        return st;
+  if (sg.on) {   // group-major copies of lse (and the indices, unless planned)
+    if ((st = hip_status(launch_permute_pairs(lse, base + sg.lse, s_tok, kv_groups, (int64_t)sg.hg * 4, true, s),
+                         "permute")))
+      return st;
     if (!(flags & SMLA_PLAN_READY) &&
         (st = hip_status(launch_permute_pairs(indices, base + sg.idx, s_tok, kv_groups,
                                               (int64_t)topk * 4, true, s), "permute")))
       return st;
-    q = base + sg.q;
-    dout = base + sg.dout;
     lse = reinterpret_cast<const float*>(base + sg.lse);
     indices = reinterpret_cast<const int32_t*>(base + sg.idx);
   }

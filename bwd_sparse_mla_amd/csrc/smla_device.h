@@ -421,26 +421,47 @@ __device__ __forceinline__ void gather_kv_rows_nw(char* tile, const uint16_t* kv
   }
 }
 
-// gather_seq_rows for a workgroup of NW waves: wave wv copies rows
+// The caller's token of a kernel token.  With several kv groups (G > 1) the
+// kernels walk (group, token) pairs in group-major order, tok = g S + s, so
+// that a query group holds one kv group's rows; the caller's rows are
+// token-major, pair (s, g) at s G + g.  With one group the orders coincide.
+// (Pairs number below 2^31: s_q < 2^24 tokens, G <= 64.)
+__device__ __forceinline__ int64_t caller_token(int64_t tok, int64_t S, int G) {
+  if (G <= 1) return tok;
+  const uint32_t t = (uint32_t)tok, s = (uint32_t)S;
+  const uint32_t g = t / s;
+  return (int64_t)(t - g * s) * G + g;
+}
+
+// gather_seq_rows for a workgroup of NW waves over the kernel rows row0 ..
+// row0 + nvalid - 1 of a tensor with H rows per token whose caller rows follow
+// caller_token (S tokens per kv group, G groups): wave wv copies rows
 // R/NW * wv .. +R/NW-1 and, for wv < R/8, the tails of rows 8 wv .. 8 wv + 7.
-template <int R, int CH, int NW>
-__device__ __forceinline__ void gather_seq_rows_nw(char* tile, const uint16_t* first, int nvalid,
-                                                   int wv, int lane) {
+// (Each of those runs lies in one token: H is a multiple of R/NW and of 8.)
+template <int R, int CH, int NW, int H>
+__device__ __forceinline__ void gather_seq_rows_nw(char* tile, const uint16_t* src0, int64_t row0, int nvalid,
+                                                   int64_t S, int G, int wv, int lane) {
   constexpr int PER = R / NW;
   constexpr int W = CH * 8;  // elements per row
+  static_assert(H % PER == 0 && H % 8 == 0, "a wave's rows must lie in one token");
   const uint32_t base = lds_offset(tile);
+  auto crow = [&](int64_t p) __attribute__((always_inline)) {   // caller row of kernel row p
+    return caller_token(p / H, S, G) * H + p % H;
+  };
+  const uint16_t* first = src0 + crow(row0 + PER * wv) * W;   // the wave's rows PER wv ..
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int r = PER * wv + i;
     const bool ok = r < nvalid;
-    const uint16_t* src = (ok ? first : g_zero_row) + (uint32_t)(ok ? r : 0) * (uint32_t)W;
+    const uint16_t* src = (ok ? first : g_zero_row) + (uint32_t)(ok ? i : 0) * (uint32_t)W;
     g2lds16_s(src, 16u * (uint32_t)(lane ^ swz_lo(r)), base + 1024u * (uint32_t)r);
   }
   if constexpr (CH == ROW_CHUNKS) {
     if (wv < R / 8) {
+      const uint16_t* tfirst = src0 + crow(row0 + 8 * wv) * W;   // rows 8 wv .. 8 wv + 7
       const int r = 8 * wv + (lane >> 3);
       const bool ok = r < nvalid;
-      const uint16_t* src = (ok ? first + (uint32_t)r * (uint32_t)W : g_zero_row) + D_V +
+      const uint16_t* src = (ok ? tfirst + (uint32_t)(lane >> 3) * (uint32_t)W : g_zero_row) + D_V +
                             8 * ((lane & 7) ^ swz_hi(r));
       g2lds16_u(src, base + (uint32_t)(R * 1024 + 1024 * wv));
     }
@@ -535,13 +556,6 @@ __device__ __forceinline__ void seq_gather_copy(char* tile, const uint16_t* firs
 constexpr int KV64_TILE_BYTES = 64 * D_K * 2;   // 73728
 constexpr int KV32_TILE_BYTES = 32 * D_K * 2;   // 36864
 
-// The caller's token of a kernel token.  With several kv groups (G > 1) the
-// kernels walk (group, token) pairs in group-major order, tok = g S + s, so
-// that a query group holds one kv group's rows; the caller's rows are
-// token-major, pair (s, g) at s G + g.  With one group the orders coincide.
-__device__ __forceinline__ int64_t caller_token(int64_t tok, int64_t S, int G) {
-  return G > 1 ? (tok % S) * G + tok / S : tok;
-}
 constexpr int DO32_TILE_BYTES = 32 * D_V * 2;   // 32768
 
 // Copies `tile_rows` entries [first, first + tile_rows) of a query group's
