@@ -66,14 +66,14 @@ KernelShape kernel_shape(int64_t s_q, int64_t s_kv, int heads, int kv_groups) {
 // a 64-row query group of token-major rows would hold rows of several kv
 // groups (disjoint kv rows, each masked for the others).  The kernels then
 // walk (group, token) pairs in group-major order (pair g S + s holds token
-// s's heads of group g) and read and write q, out, dout, dq and the forward's
-// lse at the caller's token-major rows (caller_token); the indices and the
-// backward's lse are permuted into the workspace.  The staging area leads
-// the workspace; the plan's layout follows it.
+// s's heads of group g) and read and write q, out, dout, dq, the indices and
+// the forward's lse at the caller's token-major rows (caller_token); only
+// the backward's lse is permuted into the workspace (its staging area leads
+// the workspace; the plan's layout follows it).
 struct Stage {
   bool on = false;
   int hg = 0;
-  size_t lse = 0, idx = 0, bytes = 0;
+  size_t lse = 0, bytes = 0;
 };
 Stage make_stage(int64_t s_q, int heads, int kv_groups, int topk) {
   Stage st;
@@ -83,7 +83,6 @@ Stage make_stage(int64_t s_q, int heads, int kv_groups, int topk) {
   const size_t rows = (size_t)s_q * heads;
   size_t o = 0;
   st.lse = o;  o = align256(o + rows * 4);
-  st.idx = o;  o = align256(o + (size_t)s_q * kv_groups * topk * 4);
   st.bytes = o;
   return st;
 }
@@ -337,13 +336,6 @@ int smla_plan_g(const int32_t* indices, int64_t s_q, int64_t s_kv, int32_t heads
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   char* ws = base + sg.bytes;
-  if (sg.on) {
-    int32_t* ix = reinterpret_cast<int32_t*>(base + sg.idx);
-    if ((st = hip_status(launch_permute_pairs(indices, ix, s_tok, kv_groups, (int64_t)topk * 4, true, s),
-                         "permute")))
-      return st;
-    indices = ix;
-  }
   return run_plan(p, plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups,
                                sg.on ? s_tok : 0, ws, true), heads, true, s);
 }
@@ -388,13 +380,6 @@ static int fwd_impl(const void* q, const void* kv, const uint8_t* kv8, const int
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   char* ws = base + sg.bytes;
-  if (sg.on) {   // group-major copies of the indices (unless planned)
-    if (!(flags & SMLA_PLAN_READY) &&
-        (st = hip_status(launch_permute_pairs(indices, base + sg.idx, s_tok, kv_groups,
-                                              (int64_t)topk * 4, true, s), "permute")))
-      return st;
-    indices = reinterpret_cast<const int32_t*>(base + sg.idx);
-  }
   const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups,
                                 sg.on ? s_tok : 0, ws, false);
   if (!(flags & SMLA_PLAN_READY) && (st = run_plan(p, pa, heads, false, s))) return st;
@@ -522,16 +507,11 @@ int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   char* ws = base + sg.bytes;
-  if (sg.on) {   // group-major copies of lse (and the indices, unless planned)
+  if (sg.on) {   // a group-major copy of lse
     if ((st = hip_status(launch_permute_pairs(lse, base + sg.lse, s_tok, kv_groups, (int64_t)sg.hg * 4, true, s),
                          "permute")))
       return st;
-    if (!(flags & SMLA_PLAN_READY) &&
-        (st = hip_status(launch_permute_pairs(indices, base + sg.idx, s_tok, kv_groups,
-                                              (int64_t)topk * 4, true, s), "permute")))
-      return st;
     lse = reinterpret_cast<const float*>(base + sg.lse);
-    indices = reinterpret_cast<const int32_t*>(base + sg.idx);
   }
 
   const PlanArgs pa = plan_args(p, indices, s_q, s_kv, topk, k.idx_shift, kv_groups,

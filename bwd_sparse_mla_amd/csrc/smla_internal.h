@@ -49,8 +49,9 @@ struct PlanArgs {
   // of the [s_kv_idx, kv_groups, 576] kv (s_kv = s_kv_idx * kv_groups rows)
   int kv_groups;
   int64_t s_kv_idx;
-  // group-major rows (0: token-major): index row r belongs to kv group
-  // r / gmajor_s instead of r % kv_groups
+  // group-major rows (0: token-major): row r is the (group, token) pair
+  // (r / gmajor_s, r % gmajor_s), kv group r / gmajor_s, and its indices are
+  // the caller's token-major index row caller_token(r, gmajor_s, kv_groups)
   int64_t gmajor_s;
   int64_t G, NB, qcap, rcap;
   int* qcount;        // [G]   union entries (main + extra) per group

@@ -49,6 +49,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   __shared__ unsigned xflag[XFLAG_WORDS];    // slots that repeat an earlier slot's row
   __shared__ int scratch[8];
   __shared__ int s_lo, s_hi;
+  __shared__ int64_t s_ixoff[T];             // group-major rows: each token's index row
   __shared__ int s_rep;                      // window check: slots minus distinct rows
 
   const int tid = threadIdx.x;
@@ -58,6 +59,19 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   const int K = a.topk;
   const int nslots = nt * K;
   const int32_t* ix = a.idx + (t0 >> a.idx_shift) * K;   // shift > 0 only with T = 1
+  // Index value of slot s of the group: the T index rows are consecutive,
+  // except for group-major rows (kv groups), which read each token's row of
+  // the caller's token-major indices.
+  const bool gmaj = KVG && a.gmajor_s > 0;
+  auto ixv = [&](int s) __attribute__((always_inline)) {
+    if constexpr (KVG) {
+      if (gmaj) {
+        const int t = s / K;
+        return a.idx[s_ixoff[t] + (s - t * K)];
+      }
+    }
+    return ix[s];
+  };
   const int nxw = (nslots + 31) >> 5;
   const int skv = (int)a.s_kv;        // flat kv rows
   const int sidx = (int)a.s_kv_idx;   // valid index values: [0, sidx)
@@ -77,6 +91,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     s_lo = 0x7fffffff;
     s_hi = -1;
   }
+  if (gmaj && tid < nt) s_ixoff[tid] = caller_token(t0 + tid, a.gmajor_s, a.kv_groups) * K;
   for (int w = tid; w < nxw; w += 256) xflag[w] = 0u;
   __syncthreads();
 
@@ -89,7 +104,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     for (int s0 = tid; s0 < nslots; s0 += 256 * PLAN_LOADS) {   // PLAN_LOADS loads in flight per thread
       int v[PLAN_LOADS];
 #pragma unroll
-      for (int j = 0; j < PLAN_LOADS; ++j) v[j] = s0 + 256 * j < nslots ? ix[s0 + 256 * j] : -1;
+      for (int j = 0; j < PLAN_LOADS; ++j) v[j] = s0 + 256 * j < nslots ? ixv(s0 + 256 * j) : -1;
 #pragma unroll
       for (int j = 0; j < PLAN_LOADS; ++j)
         if (v[j] >= 0 && v[j] < sidx) {
@@ -145,7 +160,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 #pragma unroll
         for (int j = 0; j < PLAN_LOADS; ++j) {
           const int s = s0 + 256 * j;
-          v[j] = s < nslots ? ix[s] : -1;
+          v[j] = s < nslots ? ixv(s) : -1;
         }
 #pragma unroll
         for (int j = 0; j < PLAN_LOADS; ++j) {
@@ -271,7 +286,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
             f &= f - 1;
             const int s = 32 * w + b;
             const int t = s / K, k = s - t * K;
-            const int32_t* row = ix + (int64_t)t * K;
+            const int32_t* row = gmaj ? a.idx + s_ixoff[t] : ix + (int64_t)t * K;
             const int v = __builtin_amdgcn_readfirstlane(row[k]);
             // The row is scanned 512 slots per round (eight loads in flight per
             // lane), not 64: each round is one memory round trip.
@@ -331,7 +346,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
       f &= f - 1;
       const int s = 32 * w + b;
       const int t = s / K;
-      qrow[pos] = flat_row(ix[s], s);
+      qrow[pos] = flat_row(ixv(s), s);
       qmask[pos] = (uint8_t)(1u << t);
       ++pos;
     }
