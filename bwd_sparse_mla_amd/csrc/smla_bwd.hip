@@ -102,6 +102,18 @@ __global__ __launch_bounds__(256) void dkv_schedule_kernel(BwdArgs a) {
   dkv_schedule_unit<256>(a, blockIdx.x);
 }
 
+// Flat kv row of block row b, and the block row of flat row f (b, f < 2^24).
+__device__ __forceinline__ int64_t kv_flat_row(int64_t b, int kvg, int64_t kvs) {
+  if (kvg == 1) return b;
+  const uint32_t g = (uint32_t)b / (uint32_t)kvs;
+  return (int64_t)((uint32_t)b - g * (uint32_t)kvs) * kvg + g;
+}
+__device__ __forceinline__ int64_t kv_block_row(int64_t f, int kvg, int64_t kvs) {
+  if (kvg == 1) return f;
+  const uint32_t v = (uint32_t)f / (uint32_t)kvg;
+  return (int64_t)((uint32_t)f - v * (uint32_t)kvg) * kvs + v;
+}
+
 // ---------------------------------------------------------------------------
 // dq pass
 // ---------------------------------------------------------------------------
@@ -440,7 +452,7 @@ __device__ __forceinline__ void dkv_segment(const BwdArgs& a, int64_t blk, int u
   {
     const int64_t row = kb0 + 16 * skb + (lane_id & 15);
     if (row < a.s_kv) {
-      const uint16_t* kr = a.kv + row * D_K + 8 * (lane_id >> 4);
+      const uint16_t* kr = a.kv + kv_flat_row(row, a.kvg, a.kvs) * D_K + 8 * (lane_id >> 4);
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) kf[ks] = ld16_global(kr + 32 * ks);
     } else {
@@ -1061,7 +1073,10 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) rr[j] = x0 + j < xc ? xr[x0 + j] : -1;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) cnt += rr[j] >= r0 && rr[j] < r0 + FIN_ROWS && rr[j] < a.s_kv;
+            for (int j = 0; j < 8; ++j) {
+              const int64_t br = rr[j] >= 0 ? kv_block_row(rr[j], a.kvg, a.kvs) : -1;
+              cnt += br >= r0 && br < r0 + FIN_ROWS && br < a.s_kv;
+            }
           }
         }
         int tot;
@@ -1074,10 +1089,11 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
             for (int j = 0; j < 8; ++j) rr[j] = x0 + j < xc ? xr[x0 + j] : -1;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              if (rr[j] >= r0 && rr[j] < r0 + FIN_ROWS && rr[j] < a.s_kv) {
+              const int64_t br = rr[j] >= 0 ? kv_block_row(rr[j], a.kvg, a.kvs) : -1;
+              if (br >= r0 && br < r0 + FIN_ROWS && br < a.s_kv) {
                 if (m >= n_done && m < n_done + FIN_XCAP) {
                   sXe[m - n_done] = g * a.qcap + n_main + x0 + j;
-                  atomicOr(&s_xt, 1u << (int)(rr[j] - r0));
+                  atomicOr(&s_xt, 1u << (int)(br - r0));
                 }
                 ++m;
               }
@@ -1103,7 +1119,7 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
           const int64_t g = ent / a.qcap;
           int64_t t = g * T + (__ffs((unsigned)a.qmask[ent]) - 1);
           t = t < 0 ? 0 : (t >= a.s_q ? a.s_q - 1 : t);
-          if (lane == 0) sXr[e] = (int)(row - r0);
+          if (lane == 0) sXr[e] = (int)(kv_block_row(row, a.kvg, a.kvs) - r0);
           const int j = lane & 7, hl = lane >> 3;
           const uint16_t* kr = a.kv + row * D_K + 8 * j;
           for (int hp = 0; hp < H / 8; ++hp) {
@@ -1221,8 +1237,8 @@ __global__ __launch_bounds__(256) void dkv_finalize_kernel(BwdArgs a) {
     if (extras) v += *reinterpret_cast<const float4_t*>(sX + 4 * e);
     const int kvl = (4 * e) / D_K;
     const int col = (4 * e) % D_K;
-    const int64_t row = r0 + kvl;
-    if (row >= a.s_kv) continue;
+    if (r0 + kvl >= a.s_kv) continue;
+    const int64_t row = kv_flat_row(r0 + kvl, a.kvg, a.kvs);
     const bool hit = (touched >> kvl) & 1ull;
     if (a.dkv_f32) {
       float4_t* d = reinterpret_cast<float4_t*>(a.dkv_f32 + row * D_K + col);

@@ -559,6 +559,8 @@ int smla_bwd_g(const void* q, const void* kv, const void* out, const void* dout,
   ba.dq = static_cast<uint16_t*>(dq);
   ba.pair_s = s_tok;
   ba.pair_g = sg.on ? kv_groups : 1;
+  ba.kvg = kv_groups;
+  ba.kvs = s_kv / kv_groups;
   ba.dkv = static_cast<uint16_t*>(dkv);
   ba.dkv_f32 = dkv_f32;
   ba.accumulate = (flags & SMLA_DKV_ACCUMULATE) ? 1 : 0;

@@ -44,9 +44,12 @@ struct PlanArgs {
   int64_t s_q, s_kv;
   int topk;
   int idx_shift;      // query row t reads index row t >> idx_shift (1: two rows per token)
-  // kv groups: index row r belongs to kv group r % kv_groups, and its valid
-  // value j (0 <= j < s_kv_idx) names flat kv row j * kv_groups + r % kv_groups
-  // of the [s_kv_idx, kv_groups, 576] kv (s_kv = s_kv_idx * kv_groups rows)
+  // kv groups: index row r belongs to kv group g = r % kv_groups, and its
+  // valid value j (0 <= j < s_kv_idx) names flat kv row j * kv_groups + g of
+  // the [s_kv_idx, kv_groups, 576] kv (s_kv = s_kv_idx * kv_groups rows).
+  // The bitmaps, the union order and the kv blocks (ktab, krmask, kbase,
+  // korm) use block row g * s_kv_idx + j instead, so that a 64-row block
+  // holds one group's rows; qrow holds flat rows.
   int kv_groups;
   int64_t s_kv_idx;
   // group-major rows (0: token-major): row r is the (group, token) pair
@@ -57,7 +60,7 @@ struct PlanArgs {
   int* qcount;        // [G]   union entries (main + extra) per group
   int* xcount;        // [G]   extra entries (repeated slots) per group
   int* xtotal;        // [1]   sum of xcount (written by the order kernel)
-  int32_t* qrow;      // [G, qcap] kv row of each union entry
+  int32_t* qrow;      // [G, qcap] flat kv row of each union entry
   uint8_t* qmask;     // [G, qcap] mask of the group's tokens that select it
   int2* ktab;         // [NB, G] (record start within the group, T) or (0, 0); may be null
   unsigned long long* krmask;  // [G, rcap] 64-bit row masks, T per (block, group) pair
@@ -112,10 +115,15 @@ struct BwdArgs {
   const int2* ktab;
   const unsigned long long* krmask;
   const int* gorder;  // [G] groups by decreasing union size (dq pass)
-  // Several kv groups (pair_g > 1): out and dq are the caller's token-major
-  // rows (see caller_token); q, dout and lse are group-major copies.
+  // Several kv groups (pair_g > 1): q, out, dout and dq are the caller's
+  // token-major rows (see caller_token); lse is a group-major copy.
   int64_t pair_s;
   int pair_g;
+  // The dkv pass's kv blocks and finalize's rows are block rows: block row
+  // b is row b % kvs of kv group b / kvs, flat row (b % kvs) * kvg + b / kvs
+  // (kvg = 1: the same row).
+  int kvg;
+  int64_t kvs;
   int* spre;          // [NU + 1] dkv sub-chunks before each unit (exclusive prefix; [NU] = total)
   int* wstart;        // [DKV_WGS] first dkv unit of each dkv workgroup's range
   float* delta;       // [s_q * H] rowsum(dout * out), written by the dq pass

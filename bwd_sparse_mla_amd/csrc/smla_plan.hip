@@ -50,8 +50,12 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   __shared__ int scratch[8];
   __shared__ int s_lo, s_hi;
   __shared__ int64_t s_ixoff[T];             // group-major rows: each token's index row
+  __shared__ int s_kg[T];                    // kv groups: each token's kv group
   __shared__ int s_rep;                      // window check: slots minus distinct rows
 
+  // Index loads in flight per thread: with kv groups each load's address is
+  // formed per slot, so fewer loads per thread keep three waves per SIMD.
+  constexpr int NL = KVG ? PLAN_LOADS / 2 : PLAN_LOADS;
   const int tid = threadIdx.x;
   const int64_t g = blockIdx.x;
   const int64_t t0 = g * T;
@@ -63,11 +67,34 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   // except for group-major rows (kv groups), which read each token's row of
   // the caller's token-major indices.
   const bool gmaj = KVG && a.gmajor_s > 0;
+  // Group-local token of slot s (token t holds slots t K .. t K + K - 1;
+  // K is uniform, so the division's reciprocal is formed once).
+  auto tok_of = [&](int s) __attribute__((always_inline)) { return T == 1 ? 0 : s / K; };
+  // kv group of token t (KVG): group-major rows are pairs g S + s (S =
+  // gmajor_s), so from the first pair's (g0, r0) a token moves to the next
+  // group each time r0 + t passes a multiple of S; token-major rows (T = 1)
+  // have one group.  No divisions or LDS reads per slot.
+  // (Pairs and tokens are below 2^31.)
+  const int gS = gmaj ? (int)a.gmajor_s : 1;
+  const int g0 = gmaj ? (int)(t0 / gS) : (KVG ? (int)((t0 >> a.idx_shift) % a.kv_groups) : 0);
+  const int r0 = gmaj ? (int)(t0 - (int64_t)g0 * gS) : 0;
+  auto group_of = [&](int t, int& r) __attribute__((always_inline)) {
+    int g = g0;
+    r = r0 + t;
+    if (gmaj)
+      while (r >= gS) {
+        r -= gS;
+        ++g;
+      }
+    return g;
+  };
   auto ixv = [&](int s) __attribute__((always_inline)) {
     if constexpr (KVG) {
-      if (gmaj) {
-        const int t = s / K;
-        return a.idx[s_ixoff[t] + (s - t * K)];
+      if (gmaj) {   // slot s - t K of the caller's index row r kv_groups + g
+        const int t = tok_of(s);
+        int r;
+        const int g = group_of(t, r);
+        return a.idx[((int64_t)r * a.kv_groups + g - t) * K + s];
       }
     }
     return ix[s];
@@ -76,15 +103,22 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   const int skv = (int)a.s_kv;        // flat kv rows
   const int sidx = (int)a.s_kv_idx;   // valid index values: [0, sidx)
   const int kvg = a.kv_groups;
-  // Flat kv row of a valid value v in slot s of the group (KVG: the slot's
-  // index row picks the kv group).
-  auto flat_row = [&](int v, int s) __attribute__((always_inline)) {
+  // Rows of a valid value v of token t.  The bitmaps, the union order and
+  // the kv blocks use block rows, in which each kv group's rows form one
+  // range (row v of group g is g sidx + v), so a 64-row kv block holds one
+  // group's rows; the union list stores the flat row of the [sidx, kvg,
+  // 576] kv, v kvg + g, where the gathers read it.
+  auto brow = [&](int v, int s) __attribute__((always_inline)) {   // v of slot s
     if constexpr (KVG) {
-      const int64_t r = (t0 + s / K) >> a.idx_shift;
-      return v * kvg + (int)(a.gmajor_s ? r / a.gmajor_s : r % kvg);
+      int r;
+      return group_of(tok_of(s), r) * sidx + v;
     } else {
       return v;
     }
+  };
+  auto frow = [&](int v, int t) __attribute__((always_inline)) {
+    if constexpr (KVG) return v * kvg + s_kg[t];
+    else return v;
   };
 
   if (tid == 0) {
@@ -92,24 +126,39 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     s_hi = -1;
   }
   if (gmaj && tid < nt) s_ixoff[tid] = caller_token(t0 + tid, a.gmajor_s, a.kv_groups) * K;
+  if (KVG && tid < nt) {   // the (group, token) pair's kv group
+    const int64_t r = t0 + tid;
+    s_kg[tid] = gmaj ? (int)(r / a.gmajor_s) : (int)((r >> a.idx_shift) % kvg);
+  }
   for (int w = tid; w < nxw; w += 256) xflag[w] = 0u;
   __syncthreads();
 
-  // Span of the valid rows this group selects (one window from row 0 covers
-  // every valid row when s_kv <= WIN_BITS; the scan is skipped then).
+  // Span of the valid rows this group selects (one window covers every
+  // valid row when s_kv <= WIN_BITS; the scan is skipped then, and with kv
+  // groups the span is the block rows of the tokens' groups).
   int lo = 0, hi = skv - 1;
+  if (KVG && skv <= WIN_BITS) {
+    int gl = s_kg[0], gh = s_kg[0];
+    for (int t = 1; t < nt; ++t) {
+      gl = min(gl, s_kg[t]);
+      gh = max(gh, s_kg[t]);
+    }
+    lo = gl * sidx;
+    hi = min(skv, (gh + 1) * sidx) - 1;
+  }
   if (skv > WIN_BITS) {
     lo = 0x7fffffff;
     hi = -1;
-    for (int s0 = tid; s0 < nslots; s0 += 256 * PLAN_LOADS) {   // PLAN_LOADS loads in flight per thread
-      int v[PLAN_LOADS];
+    for (int s0 = tid; s0 < nslots; s0 += 256 * NL) {   // NL loads in flight per thread
+      int v[NL];
 #pragma unroll
-      for (int j = 0; j < PLAN_LOADS; ++j) v[j] = s0 + 256 * j < nslots ? ixv(s0 + 256 * j) : -1;
+      for (int j = 0; j < NL; ++j) v[j] = s0 + 256 * j < nslots ? ixv(s0 + 256 * j) : -1;
 #pragma unroll
-      for (int j = 0; j < PLAN_LOADS; ++j)
+      for (int j = 0; j < NL; ++j)
         if (v[j] >= 0 && v[j] < sidx) {
-          lo = min(lo, v[j]);
-          hi = max(hi, v[j]);
+          const int m = brow(v[j], s0 + 256 * j);
+          lo = min(lo, m);
+          hi = max(hi, m);
         }
     }
     lo = wave_min(lo);
@@ -121,10 +170,6 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     __syncthreads();
     lo = s_lo;
     hi = s_hi;
-    if (KVG && hi >= 0) {   // the flat rows of the values' span, every group's
-      lo *= kvg;
-      hi = hi * kvg + kvg - 1;
-    }
   }
 
   int32_t* qrow = a.qrow + g * a.qcap;
@@ -143,7 +188,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   // Windows start on a 64-row block boundary so kv blocks never straddle two.
   for (int w0 = (hi >= 0 ? (lo & ~63) : 1); w0 <= hi; w0 += WIN_BITS) {
     const int qbase0 = qbase;   // union entries before this window
-    // Bitmap pass: PLAN_LOADS index loads in flight per thread before their
+    // Bitmap pass: NL index loads in flight per thread before their
     // bitmap updates.  The first pass sets the bits with no-return atomics
     // and counts the window's valid slots; a token that lists a row twice
     // leaves fewer bits than slots, and only then does a second pass redo
@@ -155,19 +200,19 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
       if (tid == 0) s_rep = 0;
       __syncthreads();
       int cnt = 0;
-      for (int s0 = tid; s0 < nslots; s0 += 256 * PLAN_LOADS) {
-        int v[PLAN_LOADS];
+      for (int s0 = tid; s0 < nslots; s0 += 256 * NL) {
+        int v[NL];
 #pragma unroll
-        for (int j = 0; j < PLAN_LOADS; ++j) {
+        for (int j = 0; j < NL; ++j) {
           const int s = s0 + 256 * j;
           v[j] = s < nslots ? ixv(s) : -1;
         }
 #pragma unroll
-        for (int j = 0; j < PLAN_LOADS; ++j) {
+        for (int j = 0; j < NL; ++j) {
           const int s = s0 + 256 * j;
-          const int m = v[j] >= 0 && v[j] < sidx ? flat_row(v[j], s) : -1;
+          const int m = v[j] >= 0 && v[j] < sidx ? brow(v[j], s) : -1;
           if (m >= w0 && m < w0 + WIN_BITS) {
-            const int t = s / K;
+            const int t = tok_of(s);
             const int bit = m - w0;
             const unsigned mb = 1u << (bit & 31);
             if constexpr (rtn) {
@@ -221,7 +266,12 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
         unsigned mask = 0;
 #pragma unroll
         for (int t = 0; t < T; ++t) mask |= ((tb[t] >> b) & 1u) << t;
-        qrow[pos] = row0 + b;
+        if constexpr (KVG) {   // flat row of the block row (a selecting token's group)
+          const int gk = s_kg[__ffs(mask) - 1];
+          qrow[pos] = (row0 + b - gk * sidx) * kvg + gk;
+        } else {
+          qrow[pos] = row0 + b;
+        }
         qmask[pos] = (uint8_t)mask;
         ++pos;
       }
@@ -346,7 +396,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
       f &= f - 1;
       const int s = 32 * w + b;
       const int t = s / K;
-      qrow[pos] = flat_row(ixv(s), s);
+      qrow[pos] = frow(ixv(s), t);
       qmask[pos] = (uint8_t)(1u << t);
       ++pos;
     }
