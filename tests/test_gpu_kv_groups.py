@@ -23,8 +23,10 @@ CASES = {
     "h64_g8_oob": dict(S=25, H=64, G=8, K=64, S_kv=90, seed=43, pad_frac=0.2, oob_frac=0.05),
     "h256_g2": dict(S=9, H=256, G=2, K=100, S_kv=200, seed=44, pad_frac=0.25, empty_frac=0.1),
     "h128_g2_multiblock": dict(S=30, H=128, G=2, K=400, S_kv=1200, seed=45, pad_frac=0.1),
-    # index rows of 600 bytes: the group-major staging copies them in 4-byte words
+    # index rows of 600 bytes (K not a multiple of 4), read where the caller keeps them
     "h32_g2_k150": dict(S=23, H=32, G=2, K=150, S_kv=400, seed=46, pad_frac=0.2, empty_frac=0.1),
+    # three tokens, 8 heads per group: one 64-row query group spans three kv groups
+    "h64_g8_s3_dups": dict(S=3, H=64, G=8, K=50, S_kv=70, seed=47, pad_frac=0.2, dup_frac=0.1),
 }
 
 
