@@ -63,9 +63,6 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   const int K = a.topk;
   const int nslots = nt * K;
   const int32_t* ix = a.idx + (t0 >> a.idx_shift) * K;   // shift > 0 only with T = 1
-  // Index value of slot s of the group: the T index rows are consecutive,
-  // except for group-major rows (kv groups), which read each token's row of
-  // the caller's token-major indices.
   const bool gmaj = KVG && a.gmajor_s > 0;
   // Group-local token of slot s (token t holds slots t K .. t K + K - 1;
   // K is uniform, so the division's reciprocal is formed once).
@@ -78,23 +75,26 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   const int gS = gmaj ? (int)a.gmajor_s : 1;
   const int g0 = gmaj ? (int)(t0 / gS) : (KVG ? (int)((t0 >> a.idx_shift) % a.kv_groups) : 0);
   const int r0 = gmaj ? (int)(t0 - (int64_t)g0 * gS) : 0;
-  auto group_of = [&](int t, int& r) __attribute__((always_inline)) {
-    int g = g0;
+  auto group_of = [&](int t, int& r) __attribute__((always_inline)) {   // r: the pair's token
+    int kg = g0;
     r = r0 + t;
     if (gmaj)
       while (r >= gS) {
         r -= gS;
-        ++g;
+        ++kg;
       }
-    return g;
+    return kg;
   };
+  // Index value of slot s of the group: the T index rows are consecutive,
+  // except for group-major rows (kv groups), which read each token's row of
+  // the caller's token-major indices (slot s - t K of row r kv_groups + kg).
   auto ixv = [&](int s) __attribute__((always_inline)) {
     if constexpr (KVG) {
-      if (gmaj) {   // slot s - t K of the caller's index row r kv_groups + g
+      if (gmaj) {
         const int t = tok_of(s);
         int r;
-        const int g = group_of(t, r);
-        return a.idx[((int64_t)r * a.kv_groups + g - t) * K + s];
+        const int kg = group_of(t, r);
+        return a.idx[((int64_t)r * a.kv_groups + kg - t) * K + s];
       }
     }
     return ix[s];
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
   const int skv = (int)a.s_kv;        // flat kv rows
   const int sidx = (int)a.s_kv_idx;   // valid index values: [0, sidx)
   const int kvg = a.kv_groups;
-  // Rows of a valid value v of token t.  The bitmaps, the union order and
+  // Rows of a valid value v of slot s (token t).  The bitmaps, the union order and
   // the kv blocks use block rows, in which each kv group's rows form one
   // range (row v of group g is g sidx + v), so a 64-row kv block holds one
   // group's rows; the union list stores the flat row of the [sidx, kvg,
