@@ -14,7 +14,8 @@ valid (token, slot) pair over the fwd+bwd step time), the roofline of the
 dominant kernel (timed with HIP events on the library's stream) and the CPU
 baseline (the fp64 oracle on a bounded token sample, on the host cores).
 Outside the timed step it also reports the index-production top-k, the
-finite check of dq / dkv and the forward over fp8 kv records.
+finite check of dq / dkv, the forward over fp8 kv records and a step with
+two kv groups.
 """
 from __future__ import annotations
 
@@ -67,6 +68,8 @@ def parse():
                     help="time the steps without per-kernel HIP events")
     ap.add_argument("--no-topk", action="store_true",
                     help="skip the index-production (top-k) measurement")
+    ap.add_argument("--no-kv-groups", action="store_true",
+                    help="skip the two-kv-group step (its launches share the kernels' names)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads reported beside the headline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -221,6 +224,71 @@ def fp8_fwd_measure(run, w, q, kv, idx, steps: int):
     return {"what": "forward over fp8 kv records (656 B per row) vs the bf16 forward",
             "ms": round(ms8, 5), "ms_pow2_scales": round(ms8p, 5), "bf16_fwd_ms": round(ms16, 5),
             "useful_tflops": round(flops / (ms8 * 1e-3) / 1e12, 1)}
+
+
+def kv_groups_measure(dev, steps: int, stored: bool):
+    """Two kv groups of 8 heads each (H = 16) at the packed ragged batch's
+    sizes: one grouped call (kv [S_kv, 2, 576], indices [S, 2, K]) against two
+    single-group calls on the same data, each a full step (plan, forward,
+    backward).  Seeded N(0, 1) bf16 q / kv / dout; each group's indices are
+    full causal rows over the sequences {512, 1024, 1536, 1024}, shuffled
+    independently."""
+    import torch
+
+    import bwd_sparse_mla_amd as smla
+    from workloads import synth
+    rng = np.random.default_rng(11)
+    seqlens = [512, 1024, 1536, 1024]
+    S, K, G, Hg = sum(seqlens), 2048, 2, 8
+    idx_np = np.stack([synth.causal_full_rows(rng, seqlens, K) for _ in range(G)], axis=1)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+
+    def randn(*shape):
+        return torch.randn(*shape, device=dev, generator=gen).to(torch.bfloat16)
+
+    q, kv, dout = randn(S, G * Hg, 576), randn(S, G, 576), randn(S, G * Hg, 512)
+    idx = torch.from_numpy(idx_np).to(dev).contiguous()
+    scale = 1.0 / 192 ** 0.5
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    run = smla.SparseMLARunner(S, S, G * Hg, K, dev, dkv_stored_p=stored, kv_groups=G)
+
+    def grouped():
+        run.plan(idx)
+        run.fwd(q, kv, idx, scale, planned=True)
+        run.bwd(q, kv, dout, idx, scale, planned=True)
+
+    ms_g = timed(grouped)
+    if not (bool(torch.isfinite(run.dq.float()).all()) and bool(torch.isfinite(run.dkv.float()).all())):
+        raise RuntimeError("nonfinite values in the grouped backward")
+    runs = [smla.SparseMLARunner(S, S, Hg, K, dev, dkv_stored_p=stored) for _ in range(G)]
+    parts = [(q[:, g * Hg:(g + 1) * Hg].contiguous(), kv[:, g].contiguous(),
+              dout[:, g * Hg:(g + 1) * Hg].contiguous(), idx[:, g].contiguous()) for g in range(G)]
+
+    def separate():
+        for r, (qg, kvg, dog, ixg) in zip(runs, parts):
+            r.plan(ixg)
+            r.fwd(qg, kvg, ixg, scale, planned=True)
+            r.bwd(qg, kvg, dog, ixg, scale, planned=True)
+
+    ms_s = timed(separate)
+    useful = 7680 * Hg * int((idx_np >= 0).sum())
+    return {"workload": "packed ragged batch sizes, 2 kv groups x 8 heads (H=16)",
+            "ms_per_step": round(ms_g, 5), "useful_tflops": round(useful / (ms_g * 1e-3) / 1e12, 2),
+            "two_single_group_calls_ms": round(ms_s, 5)}
 
 
 def host_info():
@@ -502,6 +570,11 @@ def main():
     print("[bench] fp8 kv forward ...", file=sys.stderr, flush=True)
     fp8 = fp8_fwd_measure(run, w, q, kv, idx, max(10, args.steps))
 
+    kvgroups = None
+    if not args.no_kv_groups:
+        print("[bench] kv groups ...", file=sys.stderr, flush=True)
+        kvgroups = kv_groups_measure(dev, max(10, args.steps), stored)
+
     topk = None
     if not args.no_topk:
         print("[bench] index production (top-k) ...", file=sys.stderr, flush=True)
@@ -556,6 +629,7 @@ def main():
         "index_topk": topk,
         "nonfinite_check": finite,
         "fwd_fp8_kv": fp8,
+        "kv_groups": kvgroups,
     }
     print(json.dumps(line), flush=True)
 

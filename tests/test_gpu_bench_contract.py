@@ -39,6 +39,8 @@ def test_bench_prints_one_json_line(scores):
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1
     assert 1 <= c["cores"] <= c["affinity_cores"]
+    kg = d["kv_groups"]
+    assert kg["ms_per_step"] > 0 and kg["useful_tflops"] > 0 and kg["two_single_group_calls_ms"] > 0
     for part in ("warm", "cold_caches"):
         m = d["median"][part]
         assert 0 < m["fwd_ms"] < m["fwd_bwd_ms"] and 0 < m["bwd_ms"] < m["fwd_bwd_ms"]
