@@ -45,7 +45,10 @@ int check_shape(int64_t s_q, int64_t s_kv, int heads, int topk, int kv_groups = 
 // [s_q G, heads / G, 576] (the pair (token, group) is one row of heads / G
 // heads, reading index row s G + g of indices [s_q, G, topk]), and kv
 // [s_kv, G, 576] is s_kv G flat rows (the planner maps a valid index j of
-// group g to row j G + g).  A query group is 64 rows; with 128 heads per kv
+// group g to flat row j G + g for the gathers, and to block row g s_kv + j
+// for the kv-major blocks of the dkv pass, so that a block holds one group's
+// rows; finalize writes block row g s_kv + j to dkv row j G + g).  A query
+// group is 64 rows; with 128 heads per kv
 // group a row's heads are two groups, so the kernels run the 64-head form
 // over twice the rows (the same memory: row (2r + j, h) is (r, 64 j + h)),
 // half-row 2r + j reading index row r.
