@@ -45,12 +45,7 @@ namespace {
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan_nt(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_inclusive_scan(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
   int base = 0, tot = 0;
@@ -865,12 +860,7 @@ __device__ __forceinline__ UnitScan dkv_unit_scan(const BwdArgs& a, int wg, int6
   const int64_t b0 = min<int64_t>(a.NU, tid * cnt), b1 = min<int64_t>(a.NU, b0 + cnt);
   int sum = 0;
   for (int64_t b = b0; b < b1; ++b) sum += 2 * a.nchunk[b];
-  int x = sum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_inclusive_scan(sum);
   if (lane == 63) red[wv] = x;
   if (tid == 0) {
     red[NWV] = -1;

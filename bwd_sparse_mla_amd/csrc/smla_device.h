@@ -266,14 +266,24 @@ __device__ __forceinline__ float sum16(float v) {
 // Exclusive prefix sum over a 256-thread block; returns this thread's
 // exclusive prefix and writes the block total to *total.  `scratch` holds at
 // least 8 ints of LDS.  Must be called by all threads.
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active), on
+// the data-parallel-primitive lane moves: shifts by 1, 2, 4 and 8 within each
+// row of 16 lanes (a lane shifted in from outside its row adds 0), then lane
+// 15 added into row 1 and lane 47 into row 3, then lane 31 into rows 2 and 3.
+// Six dependent adds instead of six LDS permutes.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
+  return x;
+}
+
 __device__ __forceinline__ int block_exclusive_scan256(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_inclusive_scan(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
   int base = 0, tot = 0;
