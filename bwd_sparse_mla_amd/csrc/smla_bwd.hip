@@ -238,8 +238,7 @@ __global__ __launch_bounds__(DQ_NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
       for (int ks = 0; ks < 16; ++ks)
 #pragma unroll
         for (int j = 0; j < 8; ++j) d += bf2f((unsigned short)df[ks][j]) * bf2f((unsigned short)of[ks][j]);
-      d += __shfl_xor(d, 16);
-      d += __shfl_xor(d, 32);
+      d = sum_rows(d);   // (d_r + d_r+16) + (d_r+32 + d_r+48)
       del = d;
       if (g16 == 0 && tok < a.s_q) a.delta[tok * H + rr % H] = d;
     }

@@ -247,22 +247,6 @@ __device__ __forceinline__ float sum_rows(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Reductions across the 16 lanes that share l >> 4 (one C-fragment row group).
-__device__ __forceinline__ float max16(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
-  return v;
-}
-__device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  return v;
-}
-
 // Exclusive prefix sum over a 256-thread block; returns this thread's
 // exclusive prefix and writes the block total to *total.  `scratch` holds at
 // least 8 ints of LDS.  Must be called by all threads.

@@ -231,9 +231,8 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     {
       int cnt = bitmap_pass(Int<0>{});
       for (int i = tid; i < T * WIN_WORDS; i += 256) cnt -= __popc((&bm[0][0])[i]);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
-      if ((tid & 63) == 0 && cnt != 0) atomicAdd(&s_rep, cnt);
+      cnt = wave_inclusive_scan(cnt);   // lane 63: the wave's total
+      if ((tid & 63) == 63 && cnt != 0) atomicAdd(&s_rep, cnt);
       __syncthreads();
       if (s_rep != 0) {   // (uniform) some token lists a row twice in this window
         __syncthreads();   // every thread has read s_rep before the clear
@@ -418,9 +417,8 @@ __global__ __launch_bounds__(256) void order_groups_kernel(const int* qcount, co
   __shared__ int s_x[4];
   int x = 0;
   for (int64_t g = threadIdx.x; g < G; g += 256) x += xcount[g];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = x;
+  x = wave_inclusive_scan(x);   // lane 63: the wave's total
+  if ((threadIdx.x & 63) == 63) s_x[threadIdx.x >> 6] = x;
   order_by_cost(G, [&](int64_t g) { return (qcount[g] + 31) >> 5; }, order);   // syncs the block
   if (threadIdx.x == 0) *xtotal = s_x[0] + s_x[1] + s_x[2] + s_x[3];
 }
