@@ -27,6 +27,11 @@ CASES = {
     "h32_g2_k150": dict(S=23, H=32, G=2, K=150, S_kv=400, seed=46, pad_frac=0.2, empty_frac=0.1),
     # three tokens, 8 heads per group: one 64-row query group spans three kv groups
     "h64_g8_s3_dups": dict(S=3, H=64, G=8, K=50, S_kv=70, seed=47, pad_frac=0.2, dup_frac=0.1),
+    # more than 16384 flat kv rows (the planner scans each group's span; the
+    # query group of pairs 32..39 holds both kv groups' rows: two windows)
+    "h16_g2_wide": dict(S=37, H=16, G=2, K=300, S_kv=9000, seed=48, pad_frac=0.2, dup_frac=0.02),
+    # 64 heads per group (token-major pairs), 20000 flat kv rows
+    "h256_g4_wide": dict(S=6, H=256, G=4, K=200, S_kv=5000, seed=49, pad_frac=0.2),
 }
 
 
