@@ -4,7 +4,8 @@ grouped oracle; backward (deterministic, stored-P, atomic dkv) against the
 grouped oracle given the GPU's out / lse; rows of a group no slot selects stay
 exact zeros in dkv; empty index rows give zero out and dq; the plan built once
 gives the one-shot results bit for bit.  Cases cover 8 to 128 heads per group
-(below 64 the calls stage group-major copies in the workspace), padding
+(below 64 the kernels walk the (token, group) pairs in group-major order),
+kv blocks that straddle two groups, more than 16384 flat kv rows, padding
 anywhere, empty rows, repeated and out-of-range indices, index rows that are
 not a multiple of 16 bytes."""
 import numpy as np
