@@ -214,7 +214,23 @@ def test_single_slot_rows_exact():
     g = out.float().cpu().numpy()
     for s in range(32):
         assert np.array_equal(g[s], np.broadcast_to(kv[rows[s], :512], (16, 512)))
-    assert torch.count_nonzero(dq).item() == 0 or float(dq.abs().max()) < 1e-2
+    # With one slot P = 1, out = v and dS = P (dP - delta) is 0 in exact
+    # arithmetic: dP and delta are the same 512 products summed in different
+    # fp32 orders (|dP - delta| <= 2 * 512 * 2^-24 * sum |dout v|), and P
+    # differs from 1 by the rounding of lse's ln / exp2 round trip, a few ulp
+    # of the logit z * scale * log2(e) (|P - 1| <= (8 + 4 |z scale log2 e|) 2^-24).
+    # dq = scale * dS * k, with dS and dq rounded to bf16 on the way (1.01).
+    do = synth.bf16_bits_to_f64(w.dout)                      # [S, H, 512]
+    v = synth.bf16_bits_to_f64(w.kv)[rows]                   # [S, 576]
+    z = np.einsum("shc,sc->sh", synth.bf16_bits_to_f64(w.q), v)
+    prods = do * v[:, None, :512]
+    p_err = (8 + 4 * np.abs(z * w.sm_scale * np.log2(np.e))) * 2.0 ** -24
+    dsb = 2 * 512 * 2.0 ** -24 * np.abs(prods).sum(-1) + p_err * np.abs(prods.sum(-1))
+    bound = 1.01 * w.sm_scale * dsb[:, :, None] * np.abs(v)[:, None, :]   # [S, H, 576]
+    got = bf16_to_np64(dq)
+    print(f"[parity] single-slot dq: max {np.abs(got).max():.3e}, max bound {bound.max():.3e}, "
+          f"max ratio {(np.abs(got) / np.maximum(bound, 1e-300)).max():.3f}", flush=True)
+    assert np.all(np.abs(got) <= bound)
 
 
 def test_neighbouring_nonfinite_memory_is_never_read():
